@@ -1,0 +1,305 @@
+/*
+ * cider_oracle.c -- plain CPU reference for the fused quantized linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline do.  It shares no code, header, table or constant with the HIP
+ * library: it is a second, independent statement of what the layer computes.
+ *
+ * What is computed, and where the pages say so:
+ *   Cider README (ossradar.top repo page), "Quantization" table:
+ *     - activations: symmetric INT8, one scale per token (row of X);
+ *     - W8A8 weights: symmetric INT8, per output channel or per group of
+ *       64/128 consecutive input elements;
+ *     - W4A8 weights: symmetric INT4 with zero-point 8, stored packed in uint8;
+ *     - accumulation in INT32;
+ *     - output dequant: C_fp16 = C_int32 * s_act * s_weight, per element.
+ *   Same README, "W8A8 Quantization Granularity" table (per-channel = one scale
+ *   per output channel; per-group = one scale per 64 or 128 elements) and the
+ *   "LLM Quantization: Precision vs. Speed" note (scales by plain min-max).
+ *   Same README, "Metal Kernel Pipeline": FP16 activations -> INT8 + per-token
+ *   scales, then INT8 x INT8 -> INT32 -> FP16.
+ *
+ * Readings taken where the pages are silent (each is listed in the design doc):
+ *   - scale s = absmax / 127 (int8) or absmax / 7 (int4), computed in fp32;
+ *   - code q = clamp(round_half_even(fp32(x / s)), lo, hi), the quotient a
+ *     correctly rounded fp32 division; int8 range [-127, 127], int4 [-8, 7];
+ *   - an all-zero row or group gets s = 0 and q = 0;
+ *   - int4 nibble u = q + 8 (zero-point 8); byte j of a packed row holds
+ *     k = 2j in its low nibble and k = 2j + 1 in its high nibble;
+ *   - per-group scales are stored [N, K / group_size], row-major;
+ *   - dequant is evaluated in fp64 and rounded once to fp16 (round to nearest
+ *     even, overflow to infinity).  Per-group: y = s_tok * sum_g s_w[n,g]*acc_g.
+ *
+ * Quantization decisions are taken in fp32 because the scales are fp32
+ * values; everything after the integer accumulation is fp64.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -fPIC -shared (see build_oracle.py).
+ * Rows are split across OpenMP threads; the arithmetic per row is the plain
+ * loop written below, in the order written.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_OK = 0, ORACLE_BAD_ARG = 1, ORACLE_OVERFLOW = 2 };
+
+/* K > 0; bits 8 or 4; group_size 0 (per channel) or a divisor of K; int4
+   packs two codes per byte, so K is even. */
+static int shape_ok(int64_t K, int bits, int group_size)
+{
+    if (K <= 0 || (bits != 8 && bits != 4))
+        return 0;
+    if (group_size < 0 || (group_size > 0 && K % group_size != 0))
+        return 0;
+    if (bits == 4 && K % 2 != 0)
+        return 0;
+    return 1;
+}
+
+/* ---------------------------------------------------------------- fp16 --- */
+
+/* Exact widening of an IEEE binary16 bit pattern. */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int man = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)man, -24);              /* zero / subnormal: man * 2^-24 */
+    else if (e == 31)
+        v = man ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + man), e - 25);  /* (1 + man/1024) * 2^(e - 15) */
+    return sign ? -v : v;
+}
+
+/* Round a double to the nearest binary16 value, ties to even; overflow -> inf. */
+uint16_t oracle_double_to_half(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7e00);
+    /* 65520 is the midpoint between 65504 (largest finite) and 65536 (which
+       would be the next binade); ties go to the even neighbour, 65536 = inf. */
+    if (a >= 65520.0)
+        return (uint16_t)(sign | 0x7c00);
+    /* Quantum (distance between neighbouring halves) at a: 2^-24 below the
+       smallest normal 2^-14, else 2^(e-11) where a = f * 2^e, f in [0.5, 1). */
+    int e = 0;
+    frexp(a, &e);
+    int q = (a < ldexp(1.0, -14)) ? -24 : e - 11;
+    double m = nearbyint(ldexp(a, -q));           /* count of quanta, ties to even */
+    if (q == -24)                                  /* subnormal (m == 1024 is 2^-14) */
+        return (uint16_t)(sign | (uint16_t)m);
+    if (m == 2048.0) {                             /* rounded up into the next binade */
+        m = 1024.0;
+        q += 1;
+    }
+    /* value = m * 2^q with m in [1024, 2048): biased exponent = q + 25 */
+    return (uint16_t)(sign | ((q + 25) << 10) | ((int)m - 1024));
+}
+
+float oracle_half_to_float(uint16_t h) { return (float)oracle_half_to_double(h); }
+
+/* ------------------------------------------------------- quantization --- */
+
+/* Symmetric absmax quantization of n consecutive fp16 values.
+   Writes the integer codes to q[0..n) and returns the fp32 scale. */
+static float quantize_run(const uint16_t *x, int64_t n, float qmax, int lo, int hi,
+                          int *q)
+{
+    float absmax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(oracle_half_to_float(x[i]));
+        if (a > absmax)
+            absmax = a;
+    }
+    float s = absmax / qmax;                       /* fp32, correctly rounded */
+    for (int64_t i = 0; i < n; ++i) {
+        if (s == 0.0f) {
+            q[i] = 0;
+            continue;
+        }
+        float t = oracle_half_to_float(x[i]) / s;  /* fp32 quotient */
+        float r = nearbyintf(t);                   /* round half to even */
+        int c = (int)r;
+        if (c < lo) c = lo;
+        if (c > hi) c = hi;
+        q[i] = c;
+    }
+    return s;
+}
+
+/* Per-token activation quantization: X fp16 [M, K] with row stride ldx.
+   xq int8 [M, K] (row stride K), s_tok fp32 [M]. */
+int oracle_quantize_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                        int8_t *xq, float *s_tok)
+{
+    if (!x || !xq || !s_tok || M < 0 || K <= 0 || ldx < K)
+        return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        int qbuf[K];
+        s_tok[m] = quantize_run(x + m * ldx, K, 127.0f, -127, 127, qbuf);
+        for (int64_t k = 0; k < K; ++k)
+            xq[m * K + k] = (int8_t)qbuf[k];
+    }
+    return ORACLE_OK;
+}
+
+/* Weight quantization, W fp16 [N, K] (row stride K).
+   bits = 8: wq int8 [N, K];   bits = 4: wq uint8 [N, K/2] packed nibbles.
+   group_size = 0: one scale per output channel, s_w fp32 [N];
+   group_size = g: one scale per (n, k-group of g), s_w fp32 [N, K/g]. */
+int oracle_quantize_weight(const uint16_t *w, int64_t N, int64_t K, int bits,
+                           int group_size, uint8_t *wq, float *s_w)
+{
+    if (!w || !wq || !s_w || N < 0 || !shape_ok(K, bits, group_size))
+        return ORACLE_BAD_ARG;
+    int64_t gs = group_size ? group_size : K;
+    int64_t G = K / gs;
+    float qmax = bits == 8 ? 127.0f : 7.0f;
+    int lo = bits == 8 ? -127 : -8, hi = bits == 8 ? 127 : 7;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        int qbuf[K];
+        for (int64_t g = 0; g < G; ++g)
+            s_w[n * G + g] = quantize_run(w + n * K + g * gs, gs, qmax, lo, hi,
+                                          qbuf + g * gs);
+        if (bits == 8) {
+            for (int64_t k = 0; k < K; ++k)
+                wq[n * K + k] = (uint8_t)(int8_t)qbuf[k];
+        } else {
+            for (int64_t j = 0; j < K / 2; ++j) {
+                int u_even = qbuf[2 * j] + 8;      /* zero-point 8 */
+                int u_odd = qbuf[2 * j + 1] + 8;
+                wq[n * (K / 2) + j] = (uint8_t)(u_even | (u_odd << 4));
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------ accumulation --- */
+
+/* Weight code at (n, k) of a quantized weight, as a signed integer. */
+static int weight_code(const uint8_t *wq, int bits, int64_t K, int64_t n, int64_t k)
+{
+    if (bits == 8)
+        return (int8_t)wq[n * K + k];
+    uint8_t b = wq[n * (K / 2) + k / 2];
+    int u = (k % 2 == 0) ? (b & 0xf) : (b >> 4);
+    return u - 8;                                  /* zero-point 8 */
+}
+
+/* sum over k in [k0, k1) of xrow[k] * w[n, k], exact in int64. */
+static int64_t dot_range(const int8_t *xrow, const uint8_t *wq, int bits, int64_t K,
+                         int64_t n, int64_t k0, int64_t k1)
+{
+    int64_t s = 0;
+    for (int64_t k = k0; k < k1; ++k)
+        s += (int64_t)xrow[k] * weight_code(wq, bits, K, n, k);
+    return s;
+}
+
+/* Integer accumulators acc[m, n, g] = sum over k in group g of xq[m,k]*w[n,k].
+   acc int32 [M, N, G] with G = 1 (group_size 0) or K / group_size.
+   The sums are formed in int64 and must fit int32. */
+int oracle_gemm_acc(const int8_t *xq, const uint8_t *wq, int bits, int64_t M,
+                    int64_t N, int64_t K, int group_size, int32_t *acc)
+{
+    if (!xq || !wq || !acc || M < 0 || N < 0 || !shape_ok(K, bits, group_size))
+        return ORACLE_BAD_ARG;
+    int64_t gs = group_size ? group_size : K;
+    int64_t G = K / gs;
+    int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t g = 0; g < G; ++g) {
+                int64_t s = dot_range(xq + m * K, wq, bits, K, n, g * gs, (g + 1) * gs);
+                if (s > INT32_MAX || s < INT32_MIN)
+                    overflow = 1;
+                acc[(m * N + n) * G + g] = (int32_t)s;
+            }
+        }
+    }
+    return overflow ? ORACLE_OVERFLOW : ORACLE_OK;
+}
+
+/* ------------------------------------------------------------ dequant --- */
+
+/* fp16( s_tok * sum_g s_w[g] * acc[g] ), evaluated in fp64.  With G = 1 this
+   is acc * s_tok * s_w, the per-channel form of the 'Output dequant' row. */
+static uint16_t dequant_one(float s_tok, const float *s_w_row, const int32_t *acc_row,
+                            int64_t G)
+{
+    double t = 0.0;
+    for (int64_t g = 0; g < G; ++g)
+        t += (double)s_w_row[g] * (double)acc_row[g];
+    return oracle_double_to_half((double)s_tok * t);
+}
+
+/* y fp16 [M, N] from acc int32 [M, N, G], s_tok [M], s_w [N, G]. */
+int oracle_dequant(const int32_t *acc, const float *s_tok, const float *s_w,
+                   int64_t M, int64_t N, int64_t G, uint16_t *y)
+{
+    if (!acc || !s_tok || !s_w || !y || M < 0 || N < 0 || G <= 0)
+        return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            y[m * N + n] = dequant_one(s_tok[m], s_w + n * G, acc + (m * N + n) * G, G);
+    return ORACLE_OK;
+}
+
+/* --------------------------------------------------------- whole path --- */
+
+/* X fp16 [M, K] (row stride ldx) through quantize_act, the integer product
+   with an already-quantized weight and the dequant, one row at a time.
+   xq / s_tok receive the quantized activations; y fp16 [M, N]. */
+int oracle_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                  const uint8_t *wq, const float *s_w, int bits, int64_t N,
+                  int group_size, int8_t *xq, float *s_tok, uint16_t *y)
+{
+    if (!x || !wq || !s_w || !xq || !s_tok || !y || M < 0 || N < 0 || ldx < K ||
+        !shape_ok(K, bits, group_size))
+        return ORACLE_BAD_ARG;
+    int64_t gs = group_size ? group_size : K;
+    int64_t G = K / gs;
+    int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+    for (int64_t m = 0; m < M; ++m) {
+        int qbuf[K];
+        int32_t accs[G];
+        s_tok[m] = quantize_run(x + m * ldx, K, 127.0f, -127, 127, qbuf);
+        for (int64_t k = 0; k < K; ++k)
+            xq[m * K + k] = (int8_t)qbuf[k];
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t g = 0; g < G; ++g) {
+                int64_t s = dot_range(xq + m * K, wq, bits, K, n, g * gs, (g + 1) * gs);
+                if (s > INT32_MAX || s < INT32_MIN)
+                    overflow = 1;
+                accs[g] = (int32_t)s;
+            }
+            y[m * N + n] = dequant_one(s_tok[m], s_w + n * G, accs, G);
+        }
+    }
+    return overflow ? ORACLE_OVERFLOW : ORACLE_OK;
+}
+
+/* Threads the OpenMP loops above use. */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
