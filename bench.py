@@ -1,0 +1,307 @@
+"""Benchmark of the fused quantized linear layer on one MI355X.
+
+Headline workload: W8A8 per-channel, N=10240, K=2560, M=4096 tokens (the
+operator sweep's [N=10240, K=2560] shape of the Cider pages, at M=4096).
+One step = the whole layer on fp16 activations already resident in HBM:
+per-token quantization (cider_quantize_act) followed by the int8 matrix-core
+product with fused dequantization (cider_w8a8_gemm) -- exactly what
+cider_w8a8_linear runs, issued as its two calls so the product kernel can be
+timed on its own with HIP events recorded on the launch stream.
+
+`value` is INT8 TOPS of the whole step (2*M*N*K / step time).  The JSON line
+also carries: the roofline of the product kernel (achieved TOPS from the
+kernel's event-timed duration against the 5.0 POPS dense INT8 peak), the
+oracle's CPU throughput on a bounded sample of the same workload, the
+one-token path's GB/s against 8 TB/s, and a sweep over the operator
+workloads.  Inputs are rotated over >= 1 GB of copies so that the 256 MB
+last-level cache cannot serve them.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 matrix throughput, TOP/s
+PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E bandwidth, GB/s
+ROTATE_BYTES = 1 << 30       # working-set copies cycled through per step
+PAGES_M5PRO_PC_M4096_MS = 4.41  # the pages' per-channel latency at M=4096, [10240 x 2560], Apple M5 Pro
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+class Layer:
+    """Device buffers for one (mode, N, K, M) workload, `copies` times over."""
+
+    def __init__(self, torch, cider, bits, gs, N, K, M, x_np, w_np, copies):
+        self.torch, self.cider = torch, cider
+        self.bits, self.gs, self.N, self.K, self.M = bits, gs, N, K, M
+        dev = "cuda"
+        x = torch.from_numpy(x_np.view("int16")).to(dev).view(torch.float16)
+        w = torch.from_numpy(w_np.view("int16")).to(dev).view(torch.float16)
+        G = 1 if gs == 0 else K // gs
+        self.sets = []
+        for _ in range(copies):
+            wq = torch.empty((N, K) if bits == 8 else (N, K // 2),
+                             dtype=torch.int8 if bits == 8 else torch.uint8, device=dev)
+            sw = torch.empty((N,) if gs == 0 else (N, G), dtype=torch.float32, device=dev)
+            cider.cider_quantize_weight(w, N, K, bits, gs, wq, sw)
+            self.sets.append(dict(
+                x=x.clone(), wq=wq, sw=sw,
+                xq=torch.empty((M, K), dtype=torch.int8, device=dev),
+                st=torch.empty((M,), dtype=torch.float32, device=dev),
+                y=torch.empty((M, N), dtype=torch.float16, device=dev)))
+        del x, w
+
+    def quantize(self, i):
+        s = self.sets[i % len(self.sets)]
+        self.cider.cider_quantize_act(s["x"], self.M, self.K, self.K, s["xq"], s["st"])
+
+    def gemm(self, i):
+        s = self.sets[i % len(self.sets)]
+        f = self.cider.cider_w8a8_gemm if self.bits == 8 else self.cider.cider_w4a8_gemm
+        f(s["xq"], s["st"], s["wq"], s["sw"], self.M, self.N, self.K, self.gs, s["y"])
+
+    def linear(self, i):
+        s = self.sets[i % len(self.sets)]
+        if self.M == 1:  # quantization fused into the one-token kernel, no workspace
+            f = self.cider.cider_w8a8_linear if self.bits == 8 else self.cider.cider_w4a8_linear
+            f(s["x"], 1, self.K, self.K, s["wq"], s["sw"], self.N, self.gs, None, 0, s["y"])
+        else:
+            self.quantize(i)
+            self.gemm(i)
+
+
+def alg_bytes(bits, gs, N, K, M):
+    """Bytes the layer must move: X fp16 read once, weight codes, weight
+    scales, token scales, Y fp16 written once."""
+    G = 1 if gs == 0 else K // gs
+    wbytes = N * K if bits == 8 else N * K // 2
+    return 2 * M * K + wbytes + 4 * N * G + 4 * M + 2 * M * N
+
+
+def copies_for(bits, gs, N, K, M):
+    per = alg_bytes(bits, gs, N, K, M) + M * K
+    return max(1, min(64, math.ceil(ROTATE_BYTES / per)))
+
+
+def time_events(torch, fn, n, start_index=0):
+    """Average device duration of fn(i) over n launches, one HIP event pair
+    per launch on the current stream; returns seconds."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(start_index + i)
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / n / 1e3
+
+
+def traffic_record(kernel_source, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload)
+    if not rec:
+        return None
+    with open(kernel_source, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(M, N, K, x_np, w_np, budget_s):
+    """The oracle (as it stands) on the first rows of the same workload:
+    quantize_act + int8 product + dequant per row, timed on the host cores."""
+    from oracle.oracle import get as get_oracle
+    orc = get_oracle()
+    wq, sw = orc.quantize_weight(w_np, 8, 0)
+    t0 = time.perf_counter()
+    orc.linear(x_np[:1], wq, sw)
+    per_row = time.perf_counter() - t0
+    threads = orc.num_threads()  # rows are split across these OpenMP threads
+    rows = int(max(1, min(M, budget_s * threads / max(per_row, 1e-6))))
+    t0 = time.perf_counter()
+    orc.linear(x_np[:rows], wq, sw)
+    dt = time.perf_counter() - t0
+    return {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "first %d of %d tokens of W8A8 per-channel N=%d K=%d: quantize_act + "
+                      "int8 product + dequant, %.2f s wall" % (rows, M, N, K, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this layer has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth_inputs as si
+    import w4a8_quantized_linear_amd as cider
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cider.load(build_if_missing=True)
+    assert cider.cider_is_available(), "libcider.so reports no usable gfx950 device"
+
+    # ---------------------------------------------------------- headline ---
+    M, N, K = 4096, 10240, 2560
+    log("generating inputs M=%d N=%d K=%d" % (M, N, K))
+    x_np = si.activations(M, K)
+    w_np = si.weights(N, K)
+    B = copies_for(8, 0, N, K, M)
+    L = Layer(torch, cider, 8, 0, N, K, M, x_np, w_np, B)
+    ops = 2.0 * M * N * K
+    for i in range(args.warmup):
+        L.linear(i)
+    torch.cuda.synchronize()
+    log("timing %d steps (%d rotating copies)" % (args.steps, B))
+    gemm_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    quant_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        quant_ev[i][0].record()
+        L.quantize(i)
+        quant_ev[i][1].record()
+        gemm_ev[i][0].record()
+        L.gemm(i)
+        gemm_ev[i][1].record()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    gemm_s = sum(a.elapsed_time(b) for a, b in gemm_ev) / args.steps / 1e3
+    quant_s = sum(a.elapsed_time(b) for a, b in quant_ev) / args.steps / 1e3
+    ms_per_step = dt / args.steps * 1e3
+    value = ops / (dt / args.steps) / 1e12
+    achieved = ops / gemm_s / 1e12
+    log("step %.2f us, gemm kernel %.2f us (%.0f TOPS), quantize kernel %.2f us"
+        % (ms_per_step * 1e3, gemm_s * 1e6, achieved, quant_s * 1e6))
+    traffic = traffic_record(os.path.join(ROOT, "w4a8_quantized_linear_amd", "csrc", "gemm.hip"),
+                             "w8a8_pc_N10240_K2560_M4096")
+    result = {
+        "metric": "INT8 TOPS (% of MFMA peak) at M=4096; GB/s (% of HBM peak) at M=1",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / (ops / (PAGES_M5PRO_PC_M4096_MS * 1e-3) / 1e12), 2),
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "W8A8 per-channel linear, N=10240 K=2560 M=4096 "
+                               "(fp16 X ~N(0,1) with 1% outlier columns x20, W ~0.02*N(0,1), seed 0)",
+                   "M": M, "N": N, "K": K, "group_size": 0, "weight_bits": 8,
+                   "step": "cider_quantize_act + cider_w8a8_gemm",
+                   "rotating_copies": B},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
+                     "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "traffic": traffic, "kernel": "gemm_kernel (int8 matrix-core product)",
+                     "kernel_us": round(gemm_s * 1e6, 2),
+                     "quantize_kernel_us": round(quant_s * 1e6, 2)},
+    }
+    del L
+    torch.cuda.empty_cache()
+
+    # --------------------------------------------------------- one token ---
+    x1 = x_np[:1]
+    B1 = copies_for(8, 0, N, K, 1)
+    L1 = Layer(torch, cider, 8, 0, N, K, 1, x1, w_np, B1)
+    for i in range(20):
+        L1.linear(i)
+    s1 = time_events(torch, L1.linear, 200, 20)
+    b1 = alg_bytes(8, 0, N, K, 1)
+    result["m1"] = {"workload": "W8A8 per-channel N=10240 K=2560 M=1, quantization fused",
+                    "kernel_us": round(s1 * 1e6, 3), "bytes": b1,
+                    "gbps": round(b1 / s1 / 1e9, 1),
+                    "frac": round(b1 / s1 / 1e9 / PEAK_HBM_GBPS, 4),
+                    "rotating_copies": B1}
+    log("M=1: %.2f us, %.0f GB/s" % (s1 * 1e6, b1 / s1 / 1e9))
+    del L1
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------- sweep ---
+    if not args.no_sweep:
+        sweep = []
+        for name, wl in si.WORKLOADS.items():
+            if name == "w8a8_pc_small":
+                continue
+            Nw, Kw = wl["N"], wl["K"]
+            xs = si.activations(max(wl["M"]), Kw)
+            ws = si.weights(Nw, Kw)
+            for gs in wl["group_sizes"]:
+                for Mw in wl["M"]:
+                    Bw = copies_for(wl["bits"], gs, Nw, Kw, Mw)
+                    Lw = Layer(torch, cider, wl["bits"], gs, Nw, Kw, Mw, xs[:Mw], ws, Bw)
+                    for i in range(5):
+                        Lw.linear(i)
+                    reps = 50 if Mw <= 1024 else 20
+                    e2e = time_events(torch, Lw.linear, reps, 5)
+                    gemm = time_events(torch, Lw.gemm, reps, 5) if Mw > 1 else None
+                    ab = alg_bytes(wl["bits"], gs, Nw, Kw, Mw)
+                    opw = 2.0 * Mw * Nw * Kw
+                    rec = {"workload": name, "group_size": gs, "M": Mw, "N": Nw, "K": Kw,
+                           "e2e_us": round(e2e * 1e6, 2),
+                           "e2e_tops": round(opw / e2e / 1e12, 2),
+                           "e2e_gbps": round(ab / e2e / 1e9, 1)}
+                    if gemm is not None:
+                        rec.update({"gemm_us": round(gemm * 1e6, 2),
+                                    "gemm_tops": round(opw / gemm / 1e12, 2),
+                                    "gemm_frac_mfma": round(opw / gemm / 1e12 / PEAK_INT8_TOPS, 4)})
+                    rec["e2e_frac_hbm"] = round(ab / e2e / 1e9 / PEAK_HBM_GBPS, 4)
+                    sweep.append(rec)
+                    log("sweep %s gs=%d M=%d: e2e %.2f us (%.1f TOPS, %.0f GB/s)%s"
+                        % (name, gs, Mw, e2e * 1e6, opw / e2e / 1e12, ab / e2e / 1e9,
+                           "" if gemm is None else ", gemm %.2f us" % (gemm * 1e6)))
+                    del Lw
+                    torch.cuda.empty_cache()
+            del xs, ws
+        result["sweep"] = sweep
+
+    # -------------------------------------------------------- CPU oracle ---
+    if not args.no_cpu:
+        log("timing the oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(M, N, K, x_np, w_np, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * cider.h -- C ABI of the fused quantized linear layer for AMD Instinct MI355X
+ * (gfx950): online per-token INT8 activation quantization, INT8 x INT8 -> INT32
+ * matrix product on the matrix cores, and a fused dequantization to fp16.
+ *
+ * The operation (Cider README, ossradar.top repo page):
+ *   - "Modes" table: W8A8 = INT8 symmetric weights x INT8 per-token
+ *     activations; W4A8 = INT4 weights packed in uint8 x INT8 per-token
+ *     activations.
+ *   - "W8A8 Quantization Granularity" table: weights per output channel, or
+ *     per group of 64 / 128 input elements.
+ *   - "Quantization" table: symmetric INT8 activations per token, INT32
+ *     accumulation, output C_fp16 = C_int32 * s_act * s_weight per element;
+ *     W4A8 weights symmetric INT4 with zero-point 8.
+ *   - "Metal Kernel Pipeline": prefill quantizes FP16 activations to INT8 plus
+ *     per-token scales, then runs INT8 x INT8 -> INT32 -> FP16 with the scales
+ *     applied in the same kernel; a one-token call goes to a matrix-vector
+ *     kernel.
+ *   - "Low-Level API" / "Layer-level API": quantize_weight_int8(W) -> (w_int8,
+ *     scale), pack_weight_int4(W) -> (packed, scale), perchannel_linear(x, w,
+ *     scale), w4a8_linear(x, packed, scale); group_size = 0 means per channel.
+ *
+ * Definitions used by every call (the pages give the granularity, not the
+ * arithmetic; these are the readings this library implements):
+ *   scale      s = absmax / 127 (int8) or absmax / 7 (int4), fp32, correctly
+ *              rounded division; s = 0 for an all-zero row / group.
+ *   code       q = clamp(rint(x / s), -127, 127) (int8) or clamp(.., -8, 7)
+ *              (int4), x / s a correctly rounded fp32 division, rint rounding
+ *              half to even; q = 0 when s = 0.
+ *   int4 pack  nibble u = q + 8; byte j of a row holds k = 2j in bits 0..3
+ *              and k = 2j + 1 in bits 4..7.
+ *   product    acc[m, n] = sum_k xq[m, k] * q_w[n, k] in int32 (exact; needs
+ *              K * 127^2 < 2^31, i.e. K <= 133144).  Per group g of gs
+ *              elements: acc_g[m, n] = the same sum over k in [g*gs, (g+1)*gs).
+ *   output     per channel: y = fp16(acc * s_tok[m] * s_w[n]);
+ *              per group:   y = fp16(s_tok[m] * sum_g s_w[n, g] * acc_g),
+ *              evaluated in fp32 and rounded to nearest even.
+ *
+ * Layouts (all row-major, element strides in elements):
+ *   x      fp16 [M, K], row stride ldx >= K        (activations, tokens x in)
+ *   xq     int8 [M, K], row stride K               (quantized activations)
+ *   s_tok  fp32 [M]                                 (per-token scales)
+ *   w      fp16 [N, K]                              (nn.Linear weight, out x in)
+ *   wq     int8 [N, K]  (bits 8)  or  uint8 [N, K/2] packed (bits 4)
+ *   s_w    fp32 [N] (group_size 0) or [N, K/group_size] (group_size 64/128)
+ *   y      fp16 [M, N]
+ *
+ * Ownership and threading: every pointer is device memory owned by the
+ * caller; the library allocates, frees and synchronizes nothing.  Work is
+ * enqueued asynchronously on `stream` (a hipStream_t passed as void*; NULL is
+ * the default stream).  The library keeps no state between calls except the
+ * cached device check and the path override below; calls are thread-safe.
+ *
+ * Errors: every call checks its arguments on the host before touching the
+ * HIP runtime and returns a cider_status.  Nothing is launched when the
+ * status is not CIDER_OK, except CIDER_ERR_HIP (a launch failed).  Inputs
+ * are assumed finite; NaN or Inf inputs give unspecified codes.
+ *
+ * Envelope: M >= 0 (M = 0 is a no-op), N >= 0 with N % 64 == 0, K > 0 with
+ * K % 64 == 0 and K <= 133144, group_size in {0, 64, 128} for W8A8 and 0 for
+ * W4A8; device pointers 16-byte aligned; ldx % 8 == 0.
+ */
+#ifndef CIDER_H
+#define CIDER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CIDER_OK = 0,
+    CIDER_ERR_INVALID_ARG = 1,       /* null pointer, negative size, ldx < K, bits or group_size not allowed */
+    CIDER_ERR_UNSUPPORTED_SHAPE = 2, /* outside the envelope: K % 64, N % 64, K % group_size, K too large */
+    CIDER_ERR_MISALIGNED = 3,        /* a pointer not 16-byte aligned, or ldx % 8 != 0 */
+    CIDER_ERR_NO_DEVICE = 4,         /* no usable gfx950 device (or CIDER_FORCE_UNAVAILABLE=1) */
+    CIDER_ERR_HIP = 5,               /* the HIP runtime reported an error at launch */
+    CIDER_ERR_WORKSPACE = 6          /* workspace missing or smaller than cider_linear_workspace_bytes */
+} cider_status;
+
+/* 1 if the current HIP device is a gfx950 GPU that the library can use, else 0.
+   Never crashes: returns 0 when the runtime finds no device.  The environment
+   variable CIDER_FORCE_UNAVAILABLE=1 makes it return 0 (a test hook for the
+   degrade-gracefully behaviour of Cider README "Conditional Compilation"). */
+int cider_is_available(void);
+
+/* Static English text for a status code (never NULL). */
+const char *cider_status_str(int status);
+
+/* Weight quantization (Cider README "Low-Level API": quantize_weight_int8,
+   pack_weight_int4; "Quantization" table).
+   w: fp16 [N, K].  bits 8: wq int8 [N, K]; bits 4: wq uint8 [N, K/2] packed.
+   group_size 0: s_w fp32 [N]; 64 or 128 (bits 8 only): s_w fp32 [N, K/gs]. */
+cider_status cider_quantize_weight(const void *w_f16, int64_t N, int64_t K, int bits,
+                                   int group_size, void *wq, float *s_w, void *stream);
+
+/* Per-token activation quantization (Cider README "Metal Kernel Pipeline",
+   step quantize_per_token; "Quantization" table, Activations row).
+   x: fp16 [M, K] with row stride ldx.  xq: int8 [M, K]; s_tok: fp32 [M]. */
+cider_status cider_quantize_act(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
+                                int8_t *xq, float *s_tok, void *stream);
+
+/* W8A8 product with fused dequantization (Cider README "Metal Kernel
+   Pipeline", step matmul_fused_dequant; "TensorOps matmul2d"; "W8A8
+   Quantization Granularity").  group_size 0: per-channel s_w [N];
+   64 / 128: per-group s_w [N, K/gs].  y: fp16 [M, N].
+   M = 1 runs the matrix-vector kernel, larger M the matrix-core kernel. */
+cider_status cider_w8a8_gemm(const int8_t *xq, const float *s_tok, const int8_t *wq,
+                             const float *s_w, int64_t M, int64_t N, int64_t K,
+                             int group_size, void *y_f16, void *stream);
+
+/* W4A8 product (Cider README "Modes": Unpack -> TensorOps; "Metal Kernel
+   Pipeline": INT4 -> INT8 unpacking before the INT8 product).
+   wq4: uint8 [N, K/2] packed nibbles; s_w fp32 [N]; group_size must be 0. */
+cider_status cider_w4a8_gemm(const int8_t *xq, const float *s_tok, const uint8_t *wq4,
+                             const float *s_w, int64_t M, int64_t N, int64_t K,
+                             int group_size, void *y_f16, void *stream);
+
+/* Test hooks: the same kernels with the dequant epilogue replaced by a raw
+   store of the int32 accumulators ("Quantization" table, Accumulation INT32):
+   acc int32 [M, N] (group_size 0) or [M, N, K/gs] (one sum per group). */
+cider_status cider_w8a8_gemm_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N,
+                                 int64_t K, int group_size, int32_t *acc, void *stream);
+cider_status cider_w4a8_gemm_i32(const int8_t *xq, const uint8_t *wq4, int64_t M, int64_t N,
+                                 int64_t K, int group_size, int32_t *acc, void *stream);
+
+/* Bytes of device workspace cider_w8a8_linear / cider_w4a8_linear need for M
+   tokens of K features (the int8 activations and their scales). */
+size_t cider_linear_workspace_bytes(int64_t M, int64_t K);
+
+/* The whole layer on fp16 activations, mirroring perchannel_linear(x, w, s)
+   and w4a8_linear(x, packed, s) of Cider README "Low-Level API":
+   quantize_act into `workspace`, then the product.  For M = 1 the quantization
+   is fused into the matrix-vector kernel and the workspace is not touched.
+   x: fp16 [M, K] row stride ldx; y: fp16 [M, N]. */
+cider_status cider_w8a8_linear(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
+                               const int8_t *wq, const float *s_w, int64_t N, int group_size,
+                               void *workspace, size_t workspace_bytes, void *y_f16,
+                               void *stream);
+cider_status cider_w4a8_linear(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
+                               const uint8_t *wq4, const float *s_w, int64_t N, int group_size,
+                               void *workspace, size_t workspace_bytes, void *y_f16,
+                               void *stream);
+
+/* Test hook: force the product path for subsequent calls in this process.
+   0 = automatic (M = 1 with K <= 32768 -> matrix-vector, else matrix cores),
+   1 = always the matrix-vector kernel (calls with M > 8 or M * K > 32768 then
+   return CIDER_ERR_UNSUPPORTED_SHAPE), 2 = always the matrix-core kernel.
+   Returns the previous setting, or -1 for an invalid value. */
+int cider_set_path(int path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CIDER_H */

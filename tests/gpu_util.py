@@ -1,0 +1,114 @@
+"""Helpers for the GPU parity tests: device copies, the tolerance check and
+running the layer through the C ABI.  Imports torch lazily."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import w4a8_quantized_linear_amd as cider
+
+TOL_ABS = 1e-3
+TOL_REL = 2.0 ** -10
+
+
+def announce(msg: str):
+    sys.__stderr__.write("[gpu] %s\n" % msg)
+    sys.__stderr__.flush()
+
+
+def to_dev(a: np.ndarray):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.float16)
+    return torch.from_numpy(a).cuda()
+
+
+def to_host(t) -> np.ndarray:
+    import torch
+    t = t.detach()
+    if t.dtype == torch.float16:
+        return t.view(torch.int16).cpu().numpy().view(np.float16)
+    return t.cpu().numpy()
+
+
+def empty(shape, dtype):
+    import torch
+    return torch.empty(shape, dtype=dtype, device="cuda")
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def assert_f16_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
+    """|got - ref| <= 1e-3 + 2^-10 |ref| elementwise, NaN / Inf patterns equal."""
+    g = got.astype(np.float64)
+    r = ref.astype(np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    assert np.array_equal(np.isnan(g), np.isnan(r)), what + ": NaN pattern differs"
+    inf = np.isinf(r)
+    assert np.array_equal(np.isinf(g), inf) and np.array_equal(g[inf], r[inf]), what + ": Inf differs"
+    fin = ~(np.isnan(r) | inf)
+    err = np.abs(g[fin] - r[fin])
+    bound = TOL_ABS + TOL_REL * np.abs(r[fin])
+    bad = err > bound
+    if bad.any():
+        i = np.argmax(err / bound)
+        raise AssertionError("%s: %d of %d outputs outside tolerance, worst |d|=%.3g at ref=%.6g "
+                             "(ratio %.3g)" % (what, int(bad.sum()), bad.size, err[i], r[fin][i],
+                                               err[i] / bound[i]))
+
+
+def quantize_weight_gpu(w: np.ndarray, bits: int, gs: int):
+    """Quantize an fp16 [N, K] weight on the GPU; returns device (wq, s_w)."""
+    import torch
+    N, K = w.shape
+    wd = to_dev(w)
+    wq = empty((N, K) if bits == 8 else (N, K // 2), torch.int8 if bits == 8 else torch.uint8)
+    sw = empty((N,) if gs == 0 else (N, K // gs), torch.float32)
+    cider.cider_quantize_weight(wd, N, K, bits, gs, wq, sw)
+    return wq, sw
+
+
+def quantize_act_gpu(xd, M, K, ldx):
+    import torch
+    xq = empty((M, K), torch.int8)
+    st = empty((M,), torch.float32)
+    cider.cider_quantize_act(xd, M, K, ldx, xq, st)
+    return xq, st
+
+
+def gemm_gpu(xq, st, wq, sw, M, N, K, bits, gs):
+    import torch
+    y = empty((M, N), torch.float16)
+    f = cider.cider_w8a8_gemm if bits == 8 else cider.cider_w4a8_gemm
+    f(xq, st, wq, sw, M, N, K, gs, y)
+    return y
+
+
+def gemm_i32_gpu(xq, wq, M, N, K, bits, gs):
+    import torch
+    G = 1 if gs == 0 else K // gs
+    acc = empty((M, N) if gs == 0 else (M, N, G), torch.int32)
+    f = cider.cider_w8a8_gemm_i32 if bits == 8 else cider.cider_w4a8_gemm_i32
+    f(xq, wq, M, N, K, gs, acc)
+    return acc
+
+
+def linear_gpu(xd, M, K, ldx, wq, sw, N, bits, gs):
+    import torch
+    ws_bytes = cider.cider_linear_workspace_bytes(M, K)
+    ws = empty((max(ws_bytes, 16),), torch.uint8)
+    y = empty((M, N), torch.float16)
+    f = cider.cider_w8a8_linear if bits == 8 else cider.cider_w4a8_linear
+    f(xd, M, K, ldx, wq, sw, N, gs, ws, ws_bytes, y)
+    return y
+
+
+def cosine(a: np.ndarray, b: np.ndarray) -> float:
+    a = a.astype(np.float64).ravel()
+    b = b.astype(np.float64).ravel()
+    return float(a @ b / np.sqrt((a @ a) * (b @ b)))

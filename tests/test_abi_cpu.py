@@ -1,0 +1,145 @@
+"""The C ABI on the host: the library loads, exports every entry point the
+header declares, and rejects bad arguments with the documented status before
+any HIP call.  No kernel is ever launched here: CIDER_FORCE_UNAVAILABLE=1 is
+set for the whole module, so a call with valid arguments stops at the device
+check (CIDER_ERR_NO_DEVICE) even on a machine with a GPU.  Pointers passed
+are fake integers that are never dereferenced."""
+import os
+import re
+
+import pytest
+
+import w4a8_quantized_linear_amd as cider
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cider.h")
+
+P = 0x10000          # a 16-byte aligned fake device address
+P2 = 0x20000
+P3 = 0x30000
+P4 = 0x40000
+BAD = 0x10008        # 8-byte aligned only
+
+
+@pytest.fixture(autouse=True)
+def _no_device(monkeypatch):
+    monkeypatch.setenv("CIDER_FORCE_UNAVAILABLE", "1")
+    cider.cider_set_path(cider.PATH_AUTO)
+    yield
+    cider.cider_set_path(cider.PATH_AUTO)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cider_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    lib = cider.load()
+    names = _declared()
+    assert len(names) >= 12
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(cider.EXPORTS) == names
+
+
+def test_unavailable_without_device():
+    assert cider.cider_is_available() is False
+
+
+def test_status_strings():
+    for s in range(7):
+        assert cider.cider_status_str(s) not in ("", "unknown status")
+    assert cider.cider_status_str(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    assert cider.cider_linear_workspace_bytes(0, 64) == 0
+    assert cider.cider_linear_workspace_bytes(3, 64) == 256 + 256
+    assert cider.cider_linear_workspace_bytes(4096, 2560) == 4096 * 2560 + 16384
+
+
+def test_set_path():
+    assert cider.cider_set_path(2) == 0
+    assert cider.cider_set_path(1) == 2
+    assert cider.cider_set_path(7) == -1
+    assert cider.cider_set_path(0) == 1
+
+
+def _gemm(**kw):
+    a = dict(xq=P, s_tok=P2, wq=P3, s_w=P4, M=16, N=128, K=256, group_size=0, y_f16=P, check=False)
+    a.update(kw)
+    return cider.cider_w8a8_gemm(a["xq"], a["s_tok"], a["wq"], a["s_w"], a["M"], a["N"], a["K"],
+                                 a["group_size"], a["y_f16"], stream=0, check=False)
+
+
+def test_gemm_argument_codes():
+    assert _gemm() == cider.CIDER_ERR_NO_DEVICE
+    assert _gemm(M=-1) == cider.CIDER_ERR_INVALID_ARG
+    assert _gemm(K=0) == cider.CIDER_ERR_INVALID_ARG
+    assert _gemm(group_size=32) == cider.CIDER_ERR_INVALID_ARG
+    assert _gemm(K=96) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
+    assert _gemm(N=100) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
+    assert _gemm(K=192, group_size=128) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
+    assert _gemm(K=133248) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
+    assert _gemm(xq=None) == cider.CIDER_ERR_INVALID_ARG
+    assert _gemm(s_w=None) == cider.CIDER_ERR_INVALID_ARG
+    assert _gemm(xq=BAD) == cider.CIDER_ERR_MISALIGNED
+    assert _gemm(y_f16=BAD) == cider.CIDER_ERR_MISALIGNED
+    # empty problems are a no-op that needs neither pointers nor a device
+    assert _gemm(M=0, xq=None, wq=None, y_f16=None) == cider.CIDER_OK
+    assert _gemm(N=0, xq=None) == cider.CIDER_OK
+
+
+def test_w4a8_argument_codes():
+    f = cider.cider_w4a8_gemm
+    assert f(P, P2, P3, P4, 8, 64, 128, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert f(P, P2, P3, P4, 8, 64, 128, 64, P, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    g = cider.cider_w4a8_gemm_i32
+    assert g(P, P3, 8, 64, 128, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert g(P, BAD, 8, 64, 128, 0, P, stream=0, check=False) == cider.CIDER_ERR_MISALIGNED
+
+
+def test_i32_hooks_need_no_scales():
+    f = cider.cider_w8a8_gemm_i32
+    assert f(P, P3, 8, 64, 128, 64, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert f(P, None, 8, 64, 128, 0, P, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+
+
+def test_quantize_argument_codes():
+    qa = cider.cider_quantize_act
+    assert qa(P, 4, 256, 256, P2, P3, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert qa(P, 4, 256, 128, P2, P3, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    assert qa(P, 4, 256, 260, P2, P3, stream=0, check=False) == cider.CIDER_ERR_MISALIGNED
+    assert qa(P, 4, 200, 256, P2, P3, stream=0, check=False) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
+    assert qa(P, 0, 256, 256, None, None, stream=0, check=False) == cider.CIDER_OK
+    qw = cider.cider_quantize_weight
+    assert qw(P, 64, 256, 8, 0, P2, P3, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert qw(P, 64, 256, 8, 128, P2, P3, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert qw(P, 64, 256, 4, 64, P2, P3, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    assert qw(P, 64, 256, 6, 0, P2, P3, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    assert qw(P, 64, 320, 8, 128, P2, P3, stream=0, check=False) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
+
+
+def test_linear_argument_codes():
+    f = cider.cider_w8a8_linear
+    ws = cider.cider_linear_workspace_bytes(16, 256)
+    assert f(P, 16, 256, 256, P2, P3, 128, 0, P4, ws, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert f(P, 16, 256, 256, P2, P3, 128, 0, P4, ws - 1, P, stream=0, check=False) == cider.CIDER_ERR_WORKSPACE
+    assert f(P, 16, 256, 256, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_WORKSPACE
+    assert f(P, 16, 256, 200, P2, P3, 128, 0, P4, ws, P, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    # one token: quantization fused into the matrix-vector kernel, no workspace needed
+    assert f(P, 1, 256, 256, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+
+
+def test_forced_gemv_range():
+    assert cider.cider_set_path(cider.PATH_GEMV) == 0
+    assert _gemm(M=8, K=4096) == cider.CIDER_ERR_NO_DEVICE
+    assert _gemm(M=9) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
+    assert _gemm(M=2, K=32768 - 64 + 64 * 256) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
+
+
+def test_raises_with_check():
+    with pytest.raises(cider.CiderError):
+        cider.cider_w8a8_gemm(P, P2, P3, P4, 4, 64, 96, 0, P, stream=0)

@@ -1,0 +1,312 @@
+// C ABI of the fused quantized linear layer (declared in include/cider.h).
+//
+// Host side only: argument checks (all before the first HIP call), the
+// device check, the choice between the matrix-vector and the matrix-core
+// kernel (Cider README, ossradar.top repo page, "Quick Start": seq_len > 1 ->
+// INT8 GEMM, seq_len == 1 -> INT8 MV kernel), and the launches on the
+// caller's stream.  No allocation, no synchronization.
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "cider.h"
+#include "cider_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxK = 133144;       // K * 127^2 < 2^31
+constexpr int64_t kGemvMaxBytes = 32768;  // M * K int8 codes held in LDS
+
+std::atomic<int> g_path{0};
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// 1: usable gfx950 device current; 0: not.  Cached per device id.
+int device_usable()
+{
+    const char *force = std::getenv("CIDER_FORCE_UNAVAILABLE");
+    if (force && force[0] == '1')
+        return 0;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    static std::atomic<int> cache[64];  // 0 unknown, 1 usable, 2 not usable
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c)
+            return c == 1;
+    }
+    hipDeviceProp_t prop;
+    int ok = 0;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess)
+        ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    else
+        (void)hipGetLastError();
+    if (dev < 64)
+        cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok;
+}
+
+cider_status from_hip(hipError_t e) { return e == hipSuccess ? CIDER_OK : CIDER_ERR_HIP; }
+
+// Shape / mode checks shared by the product calls.
+cider_status check_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size)
+{
+    if (M < 0 || N < 0 || K <= 0)
+        return CIDER_ERR_INVALID_ARG;
+    if (bits != 8 && bits != 4)
+        return CIDER_ERR_INVALID_ARG;
+    if (group_size != 0 && group_size != 64 && group_size != 128)
+        return CIDER_ERR_INVALID_ARG;
+    if (bits == 4 && group_size != 0)
+        return CIDER_ERR_INVALID_ARG;
+    if (K % 64 != 0 || K > kMaxK || N % 64 != 0)
+        return CIDER_ERR_UNSUPPORTED_SHAPE;
+    if (group_size && K % group_size != 0)
+        return CIDER_ERR_UNSUPPORTED_SHAPE;
+    return CIDER_OK;
+}
+
+enum Path { PATH_AUTO = 0, PATH_GEMV = 1, PATH_GEMM = 2 };
+
+// Which kernel serves M tokens of K features; CIDER_ERR_UNSUPPORTED_SHAPE
+// when the matrix-vector kernel is forced outside its range.
+cider_status pick_path(int64_t M, int64_t K, int *path)
+{
+    const int forced = g_path.load(std::memory_order_relaxed);
+    const bool gemv_ok = M <= 8 && M * K <= kGemvMaxBytes;
+    if (forced == PATH_GEMV) {
+        if (!gemv_ok)
+            return CIDER_ERR_UNSUPPORTED_SHAPE;
+        *path = PATH_GEMV;
+    } else if (forced == PATH_GEMM) {
+        *path = PATH_GEMM;
+    } else {
+        *path = (M == 1 && gemv_ok) ? PATH_GEMV : PATH_GEMM;
+    }
+    return CIDER_OK;
+}
+
+cider_status run_product(const int8_t *xq, const float *s_tok, const void *wq, const float *s_w,
+                         int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                         cider::OutKind kind, void *out, void *stream)
+{
+    cider_status st = check_shape(M, N, K, bits, group_size);
+    if (st != CIDER_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return CIDER_OK;
+    if (!xq || !wq || !out || (kind == cider::OUT_F16 && (!s_tok || !s_w)))
+        return CIDER_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(out) ||
+        (kind == cider::OUT_F16 && (!aligned16(s_w))))
+        return CIDER_ERR_MISALIGNED;
+    int path = PATH_GEMM;
+    st = pick_path(M, K, &path);
+    if (st != CIDER_OK)
+        return st;
+    if (!device_usable())
+        return CIDER_ERR_NO_DEVICE;
+    cider::ProductArgs a{};
+    a.xq = xq;
+    a.s_tok = s_tok;
+    a.wq = wq;
+    a.s_w = s_w;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.bits = bits;
+    a.group_size = group_size;
+    a.out_kind = kind;
+    a.out = out;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return from_hip(path == PATH_GEMV ? cider::launch_gemv(a, s) : cider::launch_gemm(a, s));
+}
+
+cider_status run_linear(const void *x, int64_t M, int64_t K, int64_t ldx, const void *wq,
+                        const float *s_w, int64_t N, int bits, int group_size, void *ws,
+                        size_t ws_bytes, void *y, void *stream)
+{
+    cider_status st = check_shape(M, N, K, bits, group_size);
+    if (st != CIDER_OK)
+        return st;
+    if (ldx < K)
+        return CIDER_ERR_INVALID_ARG;
+    if (M == 0 || N == 0)
+        return CIDER_OK;
+    if (!x || !wq || !s_w || !y)
+        return CIDER_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(wq) || !aligned16(s_w) || !aligned16(y) || ldx % 8 != 0)
+        return CIDER_ERR_MISALIGNED;
+    int path = PATH_GEMM;
+    st = pick_path(M, K, &path);
+    if (st != CIDER_OK)
+        return st;
+    const bool fused = path == PATH_GEMV && M == 1;
+    if (!fused) {
+        if (!ws || ws_bytes < cider_linear_workspace_bytes(M, K))
+            return CIDER_ERR_WORKSPACE;
+        if (!aligned16(ws))
+            return CIDER_ERR_MISALIGNED;
+    }
+    if (!device_usable())
+        return CIDER_ERR_NO_DEVICE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (fused)
+        return from_hip(cider::launch_gemv_fused(static_cast<const uint16_t *>(x), K, wq, s_w, N,
+                                                 bits, group_size, y, nullptr, nullptr, s));
+    int8_t *xq = static_cast<int8_t *>(ws);
+    float *s_tok = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + round256((size_t)(M * K)));
+    hipError_t e = cider::launch_quantize_rows(static_cast<const uint16_t *>(x), M, K, ldx, 8, xq,
+                                               s_tok, s);
+    if (e != hipSuccess)
+        return CIDER_ERR_HIP;
+    cider::ProductArgs a{};
+    a.xq = xq;
+    a.s_tok = s_tok;
+    a.wq = wq;
+    a.s_w = s_w;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.bits = bits;
+    a.group_size = group_size;
+    a.out_kind = cider::OUT_F16;
+    a.out = y;
+    return from_hip(path == PATH_GEMV ? cider::launch_gemv(a, s) : cider::launch_gemm(a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int cider_is_available(void) { return device_usable(); }
+
+const char *cider_status_str(int status)
+{
+    switch (status) {
+    case CIDER_OK: return "ok";
+    case CIDER_ERR_INVALID_ARG: return "invalid argument";
+    case CIDER_ERR_UNSUPPORTED_SHAPE: return "shape outside the supported envelope";
+    case CIDER_ERR_MISALIGNED: return "pointer or stride not 16-byte aligned";
+    case CIDER_ERR_NO_DEVICE: return "no usable gfx950 device";
+    case CIDER_ERR_HIP: return "HIP runtime error at launch";
+    case CIDER_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+    }
+}
+
+cider_status cider_quantize_weight(const void *w_f16, int64_t N, int64_t K, int bits,
+                                   int group_size, void *wq, float *s_w, void *stream)
+{
+    if (N < 0 || K <= 0 || (bits != 8 && bits != 4))
+        return CIDER_ERR_INVALID_ARG;
+    if (group_size != 0 && group_size != 64 && group_size != 128)
+        return CIDER_ERR_INVALID_ARG;
+    if (bits == 4 && group_size != 0)
+        return CIDER_ERR_INVALID_ARG;
+    if (K % 64 != 0 || K > kMaxK || (group_size && K % group_size != 0))
+        return CIDER_ERR_UNSUPPORTED_SHAPE;
+    if (N == 0)
+        return CIDER_OK;
+    if (!w_f16 || !wq || !s_w)
+        return CIDER_ERR_INVALID_ARG;
+    if (!aligned16(w_f16) || !aligned16(wq) || (reinterpret_cast<uintptr_t>(s_w) & 3u))
+        return CIDER_ERR_MISALIGNED;
+    if (!device_usable())
+        return CIDER_ERR_NO_DEVICE;
+    const int64_t len = group_size ? group_size : K;
+    const int64_t rows = N * (K / len);
+    return from_hip(cider::launch_quantize_rows(static_cast<const uint16_t *>(w_f16), rows, len,
+                                                len, bits, wq, s_w,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+cider_status cider_quantize_act(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
+                                int8_t *xq, float *s_tok, void *stream)
+{
+    if (M < 0 || K <= 0 || ldx < K)
+        return CIDER_ERR_INVALID_ARG;
+    if (K % 64 != 0 || K > kMaxK)
+        return CIDER_ERR_UNSUPPORTED_SHAPE;
+    if (M == 0)
+        return CIDER_OK;
+    if (!x_f16 || !xq || !s_tok)
+        return CIDER_ERR_INVALID_ARG;
+    if (!aligned16(x_f16) || !aligned16(xq) || ldx % 8 != 0 ||
+        (reinterpret_cast<uintptr_t>(s_tok) & 3u))
+        return CIDER_ERR_MISALIGNED;
+    if (!device_usable())
+        return CIDER_ERR_NO_DEVICE;
+    return from_hip(cider::launch_quantize_rows(static_cast<const uint16_t *>(x_f16), M, K, ldx, 8,
+                                                xq, s_tok, static_cast<hipStream_t>(stream)));
+}
+
+cider_status cider_w8a8_gemm(const int8_t *xq, const float *s_tok, const int8_t *wq,
+                             const float *s_w, int64_t M, int64_t N, int64_t K, int group_size,
+                             void *y_f16, void *stream)
+{
+    return run_product(xq, s_tok, wq, s_w, M, N, K, 8, group_size, cider::OUT_F16, y_f16, stream);
+}
+
+cider_status cider_w4a8_gemm(const int8_t *xq, const float *s_tok, const uint8_t *wq4,
+                             const float *s_w, int64_t M, int64_t N, int64_t K, int group_size,
+                             void *y_f16, void *stream)
+{
+    return run_product(xq, s_tok, wq4, s_w, M, N, K, 4, group_size, cider::OUT_F16, y_f16, stream);
+}
+
+cider_status cider_w8a8_gemm_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N,
+                                 int64_t K, int group_size, int32_t *acc, void *stream)
+{
+    return run_product(xq, nullptr, wq, nullptr, M, N, K, 8, group_size, cider::OUT_I32, acc,
+                       stream);
+}
+
+cider_status cider_w4a8_gemm_i32(const int8_t *xq, const uint8_t *wq4, int64_t M, int64_t N,
+                                 int64_t K, int group_size, int32_t *acc, void *stream)
+{
+    return run_product(xq, nullptr, wq4, nullptr, M, N, K, 4, group_size, cider::OUT_I32, acc,
+                       stream);
+}
+
+size_t cider_linear_workspace_bytes(int64_t M, int64_t K)
+{
+    if (M <= 0 || K <= 0)
+        return 0;
+    return round256((size_t)(M * K)) + round256((size_t)M * sizeof(float));
+}
+
+cider_status cider_w8a8_linear(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
+                               const int8_t *wq, const float *s_w, int64_t N, int group_size,
+                               void *workspace, size_t workspace_bytes, void *y_f16, void *stream)
+{
+    return run_linear(x_f16, M, K, ldx, wq, s_w, N, 8, group_size, workspace, workspace_bytes,
+                      y_f16, stream);
+}
+
+cider_status cider_w4a8_linear(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
+                               const uint8_t *wq4, const float *s_w, int64_t N, int group_size,
+                               void *workspace, size_t workspace_bytes, void *y_f16, void *stream)
+{
+    return run_linear(x_f16, M, K, ldx, wq4, s_w, N, 4, group_size, workspace, workspace_bytes,
+                      y_f16, stream);
+}
+
+int cider_set_path(int path)
+{
+    if (path < 0 || path > 2)
+        return -1;
+    return g_path.exchange(path);
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal launch interface between the C ABI (api.hip) and the gfx950
+// kernels.  Arguments arrive here already validated: sizes inside the
+// envelope documented in include/cider.h, pointers non-null and aligned.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cider {
+
+// Symmetric absmax quantization of `rows` rows of `len` fp16 values (row
+// stride `ld` elements).  bits 8: out int8 [rows, len]; bits 4: out uint8
+// [rows, len/2] packed nibbles.  scale fp32 [rows].  len % 8 == 0.
+// Per-token activations are rows = M, len = K; per-channel weights rows = N;
+// per-group weights are the [N * K/gs, gs] view of W.
+hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t len, int64_t ld,
+                                int bits, void *out, float *scale, hipStream_t stream);
+
+// Output of the product kernels.
+enum OutKind { OUT_F16 = 0, OUT_I32 = 1 };
+
+struct ProductArgs {
+    const int8_t *xq;      // [M, K]
+    const float *s_tok;    // [M]         (OUT_F16)
+    const void *wq;        // int8 [N, K] or packed uint8 [N, K/2]
+    const float *s_w;      // [N] or [N, K/gs] (OUT_F16)
+    int64_t M, N, K;
+    int bits;              // 8 or 4
+    int group_size;        // 0, 64 or 128
+    OutKind out_kind;
+    void *out;             // fp16 [M, N] or int32 [M, N] / [M, N, K/gs]
+};
+
+// Matrix-core product (any M >= 1).
+hipError_t launch_gemm(const ProductArgs &a, hipStream_t stream);
+
+// Matrix-vector product for M <= 8 and M * K <= 65536.
+hipError_t launch_gemv(const ProductArgs &a, hipStream_t stream);
+
+// One-token layer: quantizes the fp16 row x [K] inside the matrix-vector
+// kernel and writes y fp16 [N].  xq_out / s_tok_out may be null; when given,
+// the quantized row and its scale are written there as well.
+hipError_t launch_gemv_fused(const uint16_t *x, int64_t K, const void *wq, const float *s_w,
+                             int64_t N, int bits, int group_size, void *y, int8_t *xq_out,
+                             float *s_tok_out, hipStream_t stream);
+
+}  // namespace cider

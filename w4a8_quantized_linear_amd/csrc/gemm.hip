@@ -1,0 +1,395 @@
+// INT8 matrix-core product for the fused quantized linear layer on gfx950.
+//
+// What it computes (Cider README, ossradar.top repo page, "Quantization"
+// table and "Metal Kernel Pipeline"): acc[m, n] = sum_k xq[m, k] * q_w[n, k]
+// in int32, then y = fp16(acc * s_tok[m] * s_w[n]) in the same kernel
+// ("TensorOps matmul2d": dequantization applied in the store phase).  Per
+// group of 64/128 along K ("W8A8 Quantization Granularity"): each group's
+// int32 sum is scaled by s_w[n, g] and added into an fp32 accumulator.  W4A8
+// ("Modes": Unpack -> TensorOps): packed nibbles are widened to int8 codes
+// before the int8 product.
+//
+// Design for CDNA4 (the pages' M5 tiling is prior art only):
+//   * v_mfma_i32_16x16x64_i8: 16x16 int32 block, 64-deep K per instruction.
+//     The weight tile is the A operand and the activation tile the B
+//     operand, so a lane's four accumulators are four consecutive output
+//     columns n of one token m: the epilogue stores 8 contiguous bytes.
+//   * Tiles of TN x TM outputs per workgroup, WN x WM per wavefront, K
+//     staged BK at a time through LDS, double buffered: global loads of tile
+//     k+1 are in flight while the matrix cores consume tile k; one barrier
+//     per K tile.
+//   * LDS rows of BK bytes in 16-byte chunks, chunk c of row r stored at
+//     slot c ^ swz(r): the 16 rows a fragment read touches (same chunk) land
+//     in distinct bank groups, and so do the row-major tile writes.
+//   * W4A8: a 16-byte global chunk of packed nibbles becomes two 16-byte
+//     int8 chunks in LDS, once per workgroup; every wavefront then reads
+//     plain int8 fragments.
+//   * Workgroup -> tile mapping: consecutive workgroup ids go to different
+//     XCDs (round robin over 8), so ids are remapped to give every XCD a
+//     contiguous run of tiles, walked in groups of m-panels, so the tiles
+//     sharing an L2 also share weight and activation panels.
+#include "cider_kernels.h"
+
+namespace cider {
+namespace {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kXcds = 8;
+
+template <int BK>
+__device__ __forceinline__ int lds_offset(int row, int chunk)
+{
+    constexpr int CPR = BK / 16;  // 16-byte chunks per row
+    static_assert(CPR == 4 || CPR == 8, "BK must be 64 or 128");
+    const int swz = (CPR == 8) ? (row & 7) : ((row >> 1) & 3);
+    return row * BK + ((chunk ^ swz) << 4);
+}
+
+// Widen 8 packed nibbles (k = 0..7 of a uint32, low nibble = even k) to 8
+// int8 codes q = u - 8 in k order: two dwords.
+__device__ __forceinline__ void unpack_nibbles(uint32_t v, uint32_t &d0, uint32_t &d1)
+{
+    const uint32_t lo = v & 0x0F0F0F0Fu;          // u0 u2 u4 u6
+    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;   // u1 u3 u5 u7
+    // interleave to u0 u1 u2 u3 | u4 u5 u6 u7
+    uint32_t a = (lo & 0xFFu) | ((hi & 0xFFu) << 8) | ((lo & 0xFF00u) << 8) | ((hi & 0xFF00u) << 16);
+    uint32_t b = ((lo >> 16) & 0xFFu) | ((hi >> 8) & 0xFF00u) | (lo & 0xFF000000u) >> 8 |
+                 (hi & 0xFF000000u);
+    // u in [0, 15] -> u - 8 as a two's complement byte, without carries
+    // between bytes: (u + 0x78) stays below 0x100; flipping bit 7 then
+    // subtracts 0x80.
+    d0 = (a + 0x78787878u) ^ 0x80808080u;
+    d1 = (b + 0x78787878u) ^ 0x80808080u;
+}
+
+__device__ __forceinline__ void tile_coords(int pid, int tiles_n, int tiles_m, int group_m,
+                                            int &tn, int &tm)
+{
+    const int total = tiles_n * tiles_m;
+    int logical = pid;
+    if (total % kXcds == 0) {
+        const int per = total / kXcds;
+        logical = (pid % kXcds) * per + pid / kXcds;
+    }
+    const int in_group = group_m * tiles_n;
+    const int gid = logical / in_group;
+    const int first_m = gid * group_m;
+    const int gsize = min(tiles_m - first_m, group_m);
+    const int r = logical - gid * in_group;
+    tm = first_m + r % gsize;
+    tn = r / gsize;
+}
+
+template <int TN, int TM, int BK, int WN, int WM, int BITS, int GS, int OUT>
+__global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
+    ProductArgs args, int tiles_n, int tiles_m, int group_m)
+{
+    constexpr int NWN = TN / WN, NWM = TM / WM, NT = NWN * NWM * 64;
+    constexpr int FN = WN / 16, FM = WM / 16;
+    constexpr int KSTEPS = BK / 64;
+    constexpr int GSD = GS ? GS : 1;                   // divisor-safe group size
+    constexpr int GSTEPS = GS ? GS / 64 : KSTEPS;      // k-steps per scaling group
+    constexpr int GPT = GS ? BK / GSD : 1;             // groups per K tile
+    static_assert(GS == 0 || BK % GS == 0, "a K tile holds whole groups");
+    constexpr int WBYTES_ROW = BITS == 8 ? BK : BK / 2;  // global bytes per weight row per tile
+    constexpr int W_CHUNKS = TN * WBYTES_ROW / 16;
+    constexpr int X_CHUNKS = TM * BK / 16;
+    constexpr int WPT = (W_CHUNKS + NT - 1) / NT, XPT = (X_CHUNKS + NT - 1) / NT;
+    constexpr bool W_EVEN = W_CHUNKS % NT == 0, X_EVEN = X_CHUNKS % NT == 0;
+    constexpr int W_CPR = WBYTES_ROW / 16, X_CPR = BK / 16;
+    constexpr bool SCALED_GROUPS = GS != 0 && OUT == OUT_F16;
+
+    __shared__ __attribute__((aligned(16))) uint8_t sW[2][TN * BK];
+    __shared__ __attribute__((aligned(16))) uint8_t sX[2][TM * BK];
+    __shared__ __attribute__((aligned(16))) float sS[2][SCALED_GROUPS ? GPT * TN : 4];
+
+    const int64_t M = args.M, N = args.N, K = args.K;
+    int tn, tm;
+    tile_coords(blockIdx.x, tiles_n, tiles_m, group_m, tn, tm);
+    const int64_t n0 = (int64_t)tn * TN, m0 = (int64_t)tm * TM;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave % NWN, wm = wave / NWN;
+    const int G = GS ? (int)(K / GSD) : 1;
+
+    const uint8_t *wbase = static_cast<const uint8_t *>(args.wq);
+    const int64_t wld = BITS == 8 ? K : K / 2;
+    const uint8_t *wsrc[WPT];
+    int wdst[WPT];
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+        const int id = W_EVEN ? tid + i * NT : min(tid + i * NT, W_CHUNKS - 1);
+        const int row = id / W_CPR, c = id % W_CPR;
+        const int64_t gr = min(n0 + row, N - 1);  // rows past N: any valid row, never stored
+        wsrc[i] = wbase + gr * wld + c * 16;
+        wdst[i] = BITS == 8 ? lds_offset<BK>(row, c) : row;  // int4: row, chunk pair below
+    }
+    const uint8_t *xsrc[XPT];
+    int xdst[XPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int id = X_EVEN ? tid + i * NT : min(tid + i * NT, X_CHUNKS - 1);
+        const int row = id / X_CPR, c = id % X_CPR;
+        const int64_t gr = min(m0 + row, M - 1);
+        xsrc[i] = reinterpret_cast<const uint8_t *>(args.xq) + gr * K + c * 16;
+        xdst[i] = lds_offset<BK>(row, c);
+    }
+
+    uint4 wreg[WPT], xreg[XPT];
+    float sreg[SCALED_GROUPS ? (GPT * TN + NT - 1) / NT : 1];
+
+    auto load_tile = [&](int kt) {
+        const int64_t kb = (int64_t)kt * BK;
+#pragma unroll
+        for (int i = 0; i < WPT; ++i)
+            wreg[i] = *reinterpret_cast<const uint4 *>(wsrc[i] + (BITS == 8 ? kb : kb / 2));
+#pragma unroll
+        for (int i = 0; i < XPT; ++i)
+            xreg[i] = *reinterpret_cast<const uint4 *>(xsrc[i] + kb);
+        if constexpr (SCALED_GROUPS) {
+#pragma unroll
+            for (int i = 0; i < (GPT * TN + NT - 1) / NT; ++i) {
+                const int id = tid + i * NT;
+                if (id < GPT * TN) {
+                    const int gi = id / TN, row = id % TN;
+                    const int64_t gr = min(n0 + row, N - 1);
+                    sreg[i] = args.s_w[gr * G + (int64_t)kt * GPT + gi];
+                }
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            if constexpr (BITS == 8) {
+                *reinterpret_cast<uint4 *>(&sW[buf][wdst[i]]) = wreg[i];
+            } else {
+                const int id = W_EVEN ? tid + i * NT : min(tid + i * NT, W_CHUNKS - 1);
+                const int c = id % W_CPR;
+                uint4 lo, hi;
+                unpack_nibbles(wreg[i].x, lo.x, lo.y);
+                unpack_nibbles(wreg[i].y, lo.z, lo.w);
+                unpack_nibbles(wreg[i].z, hi.x, hi.y);
+                unpack_nibbles(wreg[i].w, hi.z, hi.w);
+                *reinterpret_cast<uint4 *>(&sW[buf][lds_offset<BK>(wdst[i], 2 * c)]) = lo;
+                *reinterpret_cast<uint4 *>(&sW[buf][lds_offset<BK>(wdst[i], 2 * c + 1)]) = hi;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < XPT; ++i)
+            *reinterpret_cast<uint4 *>(&sX[buf][xdst[i]]) = xreg[i];
+        if constexpr (SCALED_GROUPS) {
+#pragma unroll
+            for (int i = 0; i < (GPT * TN + NT - 1) / NT; ++i) {
+                const int id = tid + i * NT;
+                if (id < GPT * TN)
+                    sS[buf][id] = sreg[i];  // [gi][row]
+            }
+        }
+    };
+
+    i32x4 acc[FN][FM];
+    f32x4 facc[SCALED_GROUPS ? FN : 1][SCALED_GROUPS ? FM : 1];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+            acc[i][j] = i32x4{0, 0, 0, 0};
+    if constexpr (SCALED_GROUPS) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                facc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int frow = lane & 15, fchunk = lane >> 4;
+    const int KT = (int)(K / BK);
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT)
+            load_tile(kt + 1);
+        const uint8_t *tW = sW[cur];
+        const uint8_t *tX = sX[cur];
+        if constexpr (GS == 0) {
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                i32x4 af[FN], bf[FM];
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+                    af[i] = *reinterpret_cast<const i32x4 *>(
+                        tW + lds_offset<BK>(wn * WN + i * 16 + frow, s * 4 + fchunk));
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    bf[j] = *reinterpret_cast<const i32x4 *>(
+                        tX + lds_offset<BK>(wm * WM + j * 16 + frow, s * 4 + fchunk));
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j],
+                                                                          0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int gi = 0; gi < GPT; ++gi) {
+                i32x4 af[GSTEPS][FN], bf[GSTEPS][FM];
+#pragma unroll
+                for (int s = 0; s < GSTEPS; ++s) {
+                    const int ks = gi * GSTEPS + s;
+#pragma unroll
+                    for (int i = 0; i < FN; ++i)
+                        af[s][i] = *reinterpret_cast<const i32x4 *>(
+                            tW + lds_offset<BK>(wn * WN + i * 16 + frow, ks * 4 + fchunk));
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+                        bf[s][j] = *reinterpret_cast<const i32x4 *>(
+                            tX + lds_offset<BK>(wm * WM + j * 16 + frow, ks * 4 + fchunk));
+                }
+                f32x4 sc[FN];
+                if constexpr (SCALED_GROUPS) {
+#pragma unroll
+                    for (int i = 0; i < FN; ++i)
+                        sc[i] = *reinterpret_cast<const f32x4 *>(
+                            &sS[cur][gi * TN + wn * WN + i * 16 + fchunk * 4]);
+                }
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j) {
+                        i32x4 t = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0][i], bf[0][j],
+                                                                       i32x4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+                        for (int s = 1; s < GSTEPS; ++s)
+                            t = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[s][i], bf[s][j], t, 0, 0, 0);
+                        if constexpr (SCALED_GROUPS) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                facc[i][j][r] += (float)t[r] * sc[i][r];
+                        } else {
+                            // raw per-group sums: out[(m * N + n) * G + g]
+                            const int64_t m = m0 + wm * WM + j * 16 + frow;
+                            const int64_t n = n0 + wn * WN + i * 16 + fchunk * 4;
+                            if (m < M && n < N) {
+                                int32_t *o = static_cast<int32_t *>(args.out);
+                                const int64_t g = (int64_t)kt * GPT + gi;
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    o[(m * N + n + r) * G + g] = t[r];
+                            }
+                        }
+                    }
+            }
+        }
+        if (kt + 1 < KT)
+            store_tile(cur ^ 1);
+        __syncthreads();
+    }
+
+    if constexpr (GS != 0 && OUT == OUT_I32)
+        return;  // per-group sums were stored inside the loop
+
+    // Epilogue.  Lane holds, per fragment (i, j), outputs n = nb .. nb+3 of token m.
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int64_t m = m0 + wm * WM + j * 16 + frow;
+        if (m >= M)
+            continue;
+        float st = 0.f;
+        if constexpr (OUT == OUT_F16)
+            st = args.s_tok[m];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int64_t nb = n0 + wn * WN + i * 16 + fchunk * 4;
+            if (nb >= N)
+                continue;
+            if constexpr (OUT == OUT_I32) {
+                *reinterpret_cast<i32x4 *>(static_cast<int32_t *>(args.out) + m * N + nb) = acc[i][j];
+            } else {
+                float y[4];
+                if constexpr (GS == 0) {
+                    const f32x4 sw = *reinterpret_cast<const f32x4 *>(args.s_w + nb);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        y[r] = (float)acc[i][j][r] * st * sw[r];
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        y[r] = st * facc[i][j][r];
+                }
+                uint2 packed;
+                packed.x = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[0]) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[1]) << 16);
+                packed.y = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[2]) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[3]) << 16);
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(args.out) + m * N + nb) = packed;
+            }
+        }
+    }
+}
+
+template <int TN, int TM, int BK, int WN, int WM, int BITS, int GS, int OUT>
+hipError_t launch_cfg(const ProductArgs &a, hipStream_t stream)
+{
+    const int tiles_n = (int)((a.N + TN - 1) / TN);
+    const int tiles_m = (int)((a.M + TM - 1) / TM);
+    const int group_m = 8;
+    dim3 grid(tiles_n * tiles_m), block((TN / WN) * (TM / WM) * 64);
+    hipLaunchKernelGGL((gemm_kernel<TN, TM, BK, WN, WM, BITS, GS, OUT>), grid, block, 0, stream,
+                       a, tiles_n, tiles_m, group_m);
+    return hipGetLastError();
+}
+
+// Tile shapes: (TN, TM, BK, WN, WM).
+template <int BITS, int GS, int OUT>
+hipError_t launch_mode(const ProductArgs &a, hipStream_t stream)
+{
+    // group_size 128 implies K % 128 == 0, so those always take 128-deep tiles.
+    const bool bk128 = a.K % 128 == 0;
+    if (a.M >= 512) {
+        if constexpr (GS == 0) {
+            if (bk128)
+                return launch_cfg<256, 256, 128, 128, 128, BITS, GS, OUT>(a, stream);
+            return launch_cfg<256, 256, 64, 128, 128, BITS, GS, OUT>(a, stream);
+        } else if constexpr (GS == 128) {
+            return launch_cfg<256, 128, 128, 64, 64, BITS, GS, OUT>(a, stream);
+        } else {
+            if (bk128)
+                return launch_cfg<256, 128, 128, 64, 64, BITS, GS, OUT>(a, stream);
+            return launch_cfg<256, 128, 64, 64, 64, BITS, GS, OUT>(a, stream);
+        }
+    }
+    if constexpr (GS == 128) {
+        return launch_cfg<64, 64, 128, 32, 32, BITS, GS, OUT>(a, stream);
+    } else {
+        if (bk128)
+            return launch_cfg<64, 64, 128, 32, 32, BITS, GS, OUT>(a, stream);
+        return launch_cfg<64, 64, 64, 32, 32, BITS, GS, OUT>(a, stream);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const ProductArgs &a, hipStream_t stream)
+{
+    const bool f16 = a.out_kind == OUT_F16;
+    if (a.bits == 8) {
+        switch (a.group_size) {
+        case 0: return f16 ? launch_mode<8, 0, OUT_F16>(a, stream) : launch_mode<8, 0, OUT_I32>(a, stream);
+        case 64: return f16 ? launch_mode<8, 64, OUT_F16>(a, stream) : launch_mode<8, 64, OUT_I32>(a, stream);
+        case 128: return f16 ? launch_mode<8, 128, OUT_F16>(a, stream) : launch_mode<8, 128, OUT_I32>(a, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (a.group_size == 0)
+        return f16 ? launch_mode<4, 0, OUT_F16>(a, stream) : launch_mode<4, 0, OUT_I32>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace cider

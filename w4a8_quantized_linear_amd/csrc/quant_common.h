@@ -1,0 +1,85 @@
+// Device-side quantization arithmetic shared by the quantize kernel and the
+// fused one-token matrix-vector kernel, so both produce identical codes.
+//
+// Cider README (ossradar.top repo page), "Quantization" table: symmetric INT8
+// per token for activations, symmetric INT8 / INT4 (zero-point 8) for weights.
+// Scale s = absmax / 127 (or / 7), code q = clamp(rint(x / s)).  Both
+// divisions are correctly rounded fp32 divisions (the default HIP lowering;
+// the library is never built with fast-math or approximate division) and
+// rint rounds half to even (v_rndne_f32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cider {
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Largest magnitude among the 8 fp16 values of a 16-byte chunk, as fp16
+// magnitude bits.  For finite inputs the order of |x| equals the order of the
+// bit patterns with the sign bit cleared.
+__device__ __forceinline__ uint32_t chunk_absmax_bits(uint4 v)
+{
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    const uint32_t w[4] = {v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu,
+                           v.w & 0x7FFF7FFFu};
+    u16x2 m = __builtin_bit_cast(u16x2, w[0]);
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[1]));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[2]));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[3]));
+    return m.x > m.y ? m.x : m.y;
+}
+
+template <int BITS>
+__device__ __forceinline__ float quant_divisor()
+{
+    return BITS == 8 ? 127.0f : 7.0f;
+}
+
+// Integer code of x for scale s.
+template <int BITS>
+__device__ __forceinline__ int quant_code(float x, float s)
+{
+    constexpr float lo = BITS == 8 ? -127.0f : -8.0f;
+    constexpr float hi = BITS == 8 ? 127.0f : 7.0f;
+    if (s == 0.0f)
+        return 0;
+    float r = __builtin_rintf(x / s);
+    r = __builtin_fminf(__builtin_fmaxf(r, lo), hi);
+    return (int)r;
+}
+
+// Codes of the 8 fp16 values of a chunk, packed: int8 -> 8 bytes (uint2),
+// int4 -> 8 nibbles u = q + 8 with value e at bits 4e (uint32 in .x).
+template <int BITS>
+__device__ __forceinline__ uint2 quantize_chunk(uint4 v, float s)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    int q[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        q[2 * j] = quant_code<BITS>(half_bits_to_float(w[j] & 0xFFFFu), s);
+        q[2 * j + 1] = quant_code<BITS>(half_bits_to_float(w[j] >> 16), s);
+    }
+    uint2 o;
+    if constexpr (BITS == 8) {
+        o.x = (uint32_t)(q[0] & 0xFF) | ((uint32_t)(q[1] & 0xFF) << 8) |
+              ((uint32_t)(q[2] & 0xFF) << 16) | ((uint32_t)(q[3] & 0xFF) << 24);
+        o.y = (uint32_t)(q[4] & 0xFF) | ((uint32_t)(q[5] & 0xFF) << 8) |
+              ((uint32_t)(q[6] & 0xFF) << 16) | ((uint32_t)(q[7] & 0xFF) << 24);
+    } else {
+        uint32_t p = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            p |= (uint32_t)(q[e] + 8) << (4 * e);
+        o.x = p;
+        o.y = 0;
+    }
+    return o;
+}
+
+}  // namespace cider
