@@ -57,8 +57,9 @@
  * are assumed finite; NaN or Inf inputs give unspecified codes.
  *
  * Envelope: M >= 0 (M = 0 is a no-op), N >= 0 with N % 64 == 0, K > 0 with
- * K % 64 == 0 and K <= 133144, group_size in {0, 64, 128} for W8A8 and 0 for
- * W4A8; device pointers 16-byte aligned; ldx % 8 == 0.
+ * K % 64 == 0 and K <= 133144, (M + 256) * K < 2^31 and (N + 256) * K < 2^31
+ * for the products, group_size in {0, 64, 128} for W8A8 and 0 for W4A8;
+ * device pointers 16-byte aligned; ldx % 8 == 0.
  */
 #ifndef CIDER_H
 #define CIDER_H

@@ -16,6 +16,7 @@ namespace {
 
 constexpr int64_t kMaxK = 133144;       // K * 127^2 < 2^31
 constexpr int64_t kGemvMaxBytes = 32768;  // M * K int8 codes held in LDS
+constexpr int64_t kMaxOperandBytes = int64_t(1) << 31;
 
 std::atomic<int> g_path{0};
 
@@ -72,6 +73,10 @@ cider_status check_shape(int64_t M, int64_t N, int64_t K, int bits, int group_si
     if (K % 64 != 0 || K > kMaxK || N % 64 != 0)
         return CIDER_ERR_UNSUPPORTED_SHAPE;
     if (group_size && K % group_size != 0)
+        return CIDER_ERR_UNSUPPORTED_SHAPE;
+    // The kernels address operands with 32-bit byte offsets (one tile past
+    // the end included): each operand stays below 2 GiB.
+    if ((M + 256) * K >= kMaxOperandBytes || (N + 256) * K >= kMaxOperandBytes)
         return CIDER_ERR_UNSUPPORTED_SHAPE;
     return CIDER_OK;
 }

@@ -82,109 +82,147 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_n, int tiles_m, i
     tn = r / gsize;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
+{
+    // Raw buffer, stride 0: byte offsets, loads at or past `bytes` return 0.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// One wavefront-wide asynchronous copy of 64 x 16 bytes from global memory
+// straight into LDS: lane l's 16 bytes land at lds_block + 16 * l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void *lds_block,
+                                      uint32_t voffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_block, 16, voffset, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem_all()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
+}
+
 template <int TN, int TM, int BK, int WN, int WM, int BITS, int GS, int OUT>
 __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     ProductArgs args, int tiles_n, int tiles_m, int group_m)
 {
-    constexpr int NWN = TN / WN, NWM = TM / WM, NT = NWN * NWM * 64;
+    constexpr int NWN = TN / WN, NWM = TM / WM, NT = NWN * NWM * 64, NWAVES = NT / 64;
     constexpr int FN = WN / 16, FM = WM / 16;
     constexpr int KSTEPS = BK / 64;
     constexpr int GSD = GS ? GS : 1;                   // divisor-safe group size
     constexpr int GSTEPS = GS ? GS / 64 : KSTEPS;      // k-steps per scaling group
     constexpr int GPT = GS ? BK / GSD : 1;             // groups per K tile
     static_assert(GS == 0 || BK % GS == 0, "a K tile holds whole groups");
-    constexpr int WBYTES_ROW = BITS == 8 ? BK : BK / 2;  // global bytes per weight row per tile
-    constexpr int W_CHUNKS = TN * WBYTES_ROW / 16;
-    constexpr int X_CHUNKS = TM * BK / 16;
-    constexpr int WPT = (W_CHUNKS + NT - 1) / NT, XPT = (X_CHUNKS + NT - 1) / NT;
-    constexpr bool W_EVEN = W_CHUNKS % NT == 0, X_EVEN = X_CHUNKS % NT == 0;
-    constexpr int W_CPR = WBYTES_ROW / 16, X_CPR = BK / 16;
+    constexpr int CPR = BK / 16;                       // 16-byte chunks per int8 LDS row
+    constexpr int WROWB = BITS == 8 ? BK : BK / 2;     // weight bytes per row per K tile
+    constexpr int XBLK = TM * BK / 1024, WBLK = TN * WROWB / 1024;  // 1 KB copy blocks
+    static_assert(XBLK >= 1 && WBLK >= 1, "tiles of at least 1 KB");
+    constexpr int XPW = (XBLK + NWAVES - 1) / NWAVES, WPW = (WBLK + NWAVES - 1) / NWAVES;
     constexpr bool SCALED_GROUPS = GS != 0 && OUT == OUT_F16;
+    constexpr int SPT = SCALED_GROUPS ? (GPT * TN + NT - 1) / NT : 1;  // scales per thread
 
-    __shared__ __attribute__((aligned(16))) uint8_t sW[2][TN * BK];
-    __shared__ __attribute__((aligned(16))) uint8_t sX[2][TM * BK];
-    __shared__ __attribute__((aligned(16))) float sS[2][SCALED_GROUPS ? GPT * TN : 4];
+    // Two stages per operand as distinct LDS objects, so the copies into
+    // one stage and the fragment reads from the other are never confused.
+    __shared__ __attribute__((aligned(1024))) uint8_t sX0[TM * BK];
+    __shared__ __attribute__((aligned(1024))) uint8_t sX1[TM * BK];
+    __shared__ __attribute__((aligned(1024))) uint8_t sW0[TN * WROWB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sW1[TN * WROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t sU[BITS == 4 ? TN * BK : 16];  // int4 -> int8
+    __shared__ __attribute__((aligned(16))) float sS0[SCALED_GROUPS ? GPT * TN : 4];
+    __shared__ __attribute__((aligned(16))) float sS1[SCALED_GROUPS ? GPT * TN : 4];
 
     const int64_t M = args.M, N = args.N, K = args.K;
     int tn, tm;
     tile_coords(blockIdx.x, tiles_n, tiles_m, group_m, tn, tm);
     const int64_t n0 = (int64_t)tn * TN, m0 = (int64_t)tm * TM;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep it scalar
     const int wn = wave % NWN, wm = wave / NWN;
     const int G = GS ? (int)(K / GSD) : 1;
+    const uint32_t wld = (uint32_t)(BITS == 8 ? K : K / 2);
 
-    const uint8_t *wbase = static_cast<const uint8_t *>(args.wq);
-    const int64_t wld = BITS == 8 ? K : K / 2;
-    const uint8_t *wsrc[WPT];
-    int wdst[WPT];
+    const __amdgpu_buffer_rsrc_t rX = make_rsrc(args.xq, (uint32_t)(M * K));
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(args.wq, (uint32_t)(N * (int64_t)wld));
+
+    // Per-lane source offsets of this wavefront's copy blocks.  LDS row r
+    // slot s must hold global chunk s ^ swz(r) (int8 tiles); packed int4
+    // tiles are copied unswizzled and widened by the unpack pass.
+    uint32_t xoff[XPW], woff[WPW];
 #pragma unroll
-    for (int i = 0; i < WPT; ++i) {
-        const int id = W_EVEN ? tid + i * NT : min(tid + i * NT, W_CHUNKS - 1);
-        const int row = id / W_CPR, c = id % W_CPR;
-        const int64_t gr = min(n0 + row, N - 1);  // rows past N: any valid row, never stored
-        wsrc[i] = wbase + gr * wld + c * 16;
-        wdst[i] = BITS == 8 ? lds_offset<BK>(row, c) : row;  // int4: row, chunk pair below
+    for (int j = 0; j < XPW; ++j) {
+        const int b = wave + j * NWAVES;
+        const int r = b * (1024 / BK) + lane / CPR, sl = lane % CPR;
+        const int c = sl ^ (lds_offset<BK>(r, 0) - r * BK) / 16;
+        xoff[j] = (uint32_t)((m0 + r) * K) + c * 16;
     }
-    const uint8_t *xsrc[XPT];
-    int xdst[XPT];
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-        const int id = X_EVEN ? tid + i * NT : min(tid + i * NT, X_CHUNKS - 1);
-        const int row = id / X_CPR, c = id % X_CPR;
-        const int64_t gr = min(m0 + row, M - 1);
-        xsrc[i] = reinterpret_cast<const uint8_t *>(args.xq) + gr * K + c * 16;
-        xdst[i] = lds_offset<BK>(row, c);
+    for (int j = 0; j < WPW; ++j) {
+        const int b = wave + j * NWAVES;
+        if constexpr (BITS == 8) {
+            const int r = b * (1024 / BK) + lane / CPR, sl = lane % CPR;
+            const int c = sl ^ (lds_offset<BK>(r, 0) - r * BK) / 16;
+            woff[j] = (uint32_t)((n0 + r) * (int64_t)wld) + c * 16;
+        } else {
+            constexpr int CPRP = WROWB / 16;
+            const int r = b * (1024 / WROWB) + lane / CPRP, c = lane % CPRP;
+            woff[j] = (uint32_t)((n0 + r) * (int64_t)wld) + c * 16;
+        }
     }
 
-    uint4 wreg[WPT], xreg[XPT];
-    float sreg[SCALED_GROUPS ? (GPT * TN + NT - 1) / NT : 1];
+    auto issue_copies = [&](const uint8_t *dX, const uint8_t *dW, int kt) {
+        const uint32_t kx = (uint32_t)kt * BK, kw = (uint32_t)kt * WROWB;
+#pragma unroll
+        for (int j = 0; j < XPW; ++j)
+            if (XBLK % NWAVES == 0 || wave + j * NWAVES < XBLK)  // wavefront-uniform
+                dma16(rX, dX + (wave + j * NWAVES) * 1024, xoff[j] + kx);
+#pragma unroll
+        for (int j = 0; j < WPW; ++j)
+            if (WBLK % NWAVES == 0 || wave + j * NWAVES < WBLK)
+                dma16(rW, dW + (wave + j * NWAVES) * 1024, woff[j] + kw);
+    };
 
-    auto load_tile = [&](int kt) {
-        const int64_t kb = (int64_t)kt * BK;
-#pragma unroll
-        for (int i = 0; i < WPT; ++i)
-            wreg[i] = *reinterpret_cast<const uint4 *>(wsrc[i] + (BITS == 8 ? kb : kb / 2));
-#pragma unroll
-        for (int i = 0; i < XPT; ++i)
-            xreg[i] = *reinterpret_cast<const uint4 *>(xsrc[i] + kb);
+    float sreg[SPT];
+    auto load_scales = [&](int kt) {
         if constexpr (SCALED_GROUPS) {
 #pragma unroll
-            for (int i = 0; i < (GPT * TN + NT - 1) / NT; ++i) {
-                const int id = tid + i * NT;
-                if (id < GPT * TN) {
-                    const int gi = id / TN, row = id % TN;
-                    const int64_t gr = min(n0 + row, N - 1);
-                    sreg[i] = args.s_w[gr * G + (int64_t)kt * GPT + gi];
-                }
+            for (int i = 0; i < SPT; ++i) {
+                const int id = min(tid + i * NT, GPT * TN - 1);
+                const int gi = id / TN, row = id % TN;
+                const int64_t gr = min(n0 + row, N - 1);
+                sreg[i] = args.s_w[gr * G + (int64_t)kt * GPT + gi];
             }
         }
     };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < WPT; ++i) {
-            if constexpr (BITS == 8) {
-                *reinterpret_cast<uint4 *>(&sW[buf][wdst[i]]) = wreg[i];
-            } else {
-                const int id = W_EVEN ? tid + i * NT : min(tid + i * NT, W_CHUNKS - 1);
-                const int c = id % W_CPR;
-                uint4 lo, hi;
-                unpack_nibbles(wreg[i].x, lo.x, lo.y);
-                unpack_nibbles(wreg[i].y, lo.z, lo.w);
-                unpack_nibbles(wreg[i].z, hi.x, hi.y);
-                unpack_nibbles(wreg[i].w, hi.z, hi.w);
-                *reinterpret_cast<uint4 *>(&sW[buf][lds_offset<BK>(wdst[i], 2 * c)]) = lo;
-                *reinterpret_cast<uint4 *>(&sW[buf][lds_offset<BK>(wdst[i], 2 * c + 1)]) = hi;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < XPT; ++i)
-            *reinterpret_cast<uint4 *>(&sX[buf][xdst[i]]) = xreg[i];
+    auto store_scales = [&](float *dS) {
         if constexpr (SCALED_GROUPS) {
 #pragma unroll
-            for (int i = 0; i < (GPT * TN + NT - 1) / NT; ++i) {
+            for (int i = 0; i < SPT; ++i) {
                 const int id = tid + i * NT;
                 if (id < GPT * TN)
-                    sS[buf][id] = sreg[i];  // [gi][row]
+                    dS[id] = sreg[i];  // [gi][row]
+            }
+        }
+    };
+    // int4: widen the packed stage into sU (int8, swizzled like the others).
+    auto unpack = [&](const uint8_t *dW) {
+        if constexpr (BITS == 4) {
+            constexpr int CPRP = WROWB / 16, TOTAL = TN * CPRP;
+#pragma unroll
+            for (int i = 0; i < (TOTAL + NT - 1) / NT; ++i) {
+                const int id = tid + i * NT;
+                if (TOTAL % NT == 0 || id < TOTAL) {
+                    const int row = id / CPRP, c = id % CPRP;
+                    const uint4 v = *reinterpret_cast<const uint4 *>(dW + row * WROWB + c * 16);
+                    uint4 lo, hi;
+                    unpack_nibbles(v.x, lo.x, lo.y);
+                    unpack_nibbles(v.y, lo.z, lo.w);
+                    unpack_nibbles(v.z, hi.x, hi.y);
+                    unpack_nibbles(v.w, hi.z, hi.w);
+                    *reinterpret_cast<uint4 *>(&sU[lds_offset<BK>(row, 2 * c)]) = lo;
+                    *reinterpret_cast<uint4 *>(&sU[lds_offset<BK>(row, 2 * c + 1)]) = hi;
+                }
             }
         }
     };
@@ -205,18 +243,8 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     }
 
     const int frow = lane & 15, fchunk = lane >> 4;
-    const int KT = (int)(K / BK);
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT)
-            load_tile(kt + 1);
-        const uint8_t *tW = sW[cur];
-        const uint8_t *tX = sX[cur];
+    auto compute = [&](const uint8_t *tW, const uint8_t *tX, const float *tS, int kt) {
         if constexpr (GS == 0) {
 #pragma unroll
             for (int s = 0; s < KSTEPS; ++s) {
@@ -257,7 +285,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
 #pragma unroll
                     for (int i = 0; i < FN; ++i)
                         sc[i] = *reinterpret_cast<const f32x4 *>(
-                            &sS[cur][gi * TN + wn * WN + i * 16 + fchunk * 4]);
+                            &tS[gi * TN + wn * WN + i * 16 + fchunk * 4]);
                 }
 #pragma unroll
                 for (int i = 0; i < FN; ++i)
@@ -287,9 +315,41 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
                     }
             }
         }
-        if (kt + 1 < KT)
-            store_tile(cur ^ 1);
+    };
+
+    const int KT = (int)(K / BK);
+    issue_copies(sX0, sW0, 0);
+    load_scales(0);
+    store_scales(sS0);
+    wait_vmem_all();
+    __syncthreads();
+    if constexpr (BITS == 4) {
+        unpack(sW0);
         __syncthreads();
+    }
+    // One K tile per iteration: start the copies of tile kt+1 into the other
+    // stage, run the matrix cores on this stage, then wait for the copies and
+    // meet at a barrier.
+    for (int kt = 0; kt < KT; ++kt) {
+        const bool odd = kt & 1;
+        const bool more = kt + 1 < KT;
+        if (more) {
+            issue_copies(odd ? sX0 : sX1, odd ? sW0 : sW1, kt + 1);
+            load_scales(kt + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        compute(BITS == 4 ? sU : (odd ? sW1 : sW0), odd ? sX1 : sX0, odd ? sS1 : sS0, kt);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more)
+            store_scales(odd ? sS0 : sS1);
+        wait_vmem_all();
+        __syncthreads();
+        if constexpr (BITS == 4) {
+            if (more) {
+                unpack(odd ? sW0 : sW1);
+                __syncthreads();
+            }
+        }
     }
 
     if constexpr (GS != 0 && OUT == OUT_I32)
