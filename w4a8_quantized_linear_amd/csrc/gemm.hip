@@ -10,10 +10,11 @@
 // before the int8 product.
 //
 // Design for CDNA4 (the pages' M5 tiling is prior art only):
-//   * v_mfma_i32_16x16x64_i8: 16x16 int32 block, 64-deep K per instruction.
-//     The weight tile is the A operand and the activation tile the B
-//     operand, so a lane's four accumulators are four consecutive output
-//     columns n of one token m: the epilogue stores 8 contiguous bytes.
+//   * v_mfma_i32_32x32x32_i8: 32x32 int32 block, 32-deep K per instruction
+//     (the full-rate int8 shape on gfx950; the 16x16x64 form issues at about
+//     half the rate).  The weight tile is the A operand and the activation
+//     tile the B operand, so each lane holds runs of four consecutive output
+//     channels n of one token m: the epilogue stores 8 contiguous bytes.
 //   * Tiles of TN x TM outputs per workgroup, WN x WM per wavefront, K
 //     staged BK at a time through LDS, double buffered: global loads of tile
 //     k+1 are in flight while the matrix cores consume tile k; one barrier
@@ -34,7 +35,9 @@ namespace cider {
 namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;
 
@@ -43,7 +46,9 @@ __device__ __forceinline__ int lds_offset(int row, int chunk)
 {
     constexpr int CPR = BK / 16;  // 16-byte chunks per row
     static_assert(CPR == 4 || CPR == 8, "BK must be 64 or 128");
-    const int swz = (CPR == 8) ? (row & 7) : ((row >> 1) & 3);
+    // Conflict-free for 16-byte reads of consecutive rows at one chunk,
+    // whether LDS serves 8 lanes per 128 bytes or 16 lanes per 256 bytes.
+    const int swz = (CPR == 8) ? ((row & 7) ^ ((row >> 3) & 1)) : (((row >> 1) ^ (row >> 2)) & 3);
     return row * BK + ((chunk ^ swz) << 4);
 }
 
@@ -109,10 +114,10 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     ProductArgs args, int tiles_n, int tiles_m, int group_m)
 {
     constexpr int NWN = TN / WN, NWM = TM / WM, NT = NWN * NWM * 64, NWAVES = NT / 64;
-    constexpr int FN = WN / 16, FM = WM / 16;
-    constexpr int KSTEPS = BK / 64;
+    constexpr int FN = WN / 32, FM = WM / 32;          // 32 x 32 blocks per wavefront
+    constexpr int KSTEPS = BK / 32;                    // 32-deep matrix-core steps per tile
     constexpr int GSD = GS ? GS : 1;                   // divisor-safe group size
-    constexpr int GSTEPS = GS ? GS / 64 : KSTEPS;      // k-steps per scaling group
+    constexpr int GSTEPS = GS ? GS / 32 : KSTEPS;      // k-steps per scaling group
     constexpr int GPT = GS ? BK / GSD : 1;             // groups per K tile
     static_assert(GS == 0 || BK % GS == 0, "a K tile holds whole groups");
     constexpr int CPR = BK / 16;                       // 16-byte chunks per int8 LDS row
@@ -227,22 +232,27 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
         }
     };
 
-    i32x4 acc[FN][FM];
-    f32x4 facc[SCALED_GROUPS ? FN : 1][SCALED_GROUPS ? FM : 1];
+    i32x16 acc[GS == 0 ? FN : 1][GS == 0 ? FM : 1];
+    f32x16 facc[SCALED_GROUPS ? FN : 1][SCALED_GROUPS ? FM : 1];
+    if constexpr (GS == 0) {
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+        for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < FM; ++j)
-            acc[i][j] = i32x4{0, 0, 0, 0};
+            for (int j = 0; j < FM; ++j)
+                acc[i][j] = i32x16{};
+    }
     if constexpr (SCALED_GROUPS) {
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
             for (int j = 0; j < FM; ++j)
-                facc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                facc[i][j] = f32x16{};
     }
 
-    const int frow = lane & 15, fchunk = lane >> 4;
+    // v_mfma_i32_32x32x32_i8 operands: lane l holds row (l % 32) of a 32-row
+    // block and 16 consecutive k of a 32-deep step (half l / 32).  Result:
+    // lane l holds column l % 32 and, for q = 0..3, rows 8q + 4(l/32) + 0..3.
+    const int frow = lane & 31, fhalf = lane >> 5;
 
     auto compute = [&](const uint8_t *tW, const uint8_t *tX, const float *tS, int kt) {
         if constexpr (GS == 0) {
@@ -252,16 +262,16 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
 #pragma unroll
                 for (int i = 0; i < FN; ++i)
                     af[i] = *reinterpret_cast<const i32x4 *>(
-                        tW + lds_offset<BK>(wn * WN + i * 16 + frow, s * 4 + fchunk));
+                        tW + lds_offset<BK>(wn * WN + i * 32 + frow, s * 2 + fhalf));
 #pragma unroll
                 for (int j = 0; j < FM; ++j)
                     bf[j] = *reinterpret_cast<const i32x4 *>(
-                        tX + lds_offset<BK>(wm * WM + j * 16 + frow, s * 4 + fchunk));
+                        tX + lds_offset<BK>(wm * WM + j * 32 + frow, s * 2 + fhalf));
 #pragma unroll
                 for (int i = 0; i < FN; ++i)
 #pragma unroll
                     for (int j = 0; j < FM; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j],
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j],
                                                                           0, 0, 0);
             }
         } else {
@@ -274,42 +284,51 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
 #pragma unroll
                     for (int i = 0; i < FN; ++i)
                         af[s][i] = *reinterpret_cast<const i32x4 *>(
-                            tW + lds_offset<BK>(wn * WN + i * 16 + frow, ks * 4 + fchunk));
+                            tW + lds_offset<BK>(wn * WN + i * 32 + frow, ks * 2 + fhalf));
 #pragma unroll
                     for (int j = 0; j < FM; ++j)
                         bf[s][j] = *reinterpret_cast<const i32x4 *>(
-                            tX + lds_offset<BK>(wm * WM + j * 16 + frow, ks * 4 + fchunk));
+                            tX + lds_offset<BK>(wm * WM + j * 32 + frow, ks * 2 + fhalf));
                 }
-                f32x4 sc[FN];
+                f32x4 sc[FN][4];
                 if constexpr (SCALED_GROUPS) {
 #pragma unroll
                     for (int i = 0; i < FN; ++i)
-                        sc[i] = *reinterpret_cast<const f32x4 *>(
-                            &tS[gi * TN + wn * WN + i * 16 + fchunk * 4]);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            sc[i][q] = *reinterpret_cast<const f32x4 *>(
+                                &tS[gi * TN + wn * WN + i * 32 + q * 8 + fhalf * 4]);
                 }
 #pragma unroll
                 for (int i = 0; i < FN; ++i)
 #pragma unroll
                     for (int j = 0; j < FM; ++j) {
-                        i32x4 t = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0][i], bf[0][j],
-                                                                       i32x4{0, 0, 0, 0}, 0, 0, 0);
+                        i32x16 t = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[0][i], bf[0][j],
+                                                                        i32x16{}, 0, 0, 0);
 #pragma unroll
                         for (int s = 1; s < GSTEPS; ++s)
-                            t = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[s][i], bf[s][j], t, 0, 0, 0);
+                            t = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s][i], bf[s][j], t, 0, 0, 0);
                         if constexpr (SCALED_GROUPS) {
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                facc[i][j][r] += (float)t[r] * sc[i][r];
+                            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    facc[i][j][4 * q + r] += (float)t[4 * q + r] * sc[i][q][r];
                         } else {
                             // raw per-group sums: out[(m * N + n) * G + g]
-                            const int64_t m = m0 + wm * WM + j * 16 + frow;
-                            const int64_t n = n0 + wn * WN + i * 16 + fchunk * 4;
-                            if (m < M && n < N) {
+                            const int64_t m = m0 + wm * WM + j * 32 + frow;
+                            if (m < M) {
                                 int32_t *o = static_cast<int32_t *>(args.out);
                                 const int64_t g = (int64_t)kt * GPT + gi;
 #pragma unroll
-                                for (int r = 0; r < 4; ++r)
-                                    o[(m * N + n + r) * G + g] = t[r];
+                                for (int q = 0; q < 4; ++q) {
+                                    const int64_t n = n0 + wn * WN + i * 32 + q * 8 + fhalf * 4;
+                                    if (n < N) {
+#pragma unroll
+                                        for (int r = 0; r < 4; ++r)
+                                            o[(m * N + n + r) * G + g] = t[4 * q + r];
+                                    }
+                                }
                             }
                         }
                     }
@@ -355,10 +374,11 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     if constexpr (GS != 0 && OUT == OUT_I32)
         return;  // per-group sums were stored inside the loop
 
-    // Epilogue.  Lane holds, per fragment (i, j), outputs n = nb .. nb+3 of token m.
+    // Epilogue: per block (i, j) the lane holds token m and, for q = 0..3,
+    // output channels nb .. nb+3 with nb = block base + 8q + 4 * (lane / 32).
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-        const int64_t m = m0 + wm * WM + j * 16 + frow;
+        const int64_t m = m0 + wm * WM + j * 32 + frow;
         if (m >= M)
             continue;
         float st = 0.f;
@@ -366,29 +386,35 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
             st = args.s_tok[m];
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
-            const int64_t nb = n0 + wn * WN + i * 16 + fchunk * 4;
-            if (nb >= N)
-                continue;
-            if constexpr (OUT == OUT_I32) {
-                *reinterpret_cast<i32x4 *>(static_cast<int32_t *>(args.out) + m * N + nb) = acc[i][j];
-            } else {
-                float y[4];
-                if constexpr (GS == 0) {
-                    const f32x4 sw = *reinterpret_cast<const f32x4 *>(args.s_w + nb);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        y[r] = (float)acc[i][j][r] * st * sw[r];
+            for (int q = 0; q < 4; ++q) {
+                const int64_t nb = n0 + wn * WN + i * 32 + q * 8 + fhalf * 4;
+                if (nb >= N)
+                    continue;
+                if constexpr (OUT == OUT_I32) {
+                    const i32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]};
+                    *reinterpret_cast<i32x4 *>(static_cast<int32_t *>(args.out) + m * N + nb) = v;
                 } else {
+                    float y[4];
+                    if constexpr (GS == 0) {
+                        const f32x4 sw = *reinterpret_cast<const f32x4 *>(args.s_w + nb);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        y[r] = st * facc[i][j][r];
+                        for (int r = 0; r < 4; ++r)
+                            y[r] = (float)acc[i][j][4 * q + r] * st * sw[r];
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            y[r] = st * facc[i][j][4 * q + r];
+                    }
+                    uint2 packed;
+                    packed.x = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[0]) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[1]) << 16);
+                    packed.y = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[2]) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[3]) << 16);
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(args.out) + m * N + nb) =
+                        packed;
                 }
-                uint2 packed;
-                packed.x = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[0]) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[1]) << 16);
-                packed.y = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[2]) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[3]) << 16);
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(args.out) + m * N + nb) = packed;
             }
         }
     }
@@ -438,17 +464,16 @@ hipError_t launch_mode(const ProductArgs &a, hipStream_t stream)
 
 hipError_t launch_gemm(const ProductArgs &a, hipStream_t stream)
 {
+    if (a.group_size == 0)
+        return launch_gemm_pc(a, stream);
     const bool f16 = a.out_kind == OUT_F16;
     if (a.bits == 8) {
         switch (a.group_size) {
-        case 0: return f16 ? launch_mode<8, 0, OUT_F16>(a, stream) : launch_mode<8, 0, OUT_I32>(a, stream);
         case 64: return f16 ? launch_mode<8, 64, OUT_F16>(a, stream) : launch_mode<8, 64, OUT_I32>(a, stream);
         case 128: return f16 ? launch_mode<8, 128, OUT_F16>(a, stream) : launch_mode<8, 128, OUT_I32>(a, stream);
         default: return hipErrorInvalidValue;
         }
     }
-    if (a.group_size == 0)
-        return f16 ? launch_mode<4, 0, OUT_F16>(a, stream) : launch_mode<4, 0, OUT_I32>(a, stream);
     return hipErrorInvalidValue;
 }
 

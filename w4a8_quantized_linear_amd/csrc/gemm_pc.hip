@@ -1,0 +1,420 @@
+// Pipelined matrix-core product for one scale per output channel: W8A8
+// per-channel and W4A8 (Cider README, ossradar.top repo page, "Quantization"
+// table: INT32 accumulation, C_fp16 = C_int32 * s_act * s_weight per element;
+// "Modes": W4A8 unpacks INT4 before the INT8 product; "TensorOps matmul2d":
+// dequantization fused into the store phase).
+//
+// Structure (gfx950):
+//   * v_mfma_i32_32x32x32_i8 with the weight tile as operand A and the token
+//     tile as operand B; a wavefront owns WN x WM outputs.
+//   * K advances 64 bytes per tile.  Tiles go from HBM to LDS with
+//     buffer_load_dwordx4 ... lds (no registers involved) through a ring of
+//     STAGES LDS stages, so STAGES - 1 tiles of copies are in flight while
+//     the matrix cores work; a tile's copies are awaited with a counted
+//     vmcnt, not a full drain.
+//   * Each 64-deep tile is two 32-deep matrix-core steps.  The fragments of
+//     the next step are read from LDS while the current step's MFMAs run
+//     (two register sets, reads interleaved between MFMAs).  The one
+//     barrier per tile sits between the two steps, where the queued MFMAs
+//     cover it; right after it the stage just consumed is refilled.
+//   * int8 tiles: rows of 64 bytes, 16-byte chunk c of row r at slot
+//     c ^ (((r >> 1) ^ (r >> 2)) & 3), conflict-free for the fragment reads.
+//     Packed int4 tiles: rows of 32 bytes, chunk c at slot c ^ ((r >> 3) & 1);
+//     a lane reads 8 packed bytes and widens them to 16 int8 codes in
+//     registers, so no unpacked copy of the weight tile is ever stored.
+//   * Out-of-range rows read as zeros (buffer descriptors bound the operand);
+//     their outputs are not stored.
+#include "cider_kernels.h"
+
+namespace cider {
+namespace {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kXcds = 8;
+
+// LDS slot of 16-byte chunk `chunk` of int8 tile row `row` (rows of BK
+// bytes).  Conflict-free for 16-byte reads of 32 consecutive rows at one
+// chunk, whether LDS serves 8 lanes per 128 bytes or 16 lanes per 256 bytes.
+template <int BK>
+__device__ __forceinline__ int swz8(int row)
+{
+    return BK == 64 ? (((row >> 1) ^ (row >> 2)) & 3) : ((row & 7) ^ ((row >> 3) & 1));
+}
+template <int BK>
+__device__ __forceinline__ int off8(int row, int chunk)
+{
+    return row * BK + ((chunk ^ swz8<BK>(row)) << 4);
+}
+// Packed int4 rows of BK/2 bytes.
+template <int BK>
+__device__ __forceinline__ int swz4(int row)
+{
+    return BK == 64 ? ((row >> 3) & 1) : (((row >> 1) ^ (row >> 2)) & 3);
+}
+template <int BK>
+__device__ __forceinline__ int off4(int row, int chunk)
+{
+    return row * (BK / 2) + ((chunk ^ swz4<BK>(row)) << 4);
+}
+
+// Raw buffer resource (gfx9 layout, stride 0): byte offsets, loads at or
+// past `bytes` return 0.  Kept in scalar registers.
+__device__ __forceinline__ i32x4 make_rsrc(const void *p, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// One wavefront-wide asynchronous copy of 64 x 16 bytes from global memory
+// straight into LDS: lane l's 16 bytes land at LDS address lds + 16 * l.
+// Written as an instruction of its own because the compiler, seeing an LDS
+// write it cannot disambiguate, would otherwise drain every copy in flight
+// before each later LDS read; ordering against readers is enforced here by
+// the counted vmcnt waits and barriers of the pipeline instead.  There is no
+// register result: the data goes to LDS, and the operands are read at issue.
+__device__ __forceinline__ void dma16(const i32x4 &rsrc, const void *lds_block, uint32_t voffset)
+{
+    const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_t *)lds_block;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voffset), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits 3:0 and
+// 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+__device__ __forceinline__ void wait_lgkm0()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
+// Widen 8 packed nibbles (low nibble = even k) to int8 codes q = u - 8.
+__device__ __forceinline__ void unpack8(uint32_t v, uint32_t &d0, uint32_t &d1)
+{
+    const uint32_t lo = v & 0x0F0F0F0Fu;
+    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
+    const uint32_t a = (lo & 0xFFu) | ((hi & 0xFFu) << 8) | ((lo & 0xFF00u) << 8) | ((hi & 0xFF00u) << 16);
+    const uint32_t b = ((lo >> 16) & 0xFFu) | ((hi >> 8) & 0xFF00u) | ((lo & 0xFF000000u) >> 8) |
+                       (hi & 0xFF000000u);
+    d0 = (a + 0x78787878u) ^ 0x80808080u;
+    d1 = (b + 0x78787878u) ^ 0x80808080u;
+}
+
+__device__ __forceinline__ void tile_coords(int pid, int tiles_n, int tiles_m, int group_m,
+                                            int &tn, int &tm)
+{
+    const int total = tiles_n * tiles_m;
+    int logical = pid;
+    if (total % kXcds == 0) {
+        const int per = total / kXcds;
+        logical = (pid % kXcds) * per + pid / kXcds;
+    }
+    const int in_group = group_m * tiles_n;
+    const int gid = logical / in_group;
+    const int first_m = gid * group_m;
+    const int gsize = min(tiles_m - first_m, group_m);
+    const int r = logical - gid * in_group;
+    tm = first_m + r % gsize;
+    tn = r / gsize;
+}
+
+template <int TN, int TM, int WN, int WM, int BK, int BITS, int OUT, int STAGES>
+__global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_pc_kernel(
+    ProductArgs args, int tiles_n, int tiles_m, int group_m)
+{
+    constexpr int NWN = TN / WN, NWM = TM / WM, NW = NWN * NWM;
+    constexpr int FN = WN / 32, FM = WM / 32;
+    constexpr int KSTEPS = BK / 32;
+    static_assert(KSTEPS % 2 == 0, "an even number of 32-deep steps per tile");
+    constexpr int XROW = BK, WROW = BITS == 8 ? BK : BK / 2;        // bytes per tile row
+    constexpr int XBYTES = TM * XROW, WBYTES = TN * WROW;            // per stage
+    constexpr int STAGE = XBYTES + WBYTES;
+    constexpr int XB = XBYTES / 1024, WB = WBYTES / 1024;            // 1 KB copy blocks
+    constexpr int XPW = (XB + NW - 1) / NW, WPW = (WB + NW - 1) / NW;
+    constexpr int D = XPW + WPW;                                     // copies per wave per tile
+    static_assert(XB >= 1 && WB >= 1, "tiles of at least 1 KB");
+    static_assert(XB % NW == 0 && WB % NW == 0, "copy blocks split evenly over wavefronts");
+    static_assert(STAGES >= 2 && (STAGES - 1) * D < 64, "vmcnt range");
+
+    constexpr int OUT_BYTES = NW * WM * WN * 2;  // fp16 output staging, one region per wave
+    __shared__ __attribute__((aligned(1024))) uint8_t
+        smem[STAGES * STAGE > OUT_BYTES ? STAGES * STAGE : OUT_BYTES];
+    __shared__ __attribute__((aligned(16))) float s_sw[OUT == OUT_F16 ? TN : 4];   // s_w tile
+    __shared__ __attribute__((aligned(16))) float s_st[OUT == OUT_F16 ? TM : 4];   // s_tok tile
+
+    const int64_t M = args.M, N = args.N, K = args.K;
+    int tn, tm;
+    tile_coords(blockIdx.x, tiles_n, tiles_m, group_m, tn, tm);
+    const int64_t n0 = (int64_t)tn * TN, m0 = (int64_t)tm * TM;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave % NWN, wm = wave / NWN;
+    const uint32_t wld = (uint32_t)(BITS == 8 ? K : K / 2);
+    const int KT = (int)(K / BK);
+
+    const i32x4 rX = make_rsrc(args.xq, (uint32_t)(M * K));
+    const i32x4 rW = make_rsrc(args.wq, (uint32_t)(N * (int64_t)wld));
+
+    // Source offset of this lane's 16 bytes in each of the wave's copy blocks:
+    // LDS slot s of row r receives global chunk s ^ swizzle(r).
+    uint32_t xoff[XPW], woff[WPW];
+    constexpr int CX = XROW / 16, CW = WROW / 16;  // 16-byte chunks per row
+#pragma unroll
+    for (int j = 0; j < XPW; ++j) {
+        const int b = wave * XPW + j;
+        const int r = b * (1024 / XROW) + lane / CX, c = (lane % CX) ^ swz8<BK>(r);
+        xoff[j] = (uint32_t)((m0 + r) * K) + c * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < WPW; ++j) {
+        const int b = wave * WPW + j;
+        const int r = b * (1024 / WROW) + lane / CW;
+        const int c = (lane % CW) ^ (BITS == 8 ? swz8<BK>(r) : swz4<BK>(r));
+        woff[j] = (uint32_t)((n0 + r) * (int64_t)wld) + c * 16;
+    }
+    // Copy instruction j (0 <= j < D) of this wave's share of tile `src`
+    // into LDS stage `stage`.
+    auto copy_one = [&](int j, int stage, int src) {
+        uint8_t *st = smem + stage * STAGE;
+        if (j < XPW)
+            dma16(rX, st + (wave * XPW + j) * 1024, xoff[j] + (uint32_t)src * XROW);
+        else
+            dma16(rW, st + XBYTES + (wave * WPW + (j - XPW)) * 1024,
+                  woff[j - XPW] + (uint32_t)src * WROW);
+    };
+
+    // Fragment register sets: a = weight rows (operand A, int8 codes; for
+    // int4 the packed bytes sit in ap until widened), b = token rows.
+    struct Frags {
+        i32x4 a[FN];
+        uint2 ap[BITS == 4 ? FN : 1];
+        i32x4 b[FM];
+    };
+    const int frow = lane & 31, fhalf = lane >> 5;
+    constexpr int LOADS = FN + FM;
+    // Fragment read k: weight fragments first, then token fragments.
+    auto load_one = [&](Frags &f, int k, int kt, int ks) {
+        const uint8_t *st = smem + (kt % STAGES) * STAGE;
+        if (k < FN) {
+            const int r = wn * WN + k * 32 + frow;
+            if constexpr (BITS == 8)
+                f.a[k] = *reinterpret_cast<const i32x4 *>(st + XBYTES + off8<BK>(r, ks * 2 + fhalf));
+            else
+                f.ap[k] = *reinterpret_cast<const uint2 *>(st + XBYTES + off4<BK>(r, ks) + fhalf * 8);
+        } else {
+            const int j = k - FN;
+            f.b[j] = *reinterpret_cast<const i32x4 *>(st + off8<BK>(wm * WM + j * 32 + frow, ks * 2 + fhalf));
+        }
+    };
+    auto widen = [&](Frags &f, int i) {
+        if constexpr (BITS == 4) {
+            uint32_t d0, d1, d2, d3;
+            unpack8(f.ap[i].x, d0, d1);
+            unpack8(f.ap[i].y, d2, d3);
+            f.a[i] = i32x4{(int)d0, (int)d1, (int)d2, (int)d3};
+        }
+    };
+
+    i32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+            acc[i][j] = i32x16{};
+
+    // One 32-deep step: `copies` copy instructions first (a short burst; the
+    // other wavefront on the SIMD keeps the matrix core busy meanwhile), then
+    // the FN x FM MFMAs on `cur` with the LOADS fragment reads of the next
+    // step (into `nxt`) spread between them by the scheduler.
+    auto step = [&](Frags &cur, Frags &nxt, int lkt, int lks, int copies, int cstart, int cstage,
+                    int csrc) {
+        constexpr int MF = FN * FM;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            if (c < copies)
+                copy_one(cstart + c, cstage, csrc);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < LOADS; ++k)
+            load_one(nxt, k, lkt, lks);
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            widen(cur, i);
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0);
+        }
+        constexpr int PER = MF / LOADS > 0 ? MF / LOADS : 1;
+#pragma unroll
+        for (int k = 0; k < LOADS; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // then MFMAs
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // The dequant scales of this tile's channels and tokens, staged in LDS at
+    // the start (plain loads whose latency hides under the prologue copies);
+    // indices are clamped into range, values past the edge are never used.
+    if constexpr (OUT == OUT_F16) {
+        for (int t = threadIdx.x; t < TN + TM; t += NW * 64) {
+            if (t < TN)
+                s_sw[t] = args.s_w[min(n0 + t, N - 1)];
+            else
+                s_st[t - TN] = args.s_tok[min(m0 + (t - TN), M - 1)];
+        }
+    }
+
+    // Ring of STAGES stages.  Tile kt is computed from stage kt % STAGES;
+    // while it runs, tile kt + STAGES - 1 is copied into the stage tile kt-1
+    // used (free since tile kt-1's barrier), half of its copies during each
+    // of the two steps.  Every iteration issues exactly one tile of copies
+    // (past the end they re-read tile KT-1 into the free stage, which nobody
+    // reads), so the vmcnt bound at each barrier is a constant.
+    static_assert(KSTEPS == 2, "two 32-deep steps per tile");
+    static_assert(STAGES >= 3, "the refill targets the stage freed one tile earlier");
+    constexpr int DA = D / 2;
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            copy_one(j, p, min(p, KT - 1));
+    wait_vmcnt<(STAGES - 2) * D>();  // tile 0 has landed
+    __builtin_amdgcn_s_barrier();
+    Frags f0, f1;
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k)
+        load_one(f0, k, 0, 0);
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int rstage = (kt + STAGES - 1) % STAGES;  // == (kt - 1) mod STAGES
+        const int rsrc = min(kt + STAGES - 1, KT - 1);
+        // step 0: reads step 1's fragments, first half of the refill
+        step(f0, f1, kt, 1, DA, 0, rstage, rsrc);
+        // Tile kt+1 must have landed; tiles kt+2 .. kt+STAGES-2 and the first
+        // half of tile kt+STAGES-1 may still be in flight.  Every wave must
+        // also be done reading tile kt's stage before anyone refills it.
+        wait_lgkm0();
+        wait_vmcnt<(STAGES - 3) * D + DA>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // step 1: reads tile kt+1's step-0 fragments (at the last tile: a stage
+        // whose contents are never used), second half of the refill
+        step(f1, f0, kt + 1, 0, D - DA, DA, rstage, rsrc);
+    }
+
+    // Epilogue.  Block (i, j) gives the lane token m = wm*WM + 32j + lane%32
+    // and, for q = 0..3, output channels nb .. nb+3, nb = wn*WN + 32i + 8q +
+    // 4*(lane/32).
+    const bool full = m0 + TM <= M && n0 + TN <= N;  // uniform across the workgroup
+    if constexpr (OUT == OUT_I32) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int64_t m = m0 + wm * WM + j * 32 + frow;
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t nb = n0 + wn * WN + i * 32 + q * 8 + fhalf * 4;
+                    if (full || (m < M && nb < N)) {
+                        const i32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                         acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                        *reinterpret_cast<i32x4 *>(static_cast<int32_t *>(args.out) + m * N + nb) = v;
+                    }
+                }
+        }
+    } else {
+        // fp16 results go through this wave's own LDS region, laid out as
+        // [token][channel] rows of 2*WN bytes with 16-byte chunk c of row r at
+        // slot c ^ (r % CPRO), then leave as 16-byte stores that cover whole
+        // row segments.
+        constexpr int ROWB = WN * 2, CPRO = ROWB / 16;
+        static_assert(CPRO == 16 || CPRO == 8 || CPRO == 4, "output row chunks");
+        __syncthreads();  // every wave is done with the operand stages
+        uint8_t *ob = smem + wave * (WM * WN * 2);
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int r = j * 32 + frow;
+            const float st = s_st[wm * WM + r];
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = i * 32 + q * 8 + fhalf * 4;  // channel within the wave tile
+                    const f32x4 sw = *reinterpret_cast<const f32x4 *>(&s_sw[wn * WN + c]);
+                    float y[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        y[e] = (float)acc[i][j][4 * q + e] * st * sw[e];
+                    uint2 packed;
+                    packed.x = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[0]) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[1]) << 16);
+                    packed.y = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[2]) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[3]) << 16);
+                    const int chunk = c >> 3, within = (c & 7) * 2;
+                    *reinterpret_cast<uint2 *>(ob + r * ROWB + ((chunk ^ (r % CPRO)) << 4) + within) =
+                        packed;
+                }
+        }
+        // Each lane now stores 16-byte chunks: CPRO lanes per token row.
+        constexpr int ROWS_PER_PASS = 64 / CPRO;
+        const int lc = lane % CPRO, lr = lane / CPRO;
+        uint16_t *yout = static_cast<uint16_t *>(args.out);
+#pragma unroll 4
+        for (int p = 0; p < WM / ROWS_PER_PASS; ++p) {
+            const int r = p * ROWS_PER_PASS + lr;
+            const uint4 v = *reinterpret_cast<const uint4 *>(ob + r * ROWB + ((lc ^ (r % CPRO)) << 4));
+            const int64_t m = m0 + wm * WM + r;
+            const int64_t n = n0 + wn * WN + lc * 8;
+            if (full || (m < M && n < N))
+                *reinterpret_cast<uint4 *>(yout + m * N + n) = v;
+        }
+    }
+}
+
+template <int TN, int TM, int WN, int WM, int BK, int BITS, int OUT, int STAGES>
+hipError_t launch_cfg(const ProductArgs &a, hipStream_t stream)
+{
+    const int tiles_n = (int)((a.N + TN - 1) / TN);
+    const int tiles_m = (int)((a.M + TM - 1) / TM);
+    dim3 grid(tiles_n * tiles_m), block((TN / WN) * (TM / WM) * 64);
+    hipLaunchKernelGGL((gemm_pc_kernel<TN, TM, WN, WM, BK, BITS, OUT, STAGES>), grid, block, 0, stream,
+                       a, tiles_n, tiles_m, 8);
+    return hipGetLastError();
+}
+
+template <int BITS, int OUT>
+hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
+{
+    if (a.M >= 512)
+        return launch_cfg<256, 256, 128, 64, 64, BITS, OUT, 4>(a, stream);
+    return launch_cfg<128, 64, 64, 32, 64, BITS, OUT, 4>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_pc(const ProductArgs &a, hipStream_t stream)
+{
+    const bool f16 = a.out_kind == OUT_F16;
+    if (a.bits == 8)
+        return f16 ? launch_bits<8, OUT_F16>(a, stream) : launch_bits<8, OUT_I32>(a, stream);
+    return f16 ? launch_bits<4, OUT_F16>(a, stream) : launch_bits<4, OUT_I32>(a, stream);
+}
+
+}  // namespace cider
