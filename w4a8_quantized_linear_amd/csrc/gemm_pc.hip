@@ -81,13 +81,22 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *p, uint32_t bytes)
 // before each later LDS read; ordering against readers is enforced here by
 // the counted vmcnt waits and barriers of the pipeline instead.  There is no
 // register result: the data goes to LDS, and the operands are read at issue.
-__device__ __forceinline__ void dma16(const i32x4 &rsrc, const void *lds_block, uint32_t voffset)
+__device__ __forceinline__ uint32_t lds_address(const void *p)
 {
-    const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_t *)lds_block;
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
+    return (uint32_t)(uintptr_t)(lds_void_t *)p;
+}
+
+__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t lds_block, uint32_t voffset)
+{
+    const int lds = __builtin_amdgcn_readfirstlane((int)lds_block);
+    int saved;  // m0 is left exactly as the compiler had it
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %1\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
                  : "s"(lds), "v"(voffset), "s"(rsrc)
-                 : "memory", "m0");
+                 : "memory");
 }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits 3:0 and
@@ -146,15 +155,15 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_pc_kernel(
     constexpr int XBYTES = TM * XROW, WBYTES = TN * WROW;            // per stage
     constexpr int STAGE = XBYTES + WBYTES;
     constexpr int XB = XBYTES / 1024, WB = WBYTES / 1024;            // 1 KB copy blocks
-    constexpr int XPW = (XB + NW - 1) / NW, WPW = (WB + NW - 1) / NW;
-    constexpr int D = XPW + WPW;                                     // copies per wave per tile
-    static_assert(XB >= 1 && WB >= 1, "tiles of at least 1 KB");
-    static_assert(XB % NW == 0 && WB % NW == 0, "copy blocks split evenly over wavefronts");
+    constexpr int TB = XB + WB;
+    // Copies per wave per tile.  When the blocks do not split evenly, the
+    // last slots repeat the final block (identical bytes to the same place),
+    // so every wave issues the same number and vmcnt counts stay uniform.
+    constexpr int D = (TB + NW - 1) / NW;
+    static_assert(XBYTES % 1024 == 0 && WBYTES % 1024 == 0, "tiles of whole 1 KB blocks");
     static_assert(STAGES >= 2 && (STAGES - 1) * D < 64, "vmcnt range");
 
-    constexpr int OUT_BYTES = NW * WM * WN * 2;  // fp16 output staging, one region per wave
-    __shared__ __attribute__((aligned(1024))) uint8_t
-        smem[STAGES * STAGE > OUT_BYTES ? STAGES * STAGE : OUT_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
     __shared__ __attribute__((aligned(16))) float s_sw[OUT == OUT_F16 ? TN : 4];   // s_w tile
     __shared__ __attribute__((aligned(16))) float s_st[OUT == OUT_F16 ? TM : 4];   // s_tok tile
 
@@ -171,32 +180,36 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_pc_kernel(
     const i32x4 rX = make_rsrc(args.xq, (uint32_t)(M * K));
     const i32x4 rW = make_rsrc(args.wq, (uint32_t)(N * (int64_t)wld));
 
-    // Source offset of this lane's 16 bytes in each of the wave's copy blocks:
-    // LDS slot s of row r receives global chunk s ^ swizzle(r).
-    uint32_t xoff[XPW], woff[WPW];
+    // Source offset of this lane's 16 bytes in each of the wave's copy blocks,
+    // and the block's LDS offset within a stage.  Blocks 0 .. XB-1 hold token
+    // rows, the rest weight rows; LDS slot s of row r receives global chunk
+    // s ^ swizzle(r).
     constexpr int CX = XROW / 16, CW = WROW / 16;  // 16-byte chunks per row
+    uint32_t coff[D], cstep[D];
+    int cdst[D];
+    i32x4 crs[D];
 #pragma unroll
-    for (int j = 0; j < XPW; ++j) {
-        const int b = wave * XPW + j;
-        const int r = b * (1024 / XROW) + lane / CX, c = (lane % CX) ^ swz8<BK>(r);
-        xoff[j] = (uint32_t)((m0 + r) * K) + c * 16;
-    }
-#pragma unroll
-    for (int j = 0; j < WPW; ++j) {
-        const int b = wave * WPW + j;
-        const int r = b * (1024 / WROW) + lane / CW;
-        const int c = (lane % CW) ^ (BITS == 8 ? swz8<BK>(r) : swz4<BK>(r));
-        woff[j] = (uint32_t)((n0 + r) * (int64_t)wld) + c * 16;
+    for (int j = 0; j < D; ++j) {
+        const int b = min(wave * D + j, TB - 1);  // wavefront-uniform
+        crs[j] = b < XB ? rX : rW;
+        cstep[j] = b < XB ? XROW : WROW;
+        if (b < XB) {
+            const int r = b * (1024 / XROW) + lane / CX, c = (lane % CX) ^ swz8<BK>(r);
+            coff[j] = (uint32_t)((m0 + r) * K) + c * 16;
+            cdst[j] = b * 1024;
+        } else {
+            const int bw = b - XB;
+            const int r = bw * (1024 / WROW) + lane / CW;
+            const int c = (lane % CW) ^ (BITS == 8 ? swz8<BK>(r) : swz4<BK>(r));
+            coff[j] = (uint32_t)((n0 + r) * (int64_t)wld) + c * 16;
+            cdst[j] = XBYTES + bw * 1024;
+        }
     }
     // Copy instruction j (0 <= j < D) of this wave's share of tile `src`
     // into LDS stage `stage`.
+    const uint32_t smem_lds = lds_address(smem);
     auto copy_one = [&](int j, int stage, int src) {
-        uint8_t *st = smem + stage * STAGE;
-        if (j < XPW)
-            dma16(rX, st + (wave * XPW + j) * 1024, xoff[j] + (uint32_t)src * XROW);
-        else
-            dma16(rW, st + XBYTES + (wave * WPW + (j - XPW)) * 1024,
-                  woff[j - XPW] + (uint32_t)src * WROW);
+        dma16(crs[j], smem_lds + stage * STAGE + cdst[j], coff[j] + (uint32_t)src * cstep[j]);
     };
 
     // Fragment register sets: a = weight rows (operand A, int8 codes; for
@@ -340,18 +353,18 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_pc_kernel(
                 }
         }
     } else {
-        // fp16 results go through this wave's own LDS region, laid out as
-        // [token][channel] rows of 2*WN bytes with 16-byte chunk c of row r at
-        // slot c ^ (r % CPRO), then leave as 16-byte stores that cover whole
-        // row segments.
-        constexpr int ROWB = WN * 2, CPRO = ROWB / 16;
-        static_assert(CPRO == 16 || CPRO == 8 || CPRO == 4, "output row chunks");
+        // fp16 results go through this wave's own LDS region one 32-token
+        // block at a time: rows of 2*WN bytes padded by 16 (so the 32 rows a
+        // write instruction touches fall in distinct bank groups), then leave
+        // as 16-byte stores, consecutive lanes along a token row.
+        constexpr int ROWB = WN * 2 + 16, CPRO = WN * 2 / 16;
+        static_assert(NW * 32 * ROWB <= STAGES * STAGE, "output staging fits the stage ring");
         __syncthreads();  // every wave is done with the operand stages
-        uint8_t *ob = smem + wave * (WM * WN * 2);
+        uint8_t *ob = smem + wave * (32 * ROWB);
+        uint16_t *yout = static_cast<uint16_t *>(args.out);
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
-            const int r = j * 32 + frow;
-            const float st = s_st[wm * WM + r];
+            const float st = s_st[wm * WM + j * 32 + frow];
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -367,23 +380,21 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_pc_kernel(
                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[1]) << 16);
                     packed.y = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[2]) |
                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[3]) << 16);
-                    const int chunk = c >> 3, within = (c & 7) * 2;
-                    *reinterpret_cast<uint2 *>(ob + r * ROWB + ((chunk ^ (r % CPRO)) << 4) + within) =
-                        packed;
+                    *reinterpret_cast<uint2 *>(ob + frow * ROWB + c * 2) = packed;
                 }
-        }
-        // Each lane now stores 16-byte chunks: CPRO lanes per token row.
-        constexpr int ROWS_PER_PASS = 64 / CPRO;
-        const int lc = lane % CPRO, lr = lane / CPRO;
-        uint16_t *yout = static_cast<uint16_t *>(args.out);
-#pragma unroll 4
-        for (int p = 0; p < WM / ROWS_PER_PASS; ++p) {
-            const int r = p * ROWS_PER_PASS + lr;
-            const uint4 v = *reinterpret_cast<const uint4 *>(ob + r * ROWB + ((lc ^ (r % CPRO)) << 4));
-            const int64_t m = m0 + wm * WM + r;
-            const int64_t n = n0 + wn * WN + lc * 8;
-            if (full || (m < M && n < N))
-                *reinterpret_cast<uint4 *>(yout + m * N + n) = v;
+            constexpr int CHUNKS = 32 * CPRO;
+#pragma unroll
+            for (int it = 0; it < (CHUNKS + 63) / 64; ++it) {
+                const int id = it * 64 + lane;
+                if (CHUNKS % 64 == 0 || id < CHUNKS) {
+                    const int r = id / CPRO, c = id % CPRO;
+                    const uint4 v = *reinterpret_cast<const uint4 *>(ob + r * ROWB + c * 16);
+                    const int64_t m = m0 + wm * WM + j * 32 + r;
+                    const int64_t n = n0 + wn * WN + c * 8;
+                    if (full || (m < M && n < N))
+                        *reinterpret_cast<uint4 *>(yout + m * N + n) = v;
+                }
+            }
         }
     }
 }
@@ -403,7 +414,7 @@ template <int BITS, int OUT>
 hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
 {
     if (a.M >= 512)
-        return launch_cfg<256, 256, 128, 64, 64, BITS, OUT, 4>(a, stream);
+        return launch_cfg<320, 256, 160, 64, 64, BITS, OUT, 4>(a, stream);
     return launch_cfg<128, 64, 64, 32, 64, BITS, OUT, 4>(a, stream);
 }
 
