@@ -40,17 +40,16 @@ __device__ __forceinline__ float quant_divisor()
     return BITS == 8 ? 127.0f : 7.0f;
 }
 
-// Integer code of x for scale s.
+// Integer code of x for scale s.  Branch-free: for s == 0 (an all-zero
+// row) the quotient is discarded by the final select.
 template <int BITS>
 __device__ __forceinline__ int quant_code(float x, float s)
 {
     constexpr float lo = BITS == 8 ? -127.0f : -8.0f;
     constexpr float hi = BITS == 8 ? 127.0f : 7.0f;
-    if (s == 0.0f)
-        return 0;
     float r = __builtin_rintf(x / s);
-    r = __builtin_fminf(__builtin_fmaxf(r, lo), hi);
-    return (int)r;
+    r = __builtin_fminf(__builtin_fmaxf(r, lo), hi);  // maxNum/minNum: NaN -> bound
+    return s == 0.0f ? 0 : (int)r;
 }
 
 // Codes of the 8 fp16 values of a chunk, packed: int8 -> 8 bytes (uint2),
