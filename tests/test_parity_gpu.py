@@ -61,6 +61,62 @@ def test_quantize_act_bitexact(M, K, ldx):
     assert np.array_equal(gu.to_host(xq), rq)
 
 
+def _near_half_rows(amaxes, K=640):
+    """One row per absmax A: A itself and, for every half-integer h + 0.5 below
+    127, the fp16 values nearest (h + 0.5) * s and their two neighbours on each
+    side (s = fl32(A / 127)), signs alternating; zeros after.  Quotients at or
+    within a few ulps of a half-integer, where the rounding of x / s decides
+    the code."""
+    rows, ties = [], 0
+    for A in amaxes:
+        a16 = np.float16(A)
+        s = np.float32(a16) / np.float32(127.0)
+        vals = [a16]
+        for h in range(127):
+            base = np.array([(h + 0.5) * float(s)], np.float16).view(np.uint16)[0]
+            for d in (-2, -1, 0, 1, 2):
+                b = int(base) + d
+                if 0 <= b <= int(np.array([a16]).view(np.uint16)[0]):
+                    vals.append(np.array([b], np.uint16).view(np.float16)[0])
+        row = np.zeros(K, np.float16)
+        v = np.array(vals[:K], np.float16)
+        v[1::2] = -v[1::2]
+        row[:len(v)] = v
+        q32 = np.abs(row.astype(np.float32) / s)
+        ties += int(np.sum(q32 - np.floor(q32) == 0.5))
+        rows.append(row)
+    return np.stack(rows), ties
+
+
+NEAR_HALF_AMAX = [1.0, 0.7, 3.0, 100.0, 65504.0, 2.0 ** -10, 2.0 ** -14, 0.3337, 12.34] + list(
+    2.0 ** np.random.default_rng(17).uniform(-14.0, 15.9, 119))
+
+
+def test_quantize_near_half_quotients():
+    """Codes where fl32(x / s) sits on or next to a half-integer: the kernel's
+    rounding of the quotient must match the oracle's bit for bit (both the
+    per-token quantize kernel and, through an identity weight, the fused
+    one-token path)."""
+    orc = get_oracle()
+    x, ties = _near_half_rows(NEAR_HALF_AMAX)
+    assert ties > 0, "the rows must contain exact half-integer quotients"
+    M, K = x.shape
+    xq, st = gu.quantize_act_gpu(gu.to_dev(x), M, K, K)
+    rq, rs = orc.quantize_act(x, K=K)
+    assert np.array_equal(gu.to_host(st), rs)
+    assert np.array_equal(gu.to_host(xq), rq)
+    # fused path: y = 127 q s_tok s_w for an identity weight, one token at a time
+    eye = np.eye(K, dtype=np.float16)
+    wq, sw = orc.quantize_weight(eye, 8, 0)
+    wd, swd = gu.to_dev(wq), gu.to_dev(sw)
+    for i in range(M):
+        row = x[i:i + 1]
+        y = gu.to_host(gu.linear_gpu(gu.to_dev(row), 1, K, K, wd, swd, K, 8, 0))
+        ref, rxq, _ = orc.linear(row, wq, sw, 8, 0, K=K)
+        assert np.array_equal(rxq, rq[i:i + 1])
+        gu.assert_f16_close(y, ref, "near-half row %d" % i)
+
+
 WEIGHT_CASES = [(512, 1024, 8, 0), (512, 1024, 8, 64), (512, 1024, 8, 128), (512, 1024, 4, 0),
                 (10240, 2560, 8, 0), (2560, 10240, 8, 64), (2560, 10240, 8, 128),
                 (10240, 2560, 4, 0), (64, 20480, 8, 0), (64, 20480, 4, 0)]

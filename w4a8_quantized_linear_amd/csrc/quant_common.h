@@ -40,30 +40,23 @@ __device__ __forceinline__ float quant_divisor()
     return BITS == 8 ? 127.0f : 7.0f;
 }
 
-// Integer code of x for scale s.  Branch-free: for s == 0 (an all-zero
-// row) the quotient is discarded by the final select.
+// Integer code of x for scale s, given the quotient x / s.  Branch-free: for
+// s == 0 (an all-zero row) the quotient is discarded by the final select.
 template <int BITS>
-__device__ __forceinline__ int quant_code(float x, float s)
+__device__ __forceinline__ int code_of(float quotient, float s)
 {
     constexpr float lo = BITS == 8 ? -127.0f : -8.0f;
     constexpr float hi = BITS == 8 ? 127.0f : 7.0f;
-    float r = __builtin_rintf(x / s);
+    float r = __builtin_rintf(quotient);
     r = __builtin_fminf(__builtin_fmaxf(r, lo), hi);  // maxNum/minNum: NaN -> bound
     return s == 0.0f ? 0 : (int)r;
 }
 
-// Codes of the 8 fp16 values of a chunk, packed: int8 -> 8 bytes (uint2),
-// int4 -> 8 nibbles u = q + 8 with value e at bits 4e (uint32 in .x).
+// Packs 8 codes: int8 -> 8 bytes (uint2), int4 -> 8 nibbles u = q + 8 with
+// value e at bits 4e (uint32 in .x).
 template <int BITS>
-__device__ __forceinline__ uint2 quantize_chunk(uint4 v, float s)
+__device__ __forceinline__ uint2 pack_codes(const int (&q)[8])
 {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    int q[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        q[2 * j] = quant_code<BITS>(half_bits_to_float(w[j] & 0xFFFFu), s);
-        q[2 * j + 1] = quant_code<BITS>(half_bits_to_float(w[j] >> 16), s);
-    }
     uint2 o;
     if constexpr (BITS == 8) {
         o.x = (uint32_t)(q[0] & 0xFF) | ((uint32_t)(q[1] & 0xFF) << 8) |
@@ -79,6 +72,60 @@ __device__ __forceinline__ uint2 quantize_chunk(uint4 v, float s)
         o.y = 0;
     }
     return o;
+}
+
+// Codes of the 8 fp16 values of a chunk, packed: int8 -> 8 bytes (uint2),
+// int4 -> 8 nibbles u = q + 8 with value e at bits 4e (uint32 in .x).
+// rs must be 1.0f / s (correctly rounded).
+//
+// The code is rint of the correctly rounded quotient fl(x / s).  The product
+// t = fl(x * rs) differs from fl(x / s) by at most 3 * 2^-24 relative, i.e.
+// below 2^-15.4 in absolute terms for |x / s| <= 127.5, so rint(t) equals
+// rint(fl(x / s)) unless t lies within that distance of a half-integer.  A
+// chunk with a value within 2^-14 of a half-integer (about 1 value in 8000)
+// is recomputed with correctly rounded divisions.
+template <int BITS>
+__device__ __forceinline__ uint2 quantize_chunk(uint4 v, float s, float rs)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float f[8], t[8];
+    bool near_half = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = half_bits_to_float(w[j] & 0xFFFFu);
+        f[2 * j + 1] = half_bits_to_float(w[j] >> 16);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        t[e] = f[e] * rs;
+        const float d = t[e] - __builtin_rintf(t[e]);  // in [-0.5, 0.5]; NaN stays unflagged
+        near_half |= __builtin_fabsf(__builtin_fabsf(d) - 0.5f) < 0x1p-14f;
+    }
+    if (near_half) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            t[e] = f[e] / s;
+    }
+    int q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        q[e] = code_of<BITS>(t[e], s);
+    return pack_codes<BITS>(q);
+}
+
+// The same codes with a correctly rounded division for every value (fewer
+// live registers: for kernels that hold long rows in registers).
+template <int BITS>
+__device__ __forceinline__ uint2 quantize_chunk_div(uint4 v, float s)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    int q[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        q[2 * j] = code_of<BITS>(half_bits_to_float(w[j] & 0xFFFFu) / s, s);
+        q[2 * j + 1] = code_of<BITS>(half_bits_to_float(w[j] >> 16) / s, s);
+    }
+    return pack_codes<BITS>(q);
 }
 
 }  // namespace cider

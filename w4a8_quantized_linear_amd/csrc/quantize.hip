@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__re
     for (int i = 0; i < NCH; ++i) {
         const int c = i * TS + lane;
         if (c < nch) {
-            const uint2 q = quantize_chunk<BITS>(v[i], s);
+            const uint2 q = quantize_chunk_div<BITS>(v[i], s);
             if constexpr (BITS == 8)
                 *reinterpret_cast<uint2 *>(out + row * len + (int64_t)c * 8) = q;
             else
@@ -91,10 +91,11 @@ __global__ __launch_bounds__(256) void quantize_long_rows_kernel(const uint16_t 
     for (int w = 1; w < 4; ++w)
         amax = red[w] > amax ? red[w] : amax;
     const float s = half_bits_to_float(amax) / quant_divisor<BITS>();
+    const float rs = 1.0f / s;
     if (threadIdx.x == 0)
         scale[row] = s;
     for (int64_t c = threadIdx.x; c < nch; c += 256) {
-        const uint2 q = quantize_chunk<BITS>(*reinterpret_cast<const uint4 *>(xr + c * 8), s);
+        const uint2 q = quantize_chunk<BITS>(*reinterpret_cast<const uint4 *>(xr + c * 8), s, rs);
         if constexpr (BITS == 8)
             *reinterpret_cast<uint2 *>(out + row * len + c * 8) = q;
         else
