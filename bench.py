@@ -8,9 +8,12 @@ product with fused dequantization (cider_w8a8_gemm) -- exactly what
 cider_w8a8_linear runs, issued as its two calls so the product kernel can be
 timed on its own with HIP events recorded on the launch stream.
 
-`value` is INT8 TOPS of the whole step (2*M*N*K / step time).  The JSON line
-also carries: the roofline of the product kernel (achieved TOPS from the
-kernel's event-timed duration against the 5.0 POPS dense INT8 peak), the
+`value` is INT8 TOPS of the whole step (2*M*N*K / step time, steps back to
+back).  The JSON line also carries: the roofline of the product kernel
+(achieved TOPS from its average launch duration -- the same launches timed
+back to back between two HIP events on the launch stream -- against the
+5.0 POPS dense INT8 peak, and its HBM bytes per launch from the committed
+counter summary), the
 oracle's CPU throughput on a bounded sample of the same workload, the
 one-token path's GB/s against 8 TB/s, and a sweep over the operator
 workloads.  Inputs are rotated over >= 1 GB of copies so that the 256 MB
@@ -50,6 +53,10 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-m1", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
+                        "reference for the HBM byte counters)")
     return p.parse_args()
 
 
@@ -108,17 +115,29 @@ def copies_for(bits, gs, N, K, M):
     return max(1, min(64, math.ceil(ROTATE_BYTES / per)))
 
 
-def time_events(torch, fn, n, start_index=0):
-    """Average device duration of fn(i) over n launches, one HIP event pair
-    per launch on the current stream; returns seconds."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n)]
-    for i, (a, b) in enumerate(evs):
-        a.record()
-        fn(start_index + i)
-        b.record()
-    torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / n / 1e3
+def graph_time(torch, fn, n, replays):
+    """Average time per call of fn(0..n-1) captured once into a HIP graph and
+    replayed `replays` times back to back (events around the replays on the
+    capture stream): the device-side rate of back-to-back launches, without
+    the host's per-call launch cost.  Returns seconds per call."""
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for i in range(n):          # warm (and leaves every buffer touched)
+            fn(i)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                fn(i)
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(replays):
+            g.replay()
+        b.record(stream)
+    b.synchronize()
+    torch.cuda.current_stream().wait_stream(stream)
+    return a.elapsed_time(b) / 1e3 / (n * replays)
 
 
 def traffic_record(kernel_source, workload):
@@ -172,6 +191,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copied 1 GiB 5 times")
+        return
     cider.load(build_if_missing=True)
     assert cider.cider_is_available(), "libcider.so reports no usable gfx950 device"
 
@@ -187,29 +214,37 @@ def main():
         L.linear(i)
     torch.cuda.synchronize()
     log("timing %d steps (%d rotating copies)" % (args.steps, B))
-    gemm_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-    quant_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
+    # timed region 1: whole steps back to back -> value, ms_per_step
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        quant_ev[i][0].record()
         L.quantize(i)
-        quant_ev[i][1].record()
-        gemm_ev[i][0].record()
         L.gemm(i)
-        gemm_ev[i][1].record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    gemm_s = sum(a.elapsed_time(b) for a, b in gemm_ev) / args.steps / 1e3
-    quant_s = sum(a.elapsed_time(b) for a, b in quant_ev) / args.steps / 1e3
     ms_per_step = dt / args.steps * 1e3
     value = ops / (dt / args.steps) / 1e12
+    # timed region 2: the product kernel alone, the same launches back to back
+    # between two HIP events on its stream -> its average launch duration
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        L.gemm(i)
+    e1.record(stream)
+    e1.synchronize()
+    gemm_s = e0.elapsed_time(e1) / 1e3 / args.steps
     achieved = ops / gemm_s / 1e12
-    log("step %.2f us, gemm kernel %.2f us (%.0f TOPS), quantize kernel %.2f us"
+    # the quantize kernel alone, likewise
+    e0.record(stream)
+    for i in range(args.steps):
+        L.quantize(i)
+    e1.record(stream)
+    e1.synchronize()
+    quant_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    log("step %.2f us, product kernel %.2f us (%.0f TOPS), quantize kernel %.2f us"
         % (ms_per_step * 1e3, gemm_s * 1e6, achieved, quant_s * 1e6))
-    traffic = traffic_record(os.path.join(ROOT, "w4a8_quantized_linear_amd", "csrc", "gemm.hip"),
+    traffic = traffic_record(os.path.join(ROOT, "w4a8_quantized_linear_amd", "csrc", "gemm_pc.hip"),
                              "w8a8_pc_N10240_K2560_M4096")
     result = {
         "metric": "INT8 TOPS (% of MFMA peak) at M=4096; GB/s (% of HBM peak) at M=1",
@@ -231,7 +266,8 @@ def main():
                    "rotating_copies": B},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
                      "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                     "traffic": traffic, "kernel": "gemm_kernel (int8 matrix-core product)",
+                     "traffic": traffic,
+                     "kernel": "gemm_pc_kernel (per-channel int8 matrix-core product + dequant)",
                      "kernel_us": round(gemm_s * 1e6, 2),
                      "quantize_kernel_us": round(quant_s * 1e6, 2)},
     }
@@ -239,59 +275,14 @@ def main():
     torch.cuda.empty_cache()
 
     # --------------------------------------------------------- one token ---
-    x1 = x_np[:1]
-    B1 = copies_for(8, 0, N, K, 1)
-    L1 = Layer(torch, cider, 8, 0, N, K, 1, x1, w_np, B1)
-    for i in range(20):
-        L1.linear(i)
-    s1 = time_events(torch, L1.linear, 200, 20)
-    b1 = alg_bytes(8, 0, N, K, 1)
-    result["m1"] = {"workload": "W8A8 per-channel N=10240 K=2560 M=1, quantization fused",
-                    "kernel_us": round(s1 * 1e6, 3), "bytes": b1,
-                    "gbps": round(b1 / s1 / 1e9, 1),
-                    "frac": round(b1 / s1 / 1e9 / PEAK_HBM_GBPS, 4),
-                    "rotating_copies": B1}
-    log("M=1: %.2f us, %.0f GB/s" % (s1 * 1e6, b1 / s1 / 1e9))
-    del L1
-    torch.cuda.empty_cache()
+    if args.no_m1:
+        result["m1"] = None
+    else:
+        one_token(torch, cider, x_np, w_np, N, K, result)
 
     # ------------------------------------------------------------- sweep ---
     if not args.no_sweep:
-        sweep = []
-        for name, wl in si.WORKLOADS.items():
-            if name == "w8a8_pc_small":
-                continue
-            Nw, Kw = wl["N"], wl["K"]
-            xs = si.activations(max(wl["M"]), Kw)
-            ws = si.weights(Nw, Kw)
-            for gs in wl["group_sizes"]:
-                for Mw in wl["M"]:
-                    Bw = copies_for(wl["bits"], gs, Nw, Kw, Mw)
-                    Lw = Layer(torch, cider, wl["bits"], gs, Nw, Kw, Mw, xs[:Mw], ws, Bw)
-                    for i in range(5):
-                        Lw.linear(i)
-                    reps = 50 if Mw <= 1024 else 20
-                    e2e = time_events(torch, Lw.linear, reps, 5)
-                    gemm = time_events(torch, Lw.gemm, reps, 5) if Mw > 1 else None
-                    ab = alg_bytes(wl["bits"], gs, Nw, Kw, Mw)
-                    opw = 2.0 * Mw * Nw * Kw
-                    rec = {"workload": name, "group_size": gs, "M": Mw, "N": Nw, "K": Kw,
-                           "e2e_us": round(e2e * 1e6, 2),
-                           "e2e_tops": round(opw / e2e / 1e12, 2),
-                           "e2e_gbps": round(ab / e2e / 1e9, 1)}
-                    if gemm is not None:
-                        rec.update({"gemm_us": round(gemm * 1e6, 2),
-                                    "gemm_tops": round(opw / gemm / 1e12, 2),
-                                    "gemm_frac_mfma": round(opw / gemm / 1e12 / PEAK_INT8_TOPS, 4)})
-                    rec["e2e_frac_hbm"] = round(ab / e2e / 1e9 / PEAK_HBM_GBPS, 4)
-                    sweep.append(rec)
-                    log("sweep %s gs=%d M=%d: e2e %.2f us (%.1f TOPS, %.0f GB/s)%s"
-                        % (name, gs, Mw, e2e * 1e6, opw / e2e / 1e12, ab / e2e / 1e9,
-                           "" if gemm is None else ", gemm %.2f us" % (gemm * 1e6)))
-                    del Lw
-                    torch.cuda.empty_cache()
-            del xs, ws
-        result["sweep"] = sweep
+        result["sweep"] = sweep(torch, cider, si)
 
     # -------------------------------------------------------- CPU oracle ---
     if not args.no_cpu:
@@ -301,6 +292,64 @@ def main():
         result["cpu_baseline"] = None
 
     print(json.dumps(result), flush=True)
+
+
+def one_token(torch, cider, x_np, w_np, N, K, result):
+    """The one-token path: quantization fused into the matrix-vector kernel."""
+    x1 = x_np[:1]
+    B1 = copies_for(8, 0, N, K, 1)
+    L1 = Layer(torch, cider, 8, 0, N, K, 1, x1, w_np, B1)
+    s1 = graph_time(torch, L1.linear, B1, max(1, 4000 // B1))
+    b1 = alg_bytes(8, 0, N, K, 1)
+    result["m1"] = {"workload": "W8A8 per-channel N=10240 K=2560 M=1, quantization fused",
+                    "us_per_call": round(s1 * 1e6, 3), "bytes": b1,
+                    "gbps": round(b1 / s1 / 1e9, 1),
+                    "frac": round(b1 / s1 / 1e9 / PEAK_HBM_GBPS, 4),
+                    "timing": "HIP graph of back-to-back calls over rotating copies; "
+                              "includes the launch-to-launch gap",
+                    "rotating_copies": B1}
+    log("M=1: %.2f us per call, %.0f GB/s" % (s1 * 1e6, b1 / s1 / 1e9))
+    del L1
+    torch.cuda.empty_cache()
+
+
+def sweep(torch, cider, si):
+    """Every operator workload at every M: whole-layer and product-kernel
+    time per call (graph replay over rotating copies)."""
+    records = []
+    for name, wl in si.WORKLOADS.items():
+        if name == "w8a8_pc_small":
+            continue
+        Nw, Kw = wl["N"], wl["K"]
+        xs = si.activations(max(wl["M"]), Kw)
+        ws = si.weights(Nw, Kw)
+        for gs in wl["group_sizes"]:
+            for Mw in wl["M"]:
+                Bw = copies_for(wl["bits"], gs, Nw, Kw, Mw)
+                Lw = Layer(torch, cider, wl["bits"], gs, Nw, Kw, Mw, xs[:Mw], ws, Bw)
+                calls = max(Bw, 8)
+                replays = max(1, (200 if Mw <= 128 else 20) // calls)
+                e2e = graph_time(torch, Lw.linear, calls, replays)
+                gemm = graph_time(torch, Lw.gemm, calls, replays) if Mw > 1 else None
+                ab = alg_bytes(wl["bits"], gs, Nw, Kw, Mw)
+                opw = 2.0 * Mw * Nw * Kw
+                rec = {"workload": name, "group_size": gs, "M": Mw, "N": Nw, "K": Kw,
+                       "e2e_us": round(e2e * 1e6, 2),
+                       "e2e_tops": round(opw / e2e / 1e12, 2),
+                       "e2e_gbps": round(ab / e2e / 1e9, 1)}
+                if gemm is not None:
+                    rec.update({"gemm_us": round(gemm * 1e6, 2),
+                                "gemm_tops": round(opw / gemm / 1e12, 2),
+                                "gemm_frac_mfma": round(opw / gemm / 1e12 / PEAK_INT8_TOPS, 4)})
+                rec["e2e_frac_hbm"] = round(ab / e2e / 1e9 / PEAK_HBM_GBPS, 4)
+                records.append(rec)
+                log("sweep %s gs=%d M=%d: e2e %.2f us (%.1f TOPS, %.0f GB/s)%s"
+                    % (name, gs, Mw, e2e * 1e6, opw / e2e / 1e12, ab / e2e / 1e9,
+                       "" if gemm is None else ", gemm %.2f us" % (gemm * 1e6)))
+                del Lw
+                torch.cuda.empty_cache()
+        del xs, ws
+    return records
 
 
 if __name__ == "__main__":

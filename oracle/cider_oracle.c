@@ -20,7 +20,7 @@
  *   Same README, "Metal Kernel Pipeline": FP16 activations -> INT8 + per-token
  *   scales, then INT8 x INT8 -> INT32 -> FP16.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - scale s = absmax / 127 (int8) or absmax / 7 (int4), computed in fp32;
  *   - code q = clamp(round_half_even(fp32(x / s)), lo, hi), the quotient a
  *     correctly rounded fp32 division; int8 range [-127, 127], int4 [-8, 7];
@@ -34,7 +34,7 @@
  * Quantization decisions are taken in fp32 because the scales are fp32
  * values; everything after the integer accumulation is fp64.
  *
- * Build: gcc -O2 -ffp-contract=off -fopenmp -fPIC -shared (see build_oracle.py).
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -fPIC -shared (oracle.py, compile_oracle).
  * Rows are split across OpenMP threads; the arithmetic per row is the plain
  * loop written below, in the order written.
  */
