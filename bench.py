@@ -244,7 +244,7 @@ def main():
     quant_s = e0.elapsed_time(e1) / 1e3 / args.steps
     log("step %.2f us, product kernel %.2f us (%.0f TOPS), quantize kernel %.2f us"
         % (ms_per_step * 1e3, gemm_s * 1e6, achieved, quant_s * 1e6))
-    traffic = traffic_record(os.path.join(ROOT, "w4a8_quantized_linear_amd", "csrc", "gemm_pc.hip"),
+    traffic = traffic_record(os.path.join(ROOT, "w4a8_quantized_linear_amd", "csrc", "gemm.hip"),
                              "w8a8_pc_N10240_K2560_M4096")
     result = {
         "metric": "INT8 TOPS (% of MFMA peak) at M=4096; GB/s (% of HBM peak) at M=1",
@@ -267,7 +267,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
                      "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
                      "traffic": traffic,
-                     "kernel": "gemm_pc_kernel (per-channel int8 matrix-core product + dequant)",
+                     "kernel": "gemm_kernel (int8 matrix-core product + dequant, per channel)",
                      "kernel_us": round(gemm_s * 1e6, 2),
                      "quantize_kernel_us": round(quant_s * 1e6, 2)},
     }

@@ -31,12 +31,10 @@ struct ProductArgs {
     void *out;             // fp16 [M, N] or int32 [M, N] / [M, N, K/gs]
 };
 
-// Matrix-core product (any M >= 1): dispatches per-channel products to
-// launch_gemm_pc and per-group products to the group-scaling kernel.
+// Matrix-core product (any M >= 1, every mode).
 hipError_t launch_gemm(const ProductArgs &a, hipStream_t stream);
-hipError_t launch_gemm_pc(const ProductArgs &a, hipStream_t stream);
 
-// Matrix-vector product for M <= 8 and M * K <= 65536.
+// Matrix-vector product for M <= 8 and M * K <= 32768.
 hipError_t launch_gemv(const ProductArgs &a, hipStream_t stream);
 
 // One-token layer: quantizes the fp16 row x [K] inside the matrix-vector

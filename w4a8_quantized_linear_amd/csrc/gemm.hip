@@ -1,34 +1,36 @@
-// INT8 matrix-core product for the fused quantized linear layer on gfx950.
+// Pipelined matrix-core product for all three modes: W8A8 per channel, W8A8
+// per group of 64 / 128 along K, and W4A8 (Cider README, ossradar.top repo
+// page, "Quantization" table: INT32 accumulation, C_fp16 = C_int32 * s_act *
+// s_weight per element; "W8A8 Quantization Granularity": one scale per
+// output channel or per group; "Modes": W4A8 unpacks INT4 before the INT8
+// product; "TensorOps matmul2d": dequantization fused into the store phase).
 //
-// What it computes (Cider README, ossradar.top repo page, "Quantization"
-// table and "Metal Kernel Pipeline"): acc[m, n] = sum_k xq[m, k] * q_w[n, k]
-// in int32, then y = fp16(acc * s_tok[m] * s_w[n]) in the same kernel
-// ("TensorOps matmul2d": dequantization applied in the store phase).  Per
-// group of 64/128 along K ("W8A8 Quantization Granularity"): each group's
-// int32 sum is scaled by s_w[n, g] and added into an fp32 accumulator.  W4A8
-// ("Modes": Unpack -> TensorOps): packed nibbles are widened to int8 codes
-// before the int8 product.
-//
-// Design for CDNA4 (the pages' M5 tiling is prior art only):
-//   * v_mfma_i32_32x32x32_i8: 32x32 int32 block, 32-deep K per instruction
-//     (the full-rate int8 shape on gfx950; the 16x16x64 form issues at about
-//     half the rate).  The weight tile is the A operand and the activation
-//     tile the B operand, so each lane holds runs of four consecutive output
-//     channels n of one token m: the epilogue stores 8 contiguous bytes.
-//   * Tiles of TN x TM outputs per workgroup, WN x WM per wavefront, K
-//     staged BK at a time through LDS, double buffered: global loads of tile
-//     k+1 are in flight while the matrix cores consume tile k; one barrier
-//     per K tile.
-//   * LDS rows of BK bytes in 16-byte chunks, chunk c of row r stored at
-//     slot c ^ swz(r): the 16 rows a fragment read touches (same chunk) land
-//     in distinct bank groups, and so do the row-major tile writes.
-//   * W4A8: a 16-byte global chunk of packed nibbles becomes two 16-byte
-//     int8 chunks in LDS, once per workgroup; every wavefront then reads
-//     plain int8 fragments.
-//   * Workgroup -> tile mapping: consecutive workgroup ids go to different
-//     XCDs (round robin over 8), so ids are remapped to give every XCD a
-//     contiguous run of tiles, walked in groups of m-panels, so the tiles
-//     sharing an L2 also share weight and activation panels.
+// Structure (gfx950):
+//   * v_mfma_i32_32x32x32_i8; per channel the weight tile is operand A and
+//     the token tile operand B (a lane's outputs are 4 consecutive channels
+//     of one token); per group the roles swap (a lane's outputs are 16
+//     tokens of one channel, so each group needs one scale per lane and
+//     32-channel block).  A wavefront owns WN x WM outputs.
+//   * K advances 64 bytes per tile.  Tiles go from HBM to LDS with
+//     buffer_load_dwordx4 ... lds (no registers involved) through a ring of
+//     STAGES LDS stages, so STAGES - 1 tiles of copies are in flight while
+//     the matrix cores work; a tile's copies are awaited with a counted
+//     vmcnt, not a full drain.  Per group, the tile's channel scales of its
+//     group travel the same way (buffer_load_dword ... lds).
+//   * Each 64-deep tile is two 32-deep matrix-core steps.  The fragments of
+//     the next step are read from LDS while the current step's MFMAs run
+//     (two register sets, reads interleaved between MFMAs).  The one
+//     barrier per tile sits between the two steps, where the queued MFMAs
+//     cover it; right after it the stage just consumed is refilled.
+//   * Per group, a group's first MFMA starts from zero and, once its last
+//     K tile is multiplied, its int32 sums are scaled into fp32 accumulators.
+//   * int8 tiles: rows of 64 bytes, 16-byte chunk c of row r at slot
+//     c ^ (((r >> 1) ^ (r >> 2)) & 3), conflict-free for the fragment reads.
+//     Packed int4 tiles: rows of 32 bytes, chunk c at slot c ^ ((r >> 3) & 1);
+//     a lane reads 8 packed bytes and widens them to 16 int8 codes in
+//     registers, so no unpacked copy of the weight tile is ever stored.
+//   * Out-of-range rows read as zeros (buffer descriptors bound the operand);
+//     their outputs are not stored.
 #include "cider_kernels.h"
 
 namespace cider {
@@ -37,34 +39,114 @@ namespace {
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kXcds = 8;
 
+// LDS slot of 16-byte chunk `chunk` of int8 tile row `row` (rows of BK
+// bytes).  Conflict-free for 16-byte reads of 32 consecutive rows at one
+// chunk, whether LDS serves 8 lanes per 128 bytes or 16 lanes per 256 bytes.
 template <int BK>
-__device__ __forceinline__ int lds_offset(int row, int chunk)
+__device__ __forceinline__ int swz8(int row)
 {
-    constexpr int CPR = BK / 16;  // 16-byte chunks per row
-    static_assert(CPR == 4 || CPR == 8, "BK must be 64 or 128");
-    // Conflict-free for 16-byte reads of consecutive rows at one chunk,
-    // whether LDS serves 8 lanes per 128 bytes or 16 lanes per 256 bytes.
-    const int swz = (CPR == 8) ? ((row & 7) ^ ((row >> 3) & 1)) : (((row >> 1) ^ (row >> 2)) & 3);
-    return row * BK + ((chunk ^ swz) << 4);
+    return BK == 64 ? (((row >> 1) ^ (row >> 2)) & 3) : ((row & 7) ^ ((row >> 3) & 1));
+}
+template <int BK>
+__device__ __forceinline__ int off8(int row, int chunk)
+{
+    return row * BK + ((chunk ^ swz8<BK>(row)) << 4);
+}
+// Packed int4 rows of BK/2 bytes.
+template <int BK>
+__device__ __forceinline__ int swz4(int row)
+{
+    return BK == 64 ? ((row >> 3) & 1) : (((row >> 1) ^ (row >> 2)) & 3);
+}
+template <int BK>
+__device__ __forceinline__ int off4(int row, int chunk)
+{
+    return row * (BK / 2) + ((chunk ^ swz4<BK>(row)) << 4);
 }
 
-// Widen 8 packed nibbles (k = 0..7 of a uint32, low nibble = even k) to 8
-// int8 codes q = u - 8 in k order: two dwords.
-__device__ __forceinline__ void unpack_nibbles(uint32_t v, uint32_t &d0, uint32_t &d1)
+// Raw buffer resource (gfx9 layout, stride 0): byte offsets, loads at or
+// past `bytes` return 0.  Kept in scalar registers.
+__device__ __forceinline__ i32x4 make_rsrc(const void *p, uint32_t bytes)
 {
-    const uint32_t lo = v & 0x0F0F0F0Fu;          // u0 u2 u4 u6
-    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;   // u1 u3 u5 u7
-    // interleave to u0 u1 u2 u3 | u4 u5 u6 u7
-    uint32_t a = (lo & 0xFFu) | ((hi & 0xFFu) << 8) | ((lo & 0xFF00u) << 8) | ((hi & 0xFF00u) << 16);
-    uint32_t b = ((lo >> 16) & 0xFFu) | ((hi >> 8) & 0xFF00u) | (lo & 0xFF000000u) >> 8 |
-                 (hi & 0xFF000000u);
-    // u in [0, 15] -> u - 8 as a two's complement byte, without carries
-    // between bytes: (u + 0x78) stays below 0x100; flipping bit 7 then
-    // subtracts 0x80.
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// One wavefront-wide asynchronous copy of 64 x 16 bytes from global memory
+// straight into LDS: lane l's 16 bytes land at LDS address lds + 16 * l.
+// Written as an instruction of its own because the compiler, seeing an LDS
+// write it cannot disambiguate, would otherwise drain every copy in flight
+// before each later LDS read; ordering against readers is enforced here by
+// the counted vmcnt waits and barriers of the pipeline instead.  There is no
+// register result: the data goes to LDS, and the operands are read at issue.
+__device__ __forceinline__ uint32_t lds_address(const void *p)
+{
+    return (uint32_t)(uintptr_t)(lds_void_t *)p;
+}
+
+__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t lds_block, uint32_t voffset)
+{
+    const int lds = __builtin_amdgcn_readfirstlane((int)lds_block);
+    int saved;  // m0 is left exactly as the compiler had it
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %1\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(lds), "v"(voffset), "s"(rsrc)
+                 : "memory");
+}
+
+// The same with 4 bytes per lane: lane l's dword lands at lds + 4 * l.
+__device__ __forceinline__ void dma4(const i32x4 &rsrc, uint32_t lds_block, uint32_t voffset)
+{
+    const int lds = __builtin_amdgcn_readfirstlane((int)lds_block);
+    int saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %1\n\t"
+                 "buffer_load_dword %2, %3, 0 offen lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(lds), "v"(voffset), "s"(rsrc)
+                 : "memory");
+}
+
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
+};
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits 3:0 and
+// 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+__device__ __forceinline__ void wait_lgkm0()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
+// Widen 8 packed nibbles (low nibble = even k) to int8 codes q = u - 8.
+__device__ __forceinline__ void unpack8(uint32_t v, uint32_t &d0, uint32_t &d1)
+{
+    const uint32_t lo = v & 0x0F0F0F0Fu;
+    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
+    const uint32_t a = (lo & 0xFFu) | ((hi & 0xFFu) << 8) | ((lo & 0xFF00u) << 8) | ((hi & 0xFF00u) << 16);
+    const uint32_t b = ((lo >> 16) & 0xFFu) | ((hi >> 8) & 0xFF00u) | ((lo & 0xFF000000u) >> 8) |
+                       (hi & 0xFF000000u);
     d0 = (a + 0x78787878u) ^ 0x80808080u;
     d1 = (b + 0x78787878u) ^ 0x80808080u;
 }
@@ -87,394 +169,425 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_n, int tiles_m, i
     tn = r / gsize;
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
-{
-    // Raw buffer, stride 0: byte offsets, loads at or past `bytes` return 0.
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
-// One wavefront-wide asynchronous copy of 64 x 16 bytes from global memory
-// straight into LDS: lane l's 16 bytes land at lds_block + 16 * l.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void *lds_block,
-                                      uint32_t voffset)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_block, 16, voffset, 0, 0, 0);
-}
-
-__device__ __forceinline__ void wait_vmem_all()
-{
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
-}
-
-template <int TN, int TM, int BK, int WN, int WM, int BITS, int GS, int OUT>
+// GS = 0: one scale per channel.  GS = 64 / 128: per-group scaling.  The
+// operands then swap roles -- tokens are operand A, weights operand B -- so
+// that a lane's outputs all belong to one channel per 32-channel block and
+// need one group scale each; the int32 sum of each group is scaled into an
+// fp32 accumulator as soon as the group's last K tile is multiplied.
+template <int TN, int TM, int WN, int WM, int BK, int BITS, int GS, int OUT, int STAGES>
 __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     ProductArgs args, int tiles_n, int tiles_m, int group_m)
 {
-    constexpr int NWN = TN / WN, NWM = TM / WM, NT = NWN * NWM * 64, NWAVES = NT / 64;
-    constexpr int FN = WN / 32, FM = WM / 32;          // 32 x 32 blocks per wavefront
-    constexpr int KSTEPS = BK / 32;                    // 32-deep matrix-core steps per tile
-    constexpr int GSD = GS ? GS : 1;                   // divisor-safe group size
-    constexpr int GSTEPS = GS ? GS / 32 : KSTEPS;      // k-steps per scaling group
-    constexpr int GPT = GS ? BK / GSD : 1;             // groups per K tile
-    static_assert(GS == 0 || BK % GS == 0, "a K tile holds whole groups");
-    constexpr int CPR = BK / 16;                       // 16-byte chunks per int8 LDS row
-    constexpr int WROWB = BITS == 8 ? BK : BK / 2;     // weight bytes per row per K tile
-    constexpr int XBLK = TM * BK / 1024, WBLK = TN * WROWB / 1024;  // 1 KB copy blocks
-    static_assert(XBLK >= 1 && WBLK >= 1, "tiles of at least 1 KB");
-    constexpr int XPW = (XBLK + NWAVES - 1) / NWAVES, WPW = (WBLK + NWAVES - 1) / NWAVES;
-    constexpr bool SCALED_GROUPS = GS != 0 && OUT == OUT_F16;
-    constexpr int SPT = SCALED_GROUPS ? (GPT * TN + NT - 1) / NT : 1;  // scales per thread
+    constexpr int NWN = TN / WN, NWM = TM / WM, NW = NWN * NWM;
+    constexpr int FN = WN / 32, FM = WM / 32;
+    constexpr int KSTEPS = BK / 32;
+    static_assert(KSTEPS % 2 == 0, "an even number of 32-deep steps per tile");
+    constexpr bool PG = GS != 0;
+    static_assert(!PG || GS == BK || GS == 2 * BK, "a group spans one or two K tiles");
+    constexpr int XROW = BK, WROW = BITS == 8 ? BK : BK / 2;        // bytes per tile row
+    constexpr int XBYTES = TM * XROW, WBYTES = TN * WROW;            // per stage
+    // Per group with the fp16 epilogue: the tile's TN channel scales of the
+    // tile's group, one dword each, copied with the operands (256-byte
+    // blocks), padded to 1 KB.  The int32 hook has no scales (s_w is null):
+    // no scale copies at all.
+    constexpr bool SCOPY = PG && OUT == OUT_F16;
+    constexpr int SB = SCOPY ? TN * 4 / 256 : 0;
+    constexpr int SBYTES = SCOPY ? (TN * 4 + 1023) / 1024 * 1024 : 0;
+    static_assert(!PG || TN % 64 == 0, "whole 256-byte scale blocks");
+    constexpr int STAGE = XBYTES + WBYTES + SBYTES;
+    constexpr int XB = XBYTES / 1024, WB = WBYTES / 1024;            // 1 KB copy blocks
+    constexpr int TB = XB + WB;
+    // Copies per wave per tile.  When the blocks do not split evenly, the
+    // last slots repeat the final block (identical bytes to the same place),
+    // so every wave issues the same number and vmcnt counts stay uniform.
+    constexpr int D = (TB + NW - 1) / NW;
+    constexpr int DS = SCOPY ? (SB + NW - 1) / NW : 0;  // scale copies per wave per tile
+    constexpr int DT = D + DS;
+    static_assert(XBYTES % 1024 == 0 && WBYTES % 1024 == 0, "tiles of whole 1 KB blocks");
+    static_assert(STAGES >= 2 && (STAGES - 1) * DT < 64, "vmcnt range");
 
-    // Two stages per operand as distinct LDS objects, so the copies into
-    // one stage and the fragment reads from the other are never confused.
-    __shared__ __attribute__((aligned(1024))) uint8_t sX0[TM * BK];
-    __shared__ __attribute__((aligned(1024))) uint8_t sX1[TM * BK];
-    __shared__ __attribute__((aligned(1024))) uint8_t sW0[TN * WROWB];
-    __shared__ __attribute__((aligned(1024))) uint8_t sW1[TN * WROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t sU[BITS == 4 ? TN * BK : 16];  // int4 -> int8
-    __shared__ __attribute__((aligned(16))) float sS0[SCALED_GROUPS ? GPT * TN : 4];
-    __shared__ __attribute__((aligned(16))) float sS1[SCALED_GROUPS ? GPT * TN : 4];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+    __shared__ __attribute__((aligned(16))) float s_sw[OUT == OUT_F16 && !PG ? TN : 4];  // s_w tile
+    __shared__ __attribute__((aligned(16))) float s_st[OUT == OUT_F16 ? TM : 4];         // s_tok tile
 
     const int64_t M = args.M, N = args.N, K = args.K;
     int tn, tm;
     tile_coords(blockIdx.x, tiles_n, tiles_m, group_m, tn, tm);
     const int64_t n0 = (int64_t)tn * TN, m0 = (int64_t)tm * TM;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep it scalar
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wn = wave % NWN, wm = wave / NWN;
-    const int G = GS ? (int)(K / GSD) : 1;
     const uint32_t wld = (uint32_t)(BITS == 8 ? K : K / 2);
-
-    const __amdgpu_buffer_rsrc_t rX = make_rsrc(args.xq, (uint32_t)(M * K));
-    const __amdgpu_buffer_rsrc_t rW = make_rsrc(args.wq, (uint32_t)(N * (int64_t)wld));
-
-    // Per-lane source offsets of this wavefront's copy blocks.  LDS row r
-    // slot s must hold global chunk s ^ swz(r) (int8 tiles); packed int4
-    // tiles are copied unswizzled and widened by the unpack pass.
-    uint32_t xoff[XPW], woff[WPW];
-#pragma unroll
-    for (int j = 0; j < XPW; ++j) {
-        const int b = wave + j * NWAVES;
-        const int r = b * (1024 / BK) + lane / CPR, sl = lane % CPR;
-        const int c = sl ^ (lds_offset<BK>(r, 0) - r * BK) / 16;
-        xoff[j] = (uint32_t)((m0 + r) * K) + c * 16;
-    }
-#pragma unroll
-    for (int j = 0; j < WPW; ++j) {
-        const int b = wave + j * NWAVES;
-        if constexpr (BITS == 8) {
-            const int r = b * (1024 / BK) + lane / CPR, sl = lane % CPR;
-            const int c = sl ^ (lds_offset<BK>(r, 0) - r * BK) / 16;
-            woff[j] = (uint32_t)((n0 + r) * (int64_t)wld) + c * 16;
-        } else {
-            constexpr int CPRP = WROWB / 16;
-            const int r = b * (1024 / WROWB) + lane / CPRP, c = lane % CPRP;
-            woff[j] = (uint32_t)((n0 + r) * (int64_t)wld) + c * 16;
-        }
-    }
-
-    auto issue_copies = [&](const uint8_t *dX, const uint8_t *dW, int kt) {
-        const uint32_t kx = (uint32_t)kt * BK, kw = (uint32_t)kt * WROWB;
-#pragma unroll
-        for (int j = 0; j < XPW; ++j)
-            if (XBLK % NWAVES == 0 || wave + j * NWAVES < XBLK)  // wavefront-uniform
-                dma16(rX, dX + (wave + j * NWAVES) * 1024, xoff[j] + kx);
-#pragma unroll
-        for (int j = 0; j < WPW; ++j)
-            if (WBLK % NWAVES == 0 || wave + j * NWAVES < WBLK)
-                dma16(rW, dW + (wave + j * NWAVES) * 1024, woff[j] + kw);
-    };
-
-    float sreg[SPT];
-    auto load_scales = [&](int kt) {
-        if constexpr (SCALED_GROUPS) {
-#pragma unroll
-            for (int i = 0; i < SPT; ++i) {
-                const int id = min(tid + i * NT, GPT * TN - 1);
-                const int gi = id / TN, row = id % TN;
-                const int64_t gr = min(n0 + row, N - 1);
-                sreg[i] = args.s_w[gr * G + (int64_t)kt * GPT + gi];
-            }
-        }
-    };
-    auto store_scales = [&](float *dS) {
-        if constexpr (SCALED_GROUPS) {
-#pragma unroll
-            for (int i = 0; i < SPT; ++i) {
-                const int id = tid + i * NT;
-                if (id < GPT * TN)
-                    dS[id] = sreg[i];  // [gi][row]
-            }
-        }
-    };
-    // int4: widen the packed stage into sU (int8, swizzled like the others).
-    auto unpack = [&](const uint8_t *dW) {
-        if constexpr (BITS == 4) {
-            constexpr int CPRP = WROWB / 16, TOTAL = TN * CPRP;
-#pragma unroll
-            for (int i = 0; i < (TOTAL + NT - 1) / NT; ++i) {
-                const int id = tid + i * NT;
-                if (TOTAL % NT == 0 || id < TOTAL) {
-                    const int row = id / CPRP, c = id % CPRP;
-                    const uint4 v = *reinterpret_cast<const uint4 *>(dW + row * WROWB + c * 16);
-                    uint4 lo, hi;
-                    unpack_nibbles(v.x, lo.x, lo.y);
-                    unpack_nibbles(v.y, lo.z, lo.w);
-                    unpack_nibbles(v.z, hi.x, hi.y);
-                    unpack_nibbles(v.w, hi.z, hi.w);
-                    *reinterpret_cast<uint4 *>(&sU[lds_offset<BK>(row, 2 * c)]) = lo;
-                    *reinterpret_cast<uint4 *>(&sU[lds_offset<BK>(row, 2 * c + 1)]) = hi;
-                }
-            }
-        }
-    };
-
-    i32x16 acc[GS == 0 ? FN : 1][GS == 0 ? FM : 1];
-    f32x16 facc[SCALED_GROUPS ? FN : 1][SCALED_GROUPS ? FM : 1];
-    if constexpr (GS == 0) {
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int j = 0; j < FM; ++j)
-                acc[i][j] = i32x16{};
-    }
-    if constexpr (SCALED_GROUPS) {
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int j = 0; j < FM; ++j)
-                facc[i][j] = f32x16{};
-    }
-
-    // v_mfma_i32_32x32x32_i8 operands: lane l holds row (l % 32) of a 32-row
-    // block and 16 consecutive k of a 32-deep step (half l / 32).  Result:
-    // lane l holds column l % 32 and, for q = 0..3, rows 8q + 4(l/32) + 0..3.
-    const int frow = lane & 31, fhalf = lane >> 5;
-
-    auto compute = [&](const uint8_t *tW, const uint8_t *tX, const float *tS, int kt) {
-        if constexpr (GS == 0) {
-#pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                i32x4 af[FN], bf[FM];
-#pragma unroll
-                for (int i = 0; i < FN; ++i)
-                    af[i] = *reinterpret_cast<const i32x4 *>(
-                        tW + lds_offset<BK>(wn * WN + i * 32 + frow, s * 2 + fhalf));
-#pragma unroll
-                for (int j = 0; j < FM; ++j)
-                    bf[j] = *reinterpret_cast<const i32x4 *>(
-                        tX + lds_offset<BK>(wm * WM + j * 32 + frow, s * 2 + fhalf));
-#pragma unroll
-                for (int i = 0; i < FN; ++i)
-#pragma unroll
-                    for (int j = 0; j < FM; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j],
-                                                                          0, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int gi = 0; gi < GPT; ++gi) {
-                i32x4 af[GSTEPS][FN], bf[GSTEPS][FM];
-#pragma unroll
-                for (int s = 0; s < GSTEPS; ++s) {
-                    const int ks = gi * GSTEPS + s;
-#pragma unroll
-                    for (int i = 0; i < FN; ++i)
-                        af[s][i] = *reinterpret_cast<const i32x4 *>(
-                            tW + lds_offset<BK>(wn * WN + i * 32 + frow, ks * 2 + fhalf));
-#pragma unroll
-                    for (int j = 0; j < FM; ++j)
-                        bf[s][j] = *reinterpret_cast<const i32x4 *>(
-                            tX + lds_offset<BK>(wm * WM + j * 32 + frow, ks * 2 + fhalf));
-                }
-                f32x4 sc[FN][4];
-                if constexpr (SCALED_GROUPS) {
-#pragma unroll
-                    for (int i = 0; i < FN; ++i)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            sc[i][q] = *reinterpret_cast<const f32x4 *>(
-                                &tS[gi * TN + wn * WN + i * 32 + q * 8 + fhalf * 4]);
-                }
-#pragma unroll
-                for (int i = 0; i < FN; ++i)
-#pragma unroll
-                    for (int j = 0; j < FM; ++j) {
-                        i32x16 t = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[0][i], bf[0][j],
-                                                                        i32x16{}, 0, 0, 0);
-#pragma unroll
-                        for (int s = 1; s < GSTEPS; ++s)
-                            t = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s][i], bf[s][j], t, 0, 0, 0);
-                        if constexpr (SCALED_GROUPS) {
-#pragma unroll
-                            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                                for (int r = 0; r < 4; ++r)
-                                    facc[i][j][4 * q + r] += (float)t[4 * q + r] * sc[i][q][r];
-                        } else {
-                            // raw per-group sums: out[(m * N + n) * G + g]
-                            const int64_t m = m0 + wm * WM + j * 32 + frow;
-                            if (m < M) {
-                                int32_t *o = static_cast<int32_t *>(args.out);
-                                const int64_t g = (int64_t)kt * GPT + gi;
-#pragma unroll
-                                for (int q = 0; q < 4; ++q) {
-                                    const int64_t n = n0 + wn * WN + i * 32 + q * 8 + fhalf * 4;
-                                    if (n < N) {
-#pragma unroll
-                                        for (int r = 0; r < 4; ++r)
-                                            o[(m * N + n + r) * G + g] = t[4 * q + r];
-                                    }
-                                }
-                            }
-                        }
-                    }
-            }
-        }
-    };
-
     const int KT = (int)(K / BK);
-    issue_copies(sX0, sW0, 0);
-    load_scales(0);
-    store_scales(sS0);
-    wait_vmem_all();
-    __syncthreads();
-    if constexpr (BITS == 4) {
-        unpack(sW0);
-        __syncthreads();
-    }
-    // One K tile per iteration: start the copies of tile kt+1 into the other
-    // stage, run the matrix cores on this stage, then wait for the copies and
-    // meet at a barrier.
-    for (int kt = 0; kt < KT; ++kt) {
-        const bool odd = kt & 1;
-        const bool more = kt + 1 < KT;
-        if (more) {
-            issue_copies(odd ? sX0 : sX1, odd ? sW0 : sW1, kt + 1);
-            load_scales(kt + 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        compute(BITS == 4 ? sU : (odd ? sW1 : sW0), odd ? sX1 : sX0, odd ? sS1 : sS0, kt);
-        __builtin_amdgcn_sched_barrier(0);
-        if (more)
-            store_scales(odd ? sS0 : sS1);
-        wait_vmem_all();
-        __syncthreads();
-        if constexpr (BITS == 4) {
-            if (more) {
-                unpack(odd ? sW0 : sW1);
-                __syncthreads();
-            }
-        }
-    }
 
-    if constexpr (GS != 0 && OUT == OUT_I32)
-        return;  // per-group sums were stored inside the loop
+    const i32x4 rX = make_rsrc(args.xq, (uint32_t)(M * K));
+    const i32x4 rW = make_rsrc(args.wq, (uint32_t)(N * (int64_t)wld));
+    const int G = PG ? (int)(K / GS) : 1;
 
-    // Epilogue: per block (i, j) the lane holds token m and, for q = 0..3,
-    // output channels nb .. nb+3 with nb = block base + 8q + 4 * (lane / 32).
+    // Source offset of this lane's 16 bytes in each of the wave's copy blocks,
+    // and the block's LDS offset within a stage.  Blocks 0 .. XB-1 hold token
+    // rows, the rest weight rows; LDS slot s of row r receives global chunk
+    // s ^ swizzle(r).
+    constexpr int CX = XROW / 16, CW = WROW / 16;  // 16-byte chunks per row
+    uint32_t coff[D], cstep[D];
+    int cdst[D];
+    i32x4 crs[D];
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-        const int64_t m = m0 + wm * WM + j * 32 + frow;
-        if (m >= M)
-            continue;
-        float st = 0.f;
-        if constexpr (OUT == OUT_F16)
-            st = args.s_tok[m];
+    for (int j = 0; j < D; ++j) {
+        const int b = min(wave * D + j, TB - 1);  // wavefront-uniform
+        crs[j] = b < XB ? rX : rW;
+        cstep[j] = b < XB ? XROW : WROW;
+        if (b < XB) {
+            const int r = b * (1024 / XROW) + lane / CX, c = (lane % CX) ^ swz8<BK>(r);
+            coff[j] = (uint32_t)((m0 + r) * K) + c * 16;
+            cdst[j] = b * 1024;
+        } else {
+            const int bw = b - XB;
+            const int r = bw * (1024 / WROW) + lane / CW;
+            const int c = (lane % CW) ^ (BITS == 8 ? swz8<BK>(r) : swz4<BK>(r));
+            coff[j] = (uint32_t)((n0 + r) * (int64_t)wld) + c * 16;
+            cdst[j] = XBYTES + bw * 1024;
+        }
+    }
+    // Scale copies: block sb holds channels n0 + 64 sb .. +63; lane l reads
+    // s_w[n0 + 64 sb + l, g] (past N: out of range, reads 0).
+    const i32x4 rS = SCOPY ? make_rsrc(args.s_w, (uint32_t)(N * G * 4)) : rX;
+    uint32_t soff[DS > 0 ? DS : 1];
+    int sdst[DS > 0 ? DS : 1];
+#pragma unroll
+    for (int j = 0; j < DS; ++j) {
+        const int sb = min(wave * DS + j, SB - 1);  // wavefront-uniform
+        soff[j] = (uint32_t)((n0 + sb * 64 + lane) * G) * 4u;
+        sdst[j] = XBYTES + WBYTES + sb * 256;
+    }
+    // Copy instruction j (0 <= j < DT) of this wave's share of tile `src`
+    // into LDS stage `stage`: operand blocks, then scale blocks.
+    const uint32_t smem_lds = lds_address(smem);
+    auto copy_one = [&](int j, int stage, int src) {
+        if (j < D) {
+            dma16(crs[j], smem_lds + stage * STAGE + cdst[j], coff[j] + (uint32_t)src * cstep[j]);
+        } else if constexpr (SCOPY) {
+            const uint32_t g = (uint32_t)(src * BK / GS);
+            dma4(rS, smem_lds + stage * STAGE + sdst[j - D], soff[j - D] + g * 4u);
+        }
+    };
+
+    // Fragment register sets: a = weight rows (operand A, int8 codes; for
+    // int4 the packed bytes sit in ap until widened), b = token rows.
+    struct Frags {
+        i32x4 a[FN];
+        uint2 ap[BITS == 4 ? FN : 1];
+        i32x4 b[FM];
+    };
+    const int frow = lane & 31, fhalf = lane >> 5;
+    constexpr int LOADS = FN + FM;
+    // Fragment read k: weight fragments first, then token fragments.
+    auto load_one = [&](Frags &f, int k, int kt, int ks) {
+        const uint8_t *st = smem + (kt % STAGES) * STAGE;
+        if (k < FN) {
+            const int r = wn * WN + k * 32 + frow;
+            if constexpr (BITS == 8)
+                f.a[k] = *reinterpret_cast<const i32x4 *>(st + XBYTES + off8<BK>(r, ks * 2 + fhalf));
+            else
+                f.ap[k] = *reinterpret_cast<const uint2 *>(st + XBYTES + off4<BK>(r, ks) + fhalf * 8);
+        } else {
+            const int j = k - FN;
+            f.b[j] = *reinterpret_cast<const i32x4 *>(st + off8<BK>(wm * WM + j * 32 + frow, ks * 2 + fhalf));
+        }
+    };
+    auto widen = [&](Frags &f, int i) {
+        if constexpr (BITS == 4) {
+            uint32_t d0, d1, d2, d3;
+            unpack8(f.ap[i].x, d0, d1);
+            unpack8(f.ap[i].y, d2, d3);
+            f.a[i] = i32x4{(int)d0, (int)d1, (int)d2, (int)d3};
+        }
+    };
+
+    i32x16 acc[FN][FM];
+    // Per group (fp16 output): facc accumulates each group's int32 sums
+    // times the group's channel scales, in group order.
+    constexpr bool SCALED = PG && OUT == OUT_F16;
+    float facc[SCALED ? FN : 1][SCALED ? FM : 1][SCALED ? 16 : 1];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            acc[i][j] = i32x16{};
+            if constexpr (SCALED)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    facc[i][j][e] = 0.f;
+        }
+
+    // One 32-deep step: `copies` copy instructions first (a short burst; the
+    // other wavefront on the SIMD keeps the matrix core busy meanwhile), then
+    // the FN x FM MFMAs on `cur` with the LOADS fragment reads of the next
+    // step (into `nxt`) spread between them by the scheduler.  `first`: the
+    // step opens a group (per group only), so the MFMAs start from zero.
+    auto step = [&](auto first, Frags &cur, Frags &nxt, int lkt, int lks, int copies, int cstart,
+                    int cstage, int csrc) {
+        constexpr int MF = FN * FM;
+#pragma unroll
+        for (int c = 0; c < 12; ++c)
+            if (c < copies)
+                copy_one(cstart + c, cstage, csrc);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < LOADS; ++k)
+            load_one(nxt, k, lkt, lks);
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
+            widen(cur, i);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t nb = n0 + wn * WN + i * 32 + q * 8 + fhalf * 4;
-                if (nb >= N)
-                    continue;
-                if constexpr (OUT == OUT_I32) {
-                    const i32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                     acc[i][j][4 * q + 3]};
-                    *reinterpret_cast<i32x4 *>(static_cast<int32_t *>(args.out) + m * N + nb) = v;
+            for (int j = 0; j < FM; ++j) {
+                if constexpr (!PG) {
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0);
+                } else if constexpr (decltype(first)::value) {
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.b[j], cur.a[i], i32x16{}, 0, 0, 0);
                 } else {
-                    float y[4];
-                    if constexpr (GS == 0) {
-                        const f32x4 sw = *reinterpret_cast<const f32x4 *>(args.s_w + nb);
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+        constexpr int PER = MF / LOADS > 0 ? MF / LOADS : 1;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            y[r] = (float)acc[i][j][4 * q + r] * st * sw[r];
-                    } else {
+        for (int k = 0; k < LOADS; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // then MFMAs
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // The dequant scales of this tile's channels and tokens, staged in LDS at
+    // the start (plain loads whose latency hides under the prologue copies);
+    // indices are clamped into range, values past the edge are never used.
+    if constexpr (OUT == OUT_F16) {
+        constexpr int TSW = PG ? 0 : TN;  // per group, channel scales come with the tiles
+        for (int t = threadIdx.x; t < TSW + TM; t += NW * 64) {
+            if (t < TSW)
+                s_sw[t] = args.s_w[min(n0 + t, N - 1)];
+            else
+                s_st[t - TSW] = args.s_tok[min(m0 + (t - TSW), M - 1)];
+        }
+    }
+
+    // Ring of STAGES stages.  Tile kt is computed from stage kt % STAGES;
+    // while it runs, tile kt + STAGES - 1 is copied into the stage tile kt-1
+    // used (free since tile kt-1's barrier), half of its copies during each
+    // of the two steps.  Every iteration issues exactly one tile of copies
+    // (past the end they re-read tile KT-1 into the free stage, which nobody
+    // reads), so the vmcnt bound at each barrier is a constant.
+    static_assert(KSTEPS == 2, "two 32-deep steps per tile");
+    static_assert(STAGES >= 3, "the refill targets the stage freed one tile earlier");
+    constexpr int DA = D / 2;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            y[r] = st * facc[i][j][4 * q + r];
+    for (int p = 0; p < STAGES - 1; ++p)
+#pragma unroll
+        for (int j = 0; j < DT; ++j)
+            copy_one(j, p, min(p, KT - 1));
+    wait_vmcnt<(STAGES - 2) * DT>();  // tile 0 has landed
+    __builtin_amdgcn_s_barrier();
+    Frags f0, f1;
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k)
+        load_one(f0, k, 0, 0);
+
+    // Tile kt.  Per group: `first` opens a group, `last` closes it (its int32
+    // sums are then scaled into facc, or stored by the int32 hook).
+    auto tile = [&](int kt, auto first, auto last) {
+        const int rstage = (kt + STAGES - 1) % STAGES;  // == (kt - 1) mod STAGES
+        const int rsrc = min(kt + STAGES - 1, KT - 1);
+        // the closing group's scales, read while tile kt's stage is intact
+        float sw[SCALED ? FN : 1];
+        if constexpr (SCALED && decltype(last)::value) {
+            const float *ss = reinterpret_cast<const float *>(smem + (kt % STAGES) * STAGE + XBYTES + WBYTES);
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+                sw[i] = ss[wn * WN + i * 32 + frow];
+        }
+        // step 0: reads step 1's fragments, first half of the refill
+        step(first, f0, f1, kt, 1, DA, 0, rstage, rsrc);
+        // Tile kt+1 must have landed; tiles kt+2 .. kt+STAGES-2 and the first
+        // half of tile kt+STAGES-1 may still be in flight.  Every wave must
+        // also be done reading tile kt's stage before anyone refills it.
+        wait_lgkm0();
+        wait_vmcnt<(STAGES - 3) * DT + DA>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // step 1: reads tile kt+1's step-0 fragments (at the last tile: a stage
+        // whose contents are never used), second half of the refill
+        step(Flag<false>{}, f1, f0, kt + 1, 0, DT - DA, DA, rstage, rsrc);
+        if constexpr (PG && decltype(last)::value) {
+            if constexpr (SCALED) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            facc[i][j][e] += (float)acc[i][j][e] * sw[i];
+            } else {
+                // int32 hook: acc[m, n, g] for this lane's channel and tokens
+                const int64_t g = (int64_t)kt * BK / GS;
+#pragma unroll
+                for (int i = 0; i < FN; ++i) {
+                    const int64_t n = n0 + wn * WN + i * 32 + frow;
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int64_t m = m0 + wm * WM + j * 32 + (e / 4) * 8 + fhalf * 4 + e % 4;
+                            if (m < M && n < N)
+                                static_cast<int32_t *>(args.out)[(m * N + n) * G + g] = acc[i][j][e];
+                        }
+                }
+                wait_vmcnt<0>();  // keep the copy counts exact: no store left in flight
+            }
+        }
+    };
+    if constexpr (!PG) {
+        for (int kt = 0; kt < KT; ++kt)
+            tile(kt, Flag<false>{}, Flag<false>{});
+    } else if constexpr (GS == BK) {
+        for (int kt = 0; kt < KT; ++kt)
+            tile(kt, Flag<true>{}, Flag<true>{});
+    } else {
+        for (int kt = 0; kt < KT; kt += 2) {
+            tile(kt, Flag<true>{}, Flag<false>{});
+            tile(kt + 1, Flag<false>{}, Flag<true>{});
+        }
+    }
+
+    // Epilogue.  Block (i, j) gives the lane token m = wm*WM + 32j + lane%32
+    // and, for q = 0..3, output channels nb .. nb+3, nb = wn*WN + 32i + 8q +
+    // 4*(lane/32).
+    const bool full = m0 + TM <= M && n0 + TN <= N;  // uniform across the workgroup
+    if constexpr (PG && OUT == OUT_I32) {
+        // stored group by group above
+    } else if constexpr (PG) {
+        // Block (i, j): channel n = wn*WN + 32i + lane%32, tokens
+        // wm*WM + 32j + 8q + 4*(lane/32) + e.  Two-byte stores; each
+        // instruction writes two 64-byte runs of a token row.
+        uint16_t *yout = static_cast<uint16_t *>(args.out);
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int64_t n = n0 + wn * WN + i * 32 + frow;
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int t = wm * WM + j * 32 + (e / 4) * 8 + fhalf * 4 + e % 4;
+                    const int64_t m = m0 + t;
+                    const float y = s_st[t] * facc[i][j][e];
+                    if (full || (m < M && n < N))
+                        yout[m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
+                }
+        }
+    } else if constexpr (OUT == OUT_I32) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int64_t m = m0 + wm * WM + j * 32 + frow;
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t nb = n0 + wn * WN + i * 32 + q * 8 + fhalf * 4;
+                    if (full || (m < M && nb < N)) {
+                        const i32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                         acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                        *reinterpret_cast<i32x4 *>(static_cast<int32_t *>(args.out) + m * N + nb) = v;
                     }
+                }
+        }
+    } else {
+        // fp16 results go through this wave's own LDS region one 32-token
+        // block at a time: rows of 2*WN bytes padded by 16 (so the 32 rows a
+        // write instruction touches fall in distinct bank groups), then leave
+        // as 16-byte stores, consecutive lanes along a token row.
+        constexpr int ROWB = WN * 2 + 16, CPRO = WN * 2 / 16;
+        static_assert(NW * 32 * ROWB <= STAGES * STAGE, "output staging fits the stage ring");
+        __syncthreads();  // every wave is done with the operand stages
+        uint8_t *ob = smem + wave * (32 * ROWB);
+        uint16_t *yout = static_cast<uint16_t *>(args.out);
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const float st = s_st[wm * WM + j * 32 + frow];
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = i * 32 + q * 8 + fhalf * 4;  // channel within the wave tile
+                    const f32x4 sw = *reinterpret_cast<const f32x4 *>(&s_sw[wn * WN + c]);
+                    float y[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        y[e] = (float)acc[i][j][4 * q + e] * st * sw[e];
                     uint2 packed;
                     packed.x = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[0]) |
                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[1]) << 16);
                     packed.y = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[2]) |
                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[3]) << 16);
-                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(args.out) + m * N + nb) =
-                        packed;
+                    *reinterpret_cast<uint2 *>(ob + frow * ROWB + c * 2) = packed;
+                }
+            constexpr int CHUNKS = 32 * CPRO;
+#pragma unroll
+            for (int it = 0; it < (CHUNKS + 63) / 64; ++it) {
+                const int id = it * 64 + lane;
+                if (CHUNKS % 64 == 0 || id < CHUNKS) {
+                    const int r = id / CPRO, c = id % CPRO;
+                    const uint4 v = *reinterpret_cast<const uint4 *>(ob + r * ROWB + c * 16);
+                    const int64_t m = m0 + wm * WM + j * 32 + r;
+                    const int64_t n = n0 + wn * WN + c * 8;
+                    if (full || (m < M && n < N))
+                        *reinterpret_cast<uint4 *>(yout + m * N + n) = v;
                 }
             }
         }
     }
 }
 
-template <int TN, int TM, int BK, int WN, int WM, int BITS, int GS, int OUT>
+template <int TN, int TM, int WN, int WM, int BK, int BITS, int GS, int OUT, int STAGES>
 hipError_t launch_cfg(const ProductArgs &a, hipStream_t stream)
 {
     const int tiles_n = (int)((a.N + TN - 1) / TN);
     const int tiles_m = (int)((a.M + TM - 1) / TM);
-    const int group_m = 8;
     dim3 grid(tiles_n * tiles_m), block((TN / WN) * (TM / WM) * 64);
-    hipLaunchKernelGGL((gemm_kernel<TN, TM, BK, WN, WM, BITS, GS, OUT>), grid, block, 0, stream,
-                       a, tiles_n, tiles_m, group_m);
+    hipLaunchKernelGGL((gemm_kernel<TN, TM, WN, WM, BK, BITS, GS, OUT, STAGES>), grid, block, 0,
+                       stream, a, tiles_n, tiles_m, 8);
     return hipGetLastError();
 }
 
-// Tile shapes: (TN, TM, BK, WN, WM).
-template <int BITS, int GS, int OUT>
-hipError_t launch_mode(const ProductArgs &a, hipStream_t stream)
+template <int BITS, int OUT>
+hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
 {
-    // group_size 128 implies K % 128 == 0, so those always take 128-deep tiles.
-    const bool bk128 = a.K % 128 == 0;
-    if (a.M >= 512) {
-        if constexpr (GS == 0) {
-            if (bk128)
-                return launch_cfg<256, 256, 128, 128, 128, BITS, GS, OUT>(a, stream);
-            return launch_cfg<256, 256, 64, 128, 128, BITS, GS, OUT>(a, stream);
-        } else if constexpr (GS == 128) {
-            return launch_cfg<256, 128, 128, 64, 64, BITS, GS, OUT>(a, stream);
-        } else {
-            if (bk128)
-                return launch_cfg<256, 128, 128, 64, 64, BITS, GS, OUT>(a, stream);
-            return launch_cfg<256, 128, 64, 64, 64, BITS, GS, OUT>(a, stream);
-        }
-    }
-    if constexpr (GS == 128) {
-        return launch_cfg<64, 64, 128, 32, 32, BITS, GS, OUT>(a, stream);
-    } else {
-        if (bk128)
-            return launch_cfg<64, 64, 128, 32, 32, BITS, GS, OUT>(a, stream);
-        return launch_cfg<64, 64, 64, 32, 32, BITS, GS, OUT>(a, stream);
-    }
+    if (a.M >= 512)
+        return launch_cfg<320, 256, 160, 64, 64, BITS, 0, OUT, 4>(a, stream);
+    return launch_cfg<128, 64, 64, 32, 64, BITS, 0, OUT, 4>(a, stream);
+}
+
+// Per group: 8 waves of 32 tokens x 160 channels (320 x 128 tiles: 256 of
+// them at M = 4096, N = 2560), or 4 waves of 32 x 64 for small M.
+template <int GS, int OUT>
+hipError_t launch_group(const ProductArgs &a, hipStream_t stream)
+{
+    if (a.M >= 512)
+        return launch_cfg<320, 128, 160, 32, 64, 8, GS, OUT, 4>(a, stream);
+    return launch_cfg<128, 64, 64, 32, 64, 8, GS, OUT, 4>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const ProductArgs &a, hipStream_t stream)
 {
-    if (a.group_size == 0)
-        return launch_gemm_pc(a, stream);
     const bool f16 = a.out_kind == OUT_F16;
-    if (a.bits == 8) {
-        switch (a.group_size) {
-        case 64: return f16 ? launch_mode<8, 64, OUT_F16>(a, stream) : launch_mode<8, 64, OUT_I32>(a, stream);
-        case 128: return f16 ? launch_mode<8, 128, OUT_F16>(a, stream) : launch_mode<8, 128, OUT_I32>(a, stream);
-        default: return hipErrorInvalidValue;
-        }
-    }
-    return hipErrorInvalidValue;
+    if (a.group_size == 64)
+        return f16 ? launch_group<64, OUT_F16>(a, stream) : launch_group<64, OUT_I32>(a, stream);
+    if (a.group_size == 128)
+        return f16 ? launch_group<128, OUT_F16>(a, stream) : launch_group<128, OUT_I32>(a, stream);
+    if (a.bits == 8)
+        return f16 ? launch_bits<8, OUT_F16>(a, stream) : launch_bits<8, OUT_I32>(a, stream);
+    return f16 ? launch_bits<4, OUT_F16>(a, stream) : launch_bits<4, OUT_I32>(a, stream);
 }
 
 }  // namespace cider
