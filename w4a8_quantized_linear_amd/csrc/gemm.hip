@@ -191,9 +191,8 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     // blocks), padded to 1 KB.  The int32 hook has no scales (s_w is null):
     // no scale copies at all.
     constexpr bool SCOPY = PG && OUT == OUT_F16;
-    constexpr int SB = SCOPY ? TN * 4 / 256 : 0;
-    constexpr int SBYTES = SCOPY ? (TN * 4 + 1023) / 1024 * 1024 : 0;
-    static_assert(!PG || TN % 64 == 0, "whole 256-byte scale blocks");
+    constexpr int SB = SCOPY ? (TN * 4 + 255) / 256 : 0;  // the last block may run past TN
+    constexpr int SBYTES = SCOPY ? (SB * 256 + 1023) / 1024 * 1024 : 0;
     constexpr int STAGE = XBYTES + WBYTES + SBYTES;
     constexpr int XB = XBYTES / 1024, WB = WBYTES / 1024;            // 1 KB copy blocks
     constexpr int TB = XB + WB;
@@ -206,7 +205,12 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     static_assert(XBYTES % 1024 == 0 && WBYTES % 1024 == 0, "tiles of whole 1 KB blocks");
     static_assert(STAGES >= 2 && (STAGES - 1) * DT < 64, "vmcnt range");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+    // The fp16 per-channel epilogue reuses the stage ring to stage its rows
+    // (rows of 2 * WN bytes padded by 16); it may need more than the ring.
+    constexpr int ROWB = WN * 2 + 16;
+    constexpr int OSTAGE = OUT == OUT_F16 && !PG ? NW * 32 * ROWB : 0;
+    constexpr int SMEM = STAGES * STAGE > OSTAGE ? STAGES * STAGE : OSTAGE;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
     __shared__ __attribute__((aligned(16))) float s_sw[OUT == OUT_F16 && !PG ? TN : 4];  // s_w tile
     __shared__ __attribute__((aligned(16))) float s_st[OUT == OUT_F16 ? TM : 4];         // s_tok tile
 
@@ -505,8 +509,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
         // block at a time: rows of 2*WN bytes padded by 16 (so the 32 rows a
         // write instruction touches fall in distinct bank groups), then leave
         // as 16-byte stores, consecutive lanes along a token row.
-        constexpr int ROWB = WN * 2 + 16, CPRO = WN * 2 / 16;
-        static_assert(NW * 32 * ROWB <= STAGES * STAGE, "output staging fits the stage ring");
+        constexpr int CPRO = WN * 2 / 16;
         __syncthreads();  // every wave is done with the operand stages
         uint8_t *ob = smem + wave * (32 * ROWB);
         uint16_t *yout = static_cast<uint16_t *>(args.out);
@@ -558,22 +561,61 @@ hipError_t launch_cfg(const ProductArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Compute units of the current device (workgroups that run at once when
+// each takes a whole compute unit).
+int compute_units()
+{
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+int64_t rounds(int64_t M, int64_t N, int TM, int TN)
+{
+    const int64_t tiles = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
+    const int64_t cu = compute_units();
+    return (tiles + cu - 1) / cu;
+}
+
+// Tile shape by M (measured on MI355X over the N=10240 / N=2560 operator
+// shapes).  Small M: 64-channel x 128-token tiles with an 8-deep ring
+// (latency-bound: more copies in flight).  M <= 768: 160 x 128 with 4
+// waves.  Larger M: 320 x 256 (8 waves of 160 x 64) or 256 x 256 (8 waves
+// of 128 x 64, which finishes a tile in 0.68x the time of a 320 x 256 one
+// on warm operands, about 0.8x on HBM-cold ones),
+// whichever needs fewer whole rounds of workgroups over the compute units.
 template <int BITS, int OUT>
 hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
 {
-    if (a.M >= 512)
+    if (a.M <= 256)
+        return launch_cfg<64, 128, 32, 64, 64, BITS, 0, OUT, 8>(a, stream);
+    if (a.M <= 768)
+        return launch_cfg<160, 128, 160, 32, 64, BITS, 0, OUT, 4>(a, stream);
+    const int64_t r320 = rounds(a.M, a.N, 256, 320), r256 = rounds(a.M, a.N, 256, 256);
+    if (100 * r320 <= 80 * r256)
         return launch_cfg<320, 256, 160, 64, 64, BITS, 0, OUT, 4>(a, stream);
-    return launch_cfg<128, 64, 64, 32, 64, BITS, 0, OUT, 4>(a, stream);
+    return launch_cfg<256, 256, 128, 64, 64, BITS, 0, OUT, 4>(a, stream);
 }
 
-// Per group: 8 waves of 32 tokens x 160 channels (320 x 128 tiles: 256 of
-// them at M = 4096, N = 2560), or 4 waves of 32 x 64 for small M.
+// Per group (operands swapped; a wave owns 32 tokens of WN channels).
 template <int GS, int OUT>
 hipError_t launch_group(const ProductArgs &a, hipStream_t stream)
 {
-    if (a.M >= 512)
-        return launch_cfg<320, 128, 160, 32, 64, 8, GS, OUT, 4>(a, stream);
-    return launch_cfg<128, 64, 64, 32, 64, 8, GS, OUT, 4>(a, stream);
+    if (a.M <= 768)
+        return launch_cfg<64, 128, 64, 32, 64, 8, GS, OUT, 6>(a, stream);
+    if (a.M <= 1536)
+        return launch_cfg<128, 128, 64, 32, 64, 8, GS, OUT, 4>(a, stream);
+    if (a.M <= 3072)
+        return launch_cfg<160, 128, 160, 32, 64, 8, GS, OUT, 4>(a, stream);
+    return launch_cfg<320, 128, 160, 32, 64, 8, GS, OUT, 4>(a, stream);
 }
 
 }  // namespace
