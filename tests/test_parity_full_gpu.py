@@ -53,7 +53,7 @@ def sample_rows(M, seed=0):
 FULL = [("w8a8_pc", 8, 0, 10240, 2560, 128), ("w8a8_pc", 8, 0, 10240, 2560, 1024),
         ("w8a8_pc", 8, 0, 10240, 2560, 4096), ("w8a8_pc", 8, 0, 10240, 2560, 8192),
         ("w8a8_pg64", 8, 64, 2560, 10240, 128), ("w8a8_pg128", 8, 128, 2560, 10240, 1024),
-        ("w4a8_pc", 4, 0, 10240, 2560, 128),
+        ("w4a8_pc", 4, 0, 10240, 2560, 128), ("w4a8_pc", 4, 0, 10240, 2560, 2048),
         ("w8a8_pg64", 8, 64, 2560, 10240, 4096), ("w8a8_pg128", 8, 128, 2560, 10240, 4096),
         ("w4a8_pc", 4, 0, 10240, 2560, 4096), ("w4a8_pc", 4, 0, 10240, 2560, 8192)]
 

@@ -586,23 +586,33 @@ int64_t rounds(int64_t M, int64_t N, int TM, int TN)
 }
 
 // Tile shape by M (measured on MI355X over the N=10240 / N=2560 operator
-// shapes).  Small M: 64-channel x 128-token tiles with an 8-deep ring
-// (latency-bound: more copies in flight).  M <= 768: 160 x 128 with 4
-// waves.  Larger M: 320 x 256 (8 waves of 160 x 64) or 256 x 256 (8 waves
-// of 128 x 64, which finishes a tile in 0.68x the time of a 320 x 256 one
-// on warm operands, about 0.8x on HBM-cold ones),
-// whichever needs fewer whole rounds of workgroups over the compute units.
+// shapes).  Small M: 64-channel x 128-token tiles with a deep copy ring
+// (latency-bound: more copies in flight).  Larger M: a big tile, chosen by
+// how many whole rounds of workgroups over the compute units it needs times
+// its measured time per tile:
+//   int8: 320 x 256 (8 waves of 160 x 64), or 256 x 256 (8 waves of 128 x 64,
+//         about 0.8x the time per tile on HBM-cold operands);
+//   int4: 320 x 256, or 256 x 256 with 4 waves of 128 x 128 (each widened
+//         weight fragment feeds 4 token blocks; 0.61x the time per tile).
 template <int BITS, int OUT>
 hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
 {
     if (a.M <= 256)
         return launch_cfg<64, 128, 32, 64, 64, BITS, 0, OUT, 8>(a, stream);
-    if (a.M <= 768)
-        return launch_cfg<160, 128, 160, 32, 64, BITS, 0, OUT, 4>(a, stream);
     const int64_t r320 = rounds(a.M, a.N, 256, 320), r256 = rounds(a.M, a.N, 256, 256);
-    if (100 * r320 <= 80 * r256)
-        return launch_cfg<320, 256, 160, 64, 64, BITS, 0, OUT, 4>(a, stream);
-    return launch_cfg<256, 256, 128, 64, 64, BITS, 0, OUT, 4>(a, stream);
+    if constexpr (BITS == 8) {
+        if (a.M <= 768)
+            return launch_cfg<160, 128, 160, 32, 64, BITS, 0, OUT, 4>(a, stream);
+        if (100 * r320 <= 80 * r256)
+            return launch_cfg<320, 256, 160, 64, 64, BITS, 0, OUT, 4>(a, stream);
+        return launch_cfg<256, 256, 128, 64, 64, BITS, 0, OUT, 4>(a, stream);
+    } else {
+        if (a.M <= 768)
+            return launch_cfg<64, 128, 32, 64, 64, BITS, 0, OUT, 3>(a, stream);
+        if (100 * r320 <= 61 * r256)
+            return launch_cfg<320, 256, 160, 64, 64, BITS, 0, OUT, 4>(a, stream);
+        return launch_cfg<256, 256, 128, 128, 64, BITS, 0, OUT, 3>(a, stream);
+    }
 }
 
 // Per group (operands swapped; a wave owns 32 tokens of WN channels).
@@ -614,8 +624,8 @@ hipError_t launch_group(const ProductArgs &a, hipStream_t stream)
     if (a.M <= 1536)
         return launch_cfg<128, 128, 64, 32, 64, 8, GS, OUT, 4>(a, stream);
     if (a.M <= 3072)
-        return launch_cfg<160, 128, 160, 32, 64, 8, GS, OUT, 4>(a, stream);
-    return launch_cfg<320, 128, 160, 32, 64, 8, GS, OUT, 4>(a, stream);
+        return launch_cfg<160, 128, 160, 32, 64, 8, GS, OUT, 3>(a, stream);
+    return launch_cfg<320, 128, 160, 32, 64, 8, GS, OUT, 4>(a, stream);  // fewer re-reads of X
 }
 
 }  // namespace
