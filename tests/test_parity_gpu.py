@@ -138,7 +138,8 @@ def test_quantize_weight_bitexact(N, K, bits, gs):
 # ----------------------------------------------------------------- product ---
 
 PRODUCT_SHAPES = [(64, 512, 1024), (300, 320, 1024), (700, 576, 512), (513, 1024, 2560),
-                  (1, 512, 1024), (17, 64, 128), (1100, 704, 1024), (2100, 320, 1024)]
+                  (1, 512, 1024), (17, 64, 128), (1100, 704, 1024), (2100, 320, 1024),
+                  (40, 320, 576), (200, 192, 1344)]
 
 
 def _inputs(M, N, K, bits, gs, seed):

@@ -31,8 +31,10 @@ struct ProductArgs {
     void *out;             // fp16 [M, N] or int32 [M, N] / [M, N, K/gs]
 };
 
-// Matrix-core product (any M >= 1, every mode).
+// Matrix-core product (any M >= 1, every mode); per group with M <= 256
+// goes to the few-token kernel.
 hipError_t launch_gemm(const ProductArgs &a, hipStream_t stream);
+hipError_t launch_gemm_skinny(const ProductArgs &a, hipStream_t stream);
 
 // Matrix-vector product for M <= 8 and M * K <= 32768.
 hipError_t launch_gemv(const ProductArgs &a, hipStream_t stream);

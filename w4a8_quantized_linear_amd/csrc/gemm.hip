@@ -632,6 +632,8 @@ hipError_t launch_group(const ProductArgs &a, hipStream_t stream)
 
 hipError_t launch_gemm(const ProductArgs &a, hipStream_t stream)
 {
+    if (a.M <= 256 && a.group_size != 0)
+        return launch_gemm_skinny(a, stream);
     const bool f16 = a.out_kind == OUT_F16;
     if (a.group_size == 64)
         return f16 ? launch_group<64, OUT_F16>(a, stream) : launch_group<64, OUT_I32>(a, stream);
