@@ -54,6 +54,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-m1", action="store_true")
+    p.add_argument("--no-stack", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
                         "reference for the HBM byte counters)")
@@ -177,6 +178,113 @@ def cpu_baseline(M, N, K, x_np, w_np, budget_s):
                       "int8 product + dequant, %.2f s wall" % (rows, M, N, K, dt)}
 
 
+class DecoderStack:
+    """The layer at model scale: the four W8A8 per-channel linears of each of
+    `layers` decoder layers of an 8B-class model (QKV 6144x4096, O 4096x4096,
+    gate+up 24576x4096, down 4096x12288), chained at M tokens with no glue
+    kernels -- O reads the first 4096 columns of the QKV output and down the
+    first 12288 columns of the gate+up output, in place, through the
+    activation row stride.  Weights are distinct per layer and GEMM, drawn on
+    the host by the seeded generator (in parallel threads), quantized on the
+    device, and only the int8 codes and fp32 scales stay resident (6.95 GB
+    for 36 layers)."""
+
+    def __init__(self, torch, cider, si, layers=None, M=None, keep_fp16=(), threads=16):
+        from concurrent.futures import ThreadPoolExecutor
+        self.torch, self.cider = torch, cider
+        self.layers = si.DECODER_LAYERS if layers is None else layers
+        self.M = si.DECODER_TOKENS if M is None else M
+        self.shapes = [(N, K) for _, N, K in si.DECODER_LAYER]
+        self.weights = [[None] * len(self.shapes) for _ in range(self.layers)]
+        self.fp16 = {}  # (layer, j) -> host fp16 weights kept for a checker
+        tasks = [(l, j) for l in range(self.layers) for j in range(len(self.shapes))]
+
+        def draw(t):
+            l, j = t
+            N, K = self.shapes[j]
+            return t, si.layer_weights(l, j, N, K)
+
+        with ThreadPoolExecutor(threads) as ex:
+            for c in range(0, len(tasks), threads):
+                for (l, j), w in ex.map(draw, tasks[c:c + threads]):
+                    N, K = self.shapes[j]
+                    wd = torch.from_numpy(w.view("int16")).to("cuda").view(torch.float16)
+                    wq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+                    sw = torch.empty((N,), dtype=torch.float32, device="cuda")
+                    cider.cider_quantize_weight(wd, N, K, 8, 0, wq, sw)
+                    self.weights[l][j] = (wq, sw)
+                    if l in keep_fp16:
+                        self.fp16[(l, j)] = w
+                    del wd, w
+        M = self.M
+        kmax = max(K for _, K in self.shapes)
+        self.ws_bytes = cider.cider_linear_workspace_bytes(M, kmax)
+        self.ws = torch.empty((self.ws_bytes,), dtype=torch.uint8, device="cuda")
+        dmodel = self.shapes[0][1]
+        self.x = [torch.empty((M, dmodel), dtype=torch.float16, device="cuda") for _ in range(2)]
+        self.y = [torch.empty((M, N), dtype=torch.float16, device="cuda") for N, _ in self.shapes[:3]]
+
+    def _linear(self, x, ldx, K, l, j, y):
+        wq, sw = self.weights[l][j]
+        self.cider.cider_w8a8_linear(x, self.M, K, ldx, wq, sw, self.shapes[j][0], 0, self.ws,
+                                     self.ws_bytes, y)
+
+    def forward(self, x0, capture=()):
+        """Runs every layer on x0 (fp16 [M, 4096]); returns the final
+        activations and, for each layer in `capture`, host copies of its input
+        and of its four GEMM outputs [input, qkv, o, gate_up, down]."""
+        torch = self.torch
+        (n_qkv, k_in), (n_o, k_o), (n_gu, _), (n_dn, k_dn) = self.shapes
+        cur = x0
+        caps = {}
+        for l in range(self.layers):
+            nxt = self.x[l % 2]
+            y_qkv, y_o, y_gu = self.y
+            self._linear(cur, k_in, k_in, l, 0, y_qkv)
+            self._linear(y_qkv, n_qkv, k_o, l, 1, y_o)       # first 4096 columns of QKV
+            self._linear(y_o, n_o, k_in, l, 2, y_gu)
+            self._linear(y_gu, n_gu, k_dn, l, 3, nxt)        # first 12288 columns of gate+up
+            if l in capture:  # cur (the layer input) is not overwritten by this layer
+                caps[l] = [t.view(torch.int16).cpu().numpy().view("float16")
+                           for t in (cur, y_qkv, y_o, y_gu, nxt)]
+            cur = nxt
+        return cur, caps
+
+    def ops(self):
+        return 2.0 * self.M * sum(N * K for N, K in self.shapes) * self.layers
+
+
+def stack_bench(torch, cider, si, passes=3):
+    """Time whole passes of the 36-layer stack (each GEMM = quantize_act +
+    product, through cider_w8a8_linear)."""
+    t0 = time.perf_counter()
+    S = DecoderStack(torch, cider, si)
+    setup_s = time.perf_counter() - t0
+    x0 = torch.from_numpy(si.activations(S.M, S.shapes[0][1]).view("int16")).cuda().view(torch.float16)
+    out, _ = S.forward(x0)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(passes):
+        out, _ = S.forward(x0)
+    e1.record(stream)
+    e1.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / passes
+    finite = bool(torch.isfinite(out).all().item())
+    rec = {"workload": "8B-class decoder stack: 36 layers x (QKV 6144x4096, O 4096x4096, "
+                       "gate+up 24576x4096, down 4096x12288), W8A8 per channel, M=4096",
+           "ms_per_pass": round(t * 1e3, 3), "tops": round(S.ops() / t / 1e12, 1),
+           "frac_mfma": round(S.ops() / t / 1e12 / PEAK_INT8_TOPS, 4),
+           "passes": passes, "output_finite": finite,
+           "weight_setup_s": round(setup_s, 1)}
+    log("stack: %.3f ms per pass, %.0f TOPS (weights drawn and quantized in %.1f s)"
+        % (t * 1e3, S.ops() / t / 1e12, setup_s))
+    del S, x0, out
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -283,6 +391,10 @@ def main():
     # ------------------------------------------------------------- sweep ---
     if not args.no_sweep:
         result["sweep"] = sweep(torch, cider, si)
+
+    # ------------------------------------------------------------- stack ---
+    if not args.no_stack:
+        result["stack"] = stack_bench(torch, cider, si)
 
     # -------------------------------------------------------- CPU oracle ---
     if not args.no_cpu:

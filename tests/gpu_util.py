@@ -112,3 +112,41 @@ def cosine(a: np.ndarray, b: np.ndarray) -> float:
     a = a.astype(np.float64).ravel()
     b = b.astype(np.float64).ravel()
     return float(a @ b / np.sqrt((a @ a) * (b @ b)))
+
+
+def unpack_int4(wq4: np.ndarray) -> np.ndarray:
+    """Codes q = u - 8 of packed nibbles (low nibble = even k)."""
+    lo = (wq4 & 0x0F).astype(np.int16) - 8
+    hi = (wq4 >> 4).astype(np.int16) - 8
+    return np.stack([lo, hi], axis=-1).reshape(wq4.shape[0], -1).astype(np.int8)
+
+
+def assert_every_output(y_dev, xq: np.ndarray, s_tok: np.ndarray, wcodes: np.ndarray,
+                        s_w: np.ndarray, gs: int, what: str = "", rows_per_chunk: int = 512):
+    """Every output of a full-size product against the exact result of the
+    oracle's codes and scales: the integer sums are formed in float64 by the
+    device's dense product (exact: every partial sum is an integer below
+    2^53), scaled in float64, rounded once to fp16, then compared with the
+    fp16 tolerance.  A property check at sizes the oracle cannot finish; the
+    sampled rows of the same tests are compared with the oracle itself."""
+    import torch
+    M, K = xq.shape
+    N = wcodes.shape[0]
+    y = to_host(y_dev)
+    W = torch.from_numpy(wcodes).cuda().double()
+    sw = torch.from_numpy(np.ascontiguousarray(s_w, dtype=np.float32)).cuda().double()
+    st = torch.from_numpy(s_tok).cuda().double()
+    G = 1 if gs == 0 else K // gs
+    if gs:
+        Wg = W.view(N, G, gs).permute(1, 2, 0).contiguous()          # [G, gs, N]
+    for r0 in range(0, M, rows_per_chunk):
+        r1 = min(M, r0 + rows_per_chunk)
+        X = torch.from_numpy(xq[r0:r1]).cuda().double()
+        if gs == 0:
+            t = (X @ W.t().contiguous()) * sw[None, :]
+        else:
+            acc = torch.bmm(X.view(r1 - r0, G, gs).permute(1, 0, 2).contiguous(), Wg)  # [G, m, N]
+            t = (acc * sw.t().contiguous()[:, None, :]).sum(0)
+        ref = (t * st[r0:r1, None]).cpu().numpy().astype(np.float16)
+        assert_f16_close(y[r0:r1], ref, "%s rows %d..%d" % (what, r0, r1))
+    del W, sw, st

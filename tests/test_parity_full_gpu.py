@@ -8,7 +8,9 @@ The oracle cannot afford every output at these sizes, so:
     rows at tile boundaries, the ragged end and a few seeded random rows,
     bit-exact against the oracle's integer product of those rows;
   * fp16 outputs of the linear call: the same sampled rows, within
-    |d| <= 1e-3 + 2^-10 |ref|;
+    |d| <= 1e-3 + 2^-10 |ref|; and every output against the exact product of
+    the oracle's codes and scales (float64 sums on the device's dense
+    product, rounded once to fp16), with the same tolerance;
   * for every row, a property that holds at any size: the all-zero token
     planted in row 3 gives exactly zero outputs.
 Per-group int32 accumulators are [M, N, K/gs]; they are checked at M = 520
@@ -79,8 +81,12 @@ def test_full_size_sampled(name, bits, gs, N, K, M):
     ref_y = orc.dequant(ref_acc, rs[rows], sw)
 
     # the whole layer, as timed
-    y = gu.to_host(gu.linear_gpu(xd, M, K, K, wqd, swd, N, bits, gs))
+    yd = gu.linear_gpu(xd, M, K, K, wqd, swd, N, bits, gs)
+    y = gu.to_host(yd)
     gu.assert_f16_close(y[rows], ref_y, "%s M=%d sampled rows" % (name, M))
+    # every output against the exact product of the oracle's codes
+    gu.assert_every_output(yd, rq, rs, wq if bits == 8 else gu.unpack_int4(wq), sw, gs,
+                           "%s M=%d" % (name, M))
     assert not np.any(y[3]), "the zero token must give zero outputs"
     assert np.all(np.isfinite(y.astype(np.float32)))
 

@@ -134,6 +134,21 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// Wait until at most n * DT copies are in flight, n (wavefront-uniform)
+// clamped to 0 .. MAXN.
+template <int DT, int MAXN>
+__device__ __forceinline__ void wait_tiles(int n)
+{
+    if constexpr (MAXN <= 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (n >= MAXN)
+            wait_vmcnt<MAXN * DT>();
+        else
+            wait_tiles<DT, MAXN - 1>(n);
+    }
+}
+
 __device__ __forceinline__ void wait_lgkm0()
 {
     __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -379,9 +394,11 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     // Ring of STAGES stages.  Tile kt is computed from stage kt % STAGES;
     // while it runs, tile kt + STAGES - 1 is copied into the stage tile kt-1
     // used (free since tile kt-1's barrier), half of its copies during each
-    // of the two steps.  Every iteration issues exactly one tile of copies
-    // (past the end they re-read tile KT-1 into the free stage, which nobody
-    // reads), so the vmcnt bound at each barrier is a constant.
+    // of the two steps, so the vmcnt bound at each barrier is a constant.
+    // The last STAGES - 1 tiles issue no copies and wait for what is left
+    // of the ring.  (When K has fewer than STAGES - 1 tiles, the prologue
+    // repeats tile KT-1 into stages nobody reads; the waits below then only
+    // count conservatively.)
     static_assert(KSTEPS == 2, "two 32-deep steps per tile");
     static_assert(STAGES >= 3, "the refill targets the stage freed one tile earlier");
     constexpr int DA = D / 2;
@@ -410,18 +427,23 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
             for (int i = 0; i < FN; ++i)
                 sw[i] = ss[wn * WN + i * 32 + frow];
         }
+        const bool refill = kt + STAGES - 1 < KT;  // wavefront-uniform
         // step 0: reads step 1's fragments, first half of the refill
-        step(first, f0, f1, kt, 1, DA, 0, rstage, rsrc);
+        step(first, f0, f1, kt, 1, refill ? DA : 0, 0, rstage, rsrc);
         // Tile kt+1 must have landed; tiles kt+2 .. kt+STAGES-2 and the first
-        // half of tile kt+STAGES-1 may still be in flight.  Every wave must
-        // also be done reading tile kt's stage before anyone refills it.
+        // half of tile kt+STAGES-1 may still be in flight (in the last tiles:
+        // tiles kt+2 .. KT-1).  Every wave must also be done reading tile
+        // kt's stage before anyone refills it.
         wait_lgkm0();
-        wait_vmcnt<(STAGES - 3) * DT + DA>();
+        if (refill)
+            wait_vmcnt<(STAGES - 3) * DT + DA>();
+        else
+            wait_tiles<DT, STAGES - 3>(KT - 2 - kt);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         // step 1: reads tile kt+1's step-0 fragments (at the last tile: a stage
         // whose contents are never used), second half of the refill
-        step(Flag<false>{}, f1, f0, kt + 1, 0, DT - DA, DA, rstage, rsrc);
+        step(Flag<false>{}, f1, f0, kt + 1, 0, refill ? DT - DA : 0, DA, rstage, rsrc);
         if constexpr (PG && decltype(last)::value) {
             if constexpr (SCALED) {
 #pragma unroll
@@ -462,6 +484,11 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
             tile(kt + 1, Flag<false>{}, Flag<true>{});
         }
     }
+
+    // Nothing may still be landing in the ring (the prologue's repeats of a
+    // short K) when the epilogue reuses it or the workgroup's LDS is handed
+    // to the next workgroup.
+    wait_vmcnt<0>();
 
     // Epilogue.  Block (i, j) gives the lane token m = wm*WM + 32j + lane%32
     // and, for q = 0..3, output channels nb .. nb+3, nb = wn*WN + 32i + 8q +
@@ -510,7 +537,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
         // write instruction touches fall in distinct bank groups), then leave
         // as 16-byte stores, consecutive lanes along a token row.
         constexpr int CPRO = WN * 2 / 16;
-        __syncthreads();  // every wave is done with the operand stages
+        __syncthreads();  // every wave is done with the operand stages, and its copies have landed
         uint8_t *ob = smem + wave * (32 * ROWB);
         uint16_t *yout = static_cast<uint16_t *>(args.out);
 #pragma unroll
