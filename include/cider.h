@@ -8,7 +8,9 @@
  *     activations; W4A8 = INT4 weights packed in uint8 x INT8 per-token
  *     activations.
  *   - "W8A8 Quantization Granularity" table: weights per output channel, or
- *     per group of 64 / 128 input elements.
+ *     per group of 64 / 128 input elements.  The pages give W4A8 per column
+ *     only; this library also offers W4A8 per group of 64 / 128, the same
+ *     groups with int4 codes (one int4 scale per group).
  *   - "Quantization" table: symmetric INT8 activations per token, INT32
  *     accumulation, output C_fp16 = C_int32 * s_act * s_weight per element;
  *     W4A8 weights symmetric INT4 with zero-point 8.
@@ -58,7 +60,7 @@
  *
  * Envelope: M >= 0 (M = 0 is a no-op), N >= 0 with N % 64 == 0, K > 0 with
  * K % 64 == 0 and K <= 133144, (M + 256) * K < 2^31 and (N + 256) * K < 2^31
- * for the products, group_size in {0, 64, 128} for W8A8 and 0 for W4A8;
+ * for the products, group_size in {0, 64, 128} for W8A8 and W4A8;
  * device pointers 16-byte aligned; ldx % 8 == 0.
  */
 #ifndef CIDER_H
@@ -93,7 +95,8 @@ const char *cider_status_str(int status);
 /* Weight quantization (Cider README "Low-Level API": quantize_weight_int8,
    pack_weight_int4; "Quantization" table).
    w: fp16 [N, K].  bits 8: wq int8 [N, K]; bits 4: wq uint8 [N, K/2] packed.
-   group_size 0: s_w fp32 [N]; 64 or 128 (bits 8 only): s_w fp32 [N, K/gs]. */
+   group_size 0: s_w fp32 [N]; 64 or 128: s_w fp32 [N, K/gs] (for bits 4 each
+   group's scale is its absmax / 7 and its codes are packed like a row's). */
 cider_status cider_quantize_weight(const void *w_f16, int64_t N, int64_t K, int bits,
                                    int group_size, void *wq, float *s_w, void *stream);
 
@@ -114,7 +117,8 @@ cider_status cider_w8a8_gemm(const int8_t *xq, const float *s_tok, const int8_t 
 
 /* W4A8 product (Cider README "Modes": Unpack -> TensorOps; "Metal Kernel
    Pipeline": INT4 -> INT8 unpacking before the INT8 product).
-   wq4: uint8 [N, K/2] packed nibbles; s_w fp32 [N]; group_size must be 0. */
+   wq4: uint8 [N, K/2] packed nibbles.  group_size 0: s_w fp32 [N];
+   64 / 128: per-group s_w fp32 [N, K/gs] (the per-group output formula). */
 cider_status cider_w4a8_gemm(const int8_t *xq, const float *s_tok, const uint8_t *wq4,
                              const float *s_w, int64_t M, int64_t N, int64_t K,
                              int group_size, void *y_f16, void *stream);

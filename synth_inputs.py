@@ -58,6 +58,7 @@ WORKLOADS = {
     "w8a8_pc": dict(bits=8, N=10240, K=2560, group_sizes=(0,), M=M_SWEEP),
     "w8a8_pg": dict(bits=8, N=2560, K=10240, group_sizes=(64, 128), M=M_SWEEP),
     "w4a8_pc": dict(bits=4, N=10240, K=2560, group_sizes=(0,), M=M_SWEEP),
+    "w4a8_pg": dict(bits=4, N=2560, K=10240, group_sizes=(64, 128), M=M_SWEEP),
 }
 
 # 8B-class decoder layer: (name, N, K, column offset of its input in the

@@ -205,6 +205,35 @@ def pin_weight_int4_roundtrip_and_packing(orc):
     assert np.array_equal(lo, q[:, 0::2]) and np.array_equal(hi, q[:, 1::2])
 
 
+def pin_weight_int4_group_roundtrip(orc):
+    """int4 codes per group of 64 / 128: group g of row n holds q * 2^-(3+e)
+    with max|q| = 7, so its scale is exactly 2^-(3+e) (absmax / 7) and its
+    codes come back; an all-zero group has scale 0 and nibbles 8; a group
+    size of K reproduces the per-channel bytes and scales."""
+    rng = np.random.default_rng(12)
+    N, K = 5, 512
+    for gs in (64, 128):
+        G = K // gs
+        q = rng.integers(-7, 8, size=(N, K))
+        for n in range(N):
+            for g in range(G):
+                q[n, g * gs + rng.integers(0, gs)] = 7 if (n + g) % 2 else -7
+        e = rng.integers(0, 4, size=(N, G))
+        scale = 2.0 ** -(3.0 + e)
+        q[1, gs:2 * gs] = 0
+        w = _f16(q * np.repeat(scale, gs, axis=1))
+        wq, s = orc.quantize_weight(w, bits=4, group_size=gs)
+        expect = scale.astype(np.float32)
+        expect[1, 1] = 0
+        assert s.shape == (N, G) and np.array_equal(s, expect), gs
+        assert np.array_equal(_unpack4(wq), q), gs
+        assert np.all(wq[1, gs // 2:gs] == 0x88), gs
+    w = _f16(rng.standard_normal((N, K)))
+    a, sa = orc.quantize_weight(w, bits=4, group_size=K)
+    b, sb = orc.quantize_weight(w, bits=4)
+    assert np.array_equal(a, b) and np.array_equal(sa.reshape(-1), sb)
+
+
 def pin_zero_rows_and_ranges(orc):
     """All-zero row/group: scale 0, codes 0, output 0.  Codes stay in
     [-127, 127] (int8) and nibbles in [0, 15] with q in [-8, 7] (int4)."""
@@ -339,7 +368,7 @@ def pin_dequant_vs_fake_quant(orc):
     M, N, K = 16, 48, 512
     x = activations(M, K, seed=11)
     w = weights(N, K, seed=11)
-    for bits, gs in ((8, 0), (8, 64), (8, 128), (4, 0), (4, 64)):
+    for bits, gs in ((8, 0), (8, 64), (8, 128), (4, 0), (4, 64), (4, 128)):
         wq, sw = orc.quantize_weight(w, bits, gs)
         y, xq, st = orc.linear(x, wq, sw, bits, gs)
         codes = wq.astype(np.int64) if bits == 8 else _unpack4(wq)
@@ -361,7 +390,7 @@ def pin_symmetry(orc):
     from synth_inputs import activations, weights
     x = activations(8, 256, seed=3)
     w = weights(32, 256, seed=3)
-    for bits, gs in ((8, 0), (8, 64), (4, 0)):
+    for bits, gs in ((8, 0), (8, 64), (4, 0), (4, 64)):
         wq, sw = orc.quantize_weight(w, bits, gs)
         y, xq, st = orc.linear(x, wq, sw, bits, gs)
         yn, xqn, stn = orc.linear(-x, wq, sw, bits, gs)

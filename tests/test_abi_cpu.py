@@ -95,7 +95,10 @@ def test_gemm_argument_codes():
 def test_w4a8_argument_codes():
     f = cider.cider_w4a8_gemm
     assert f(P, P2, P3, P4, 8, 64, 128, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
-    assert f(P, P2, P3, P4, 8, 64, 128, 64, P, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    assert f(P, P2, P3, P4, 8, 64, 128, 64, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert f(P, P2, P3, P4, 8, 64, 128, 128, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert f(P, P2, P3, P4, 8, 64, 128, 32, P, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    assert f(P, P2, P3, P4, 8, 64, 192, 128, P, stream=0, check=False) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
     g = cider.cider_w4a8_gemm_i32
     assert g(P, P3, 8, 64, 128, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
     assert g(P, BAD, 8, 64, 128, 0, P, stream=0, check=False) == cider.CIDER_ERR_MISALIGNED
@@ -117,7 +120,8 @@ def test_quantize_argument_codes():
     qw = cider.cider_quantize_weight
     assert qw(P, 64, 256, 8, 0, P2, P3, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
     assert qw(P, 64, 256, 8, 128, P2, P3, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
-    assert qw(P, 64, 256, 4, 64, P2, P3, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    assert qw(P, 64, 256, 4, 64, P2, P3, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert qw(P, 64, 256, 4, 96, P2, P3, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
     assert qw(P, 64, 256, 6, 0, P2, P3, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
     assert qw(P, 64, 320, 8, 128, P2, P3, stream=0, check=False) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
 

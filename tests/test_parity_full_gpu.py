@@ -57,7 +57,9 @@ FULL = [("w8a8_pc", 8, 0, 10240, 2560, 128), ("w8a8_pc", 8, 0, 10240, 2560, 1024
         ("w8a8_pg64", 8, 64, 2560, 10240, 128), ("w8a8_pg128", 8, 128, 2560, 10240, 1024),
         ("w4a8_pc", 4, 0, 10240, 2560, 128), ("w4a8_pc", 4, 0, 10240, 2560, 2048),
         ("w8a8_pg64", 8, 64, 2560, 10240, 4096), ("w8a8_pg128", 8, 128, 2560, 10240, 4096),
-        ("w4a8_pc", 4, 0, 10240, 2560, 4096), ("w4a8_pc", 4, 0, 10240, 2560, 8192)]
+        ("w4a8_pc", 4, 0, 10240, 2560, 4096), ("w4a8_pc", 4, 0, 10240, 2560, 8192),
+        ("w4a8_pg64", 4, 64, 2560, 10240, 128), ("w4a8_pg128", 4, 128, 2560, 10240, 1024),
+        ("w4a8_pg64", 4, 64, 2560, 10240, 4096), ("w4a8_pg128", 4, 128, 2560, 10240, 8192)]
 
 
 @pytest.mark.parametrize("name,bits,gs,N,K,M", FULL, ids=["%s_M%d" % (c[0], c[5]) for c in FULL])

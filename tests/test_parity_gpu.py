@@ -17,8 +17,8 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-MODES = [(8, 0), (8, 64), (8, 128), (4, 0)]
-MODE_IDS = ["w8a8_pc", "w8a8_pg64", "w8a8_pg128", "w4a8_pc"]
+MODES = [(8, 0), (8, 64), (8, 128), (4, 0), (4, 64), (4, 128)]
+MODE_IDS = ["w8a8_pc", "w8a8_pg64", "w8a8_pg128", "w4a8_pc", "w4a8_pg64", "w4a8_pg128"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -119,7 +119,9 @@ def test_quantize_near_half_quotients():
 
 WEIGHT_CASES = [(512, 1024, 8, 0), (512, 1024, 8, 64), (512, 1024, 8, 128), (512, 1024, 4, 0),
                 (10240, 2560, 8, 0), (2560, 10240, 8, 64), (2560, 10240, 8, 128),
-                (10240, 2560, 4, 0), (64, 20480, 8, 0), (64, 20480, 4, 0)]
+                (10240, 2560, 4, 0), (64, 20480, 8, 0), (64, 20480, 4, 0),
+                (512, 1024, 4, 64), (512, 1024, 4, 128), (2560, 10240, 4, 64),
+                (2560, 10240, 4, 128)]
 
 
 @pytest.mark.parametrize("N,K,bits,gs", WEIGHT_CASES)

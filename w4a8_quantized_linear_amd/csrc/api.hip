@@ -68,8 +68,6 @@ cider_status check_shape(int64_t M, int64_t N, int64_t K, int bits, int group_si
         return CIDER_ERR_INVALID_ARG;
     if (group_size != 0 && group_size != 64 && group_size != 128)
         return CIDER_ERR_INVALID_ARG;
-    if (bits == 4 && group_size != 0)
-        return CIDER_ERR_INVALID_ARG;
     if (K % 64 != 0 || K > kMaxK || N % 64 != 0)
         return CIDER_ERR_UNSUPPORTED_SHAPE;
     if (group_size && K % group_size != 0)
@@ -216,8 +214,6 @@ cider_status cider_quantize_weight(const void *w_f16, int64_t N, int64_t K, int 
     if (N < 0 || K <= 0 || (bits != 8 && bits != 4))
         return CIDER_ERR_INVALID_ARG;
     if (group_size != 0 && group_size != 64 && group_size != 128)
-        return CIDER_ERR_INVALID_ARG;
-    if (bits == 4 && group_size != 0)
         return CIDER_ERR_INVALID_ARG;
     if (K % 64 != 0 || K > kMaxK || (group_size && K % group_size != 0))
         return CIDER_ERR_UNSUPPORTED_SHAPE;

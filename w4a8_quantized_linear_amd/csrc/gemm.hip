@@ -643,16 +643,22 @@ hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
 }
 
 // Per group (operands swapped; a wave owns 32 tokens of WN channels).
-template <int GS, int OUT>
+template <int BITS, int GS, int OUT>
 hipError_t launch_group(const ProductArgs &a, hipStream_t stream)
 {
     if (a.M <= 768)
-        return launch_cfg<64, 128, 64, 32, 64, 8, GS, OUT, 6>(a, stream);
+        return launch_cfg<64, 128, 64, 32, 64, BITS, GS, OUT, 6>(a, stream);
     if (a.M <= 1536)
-        return launch_cfg<128, 128, 64, 32, 64, 8, GS, OUT, 4>(a, stream);
+        return launch_cfg<128, 128, 64, 32, 64, BITS, GS, OUT, 4>(a, stream);
     if (a.M <= 3072)
-        return launch_cfg<160, 128, 160, 32, 64, 8, GS, OUT, 3>(a, stream);
-    return launch_cfg<320, 128, 160, 32, 64, 8, GS, OUT, 4>(a, stream);  // fewer re-reads of X
+        return launch_cfg<160, 128, 160, 32, 64, BITS, GS, OUT, 3>(a, stream);
+    return launch_cfg<320, 128, 160, 32, 64, BITS, GS, OUT, 4>(a, stream);  // fewer re-reads of X
+}
+
+template <int GS, int OUT>
+hipError_t launch_group_bits(const ProductArgs &a, hipStream_t stream)
+{
+    return a.bits == 8 ? launch_group<8, GS, OUT>(a, stream) : launch_group<4, GS, OUT>(a, stream);
 }
 
 }  // namespace
@@ -663,9 +669,9 @@ hipError_t launch_gemm(const ProductArgs &a, hipStream_t stream)
         return launch_gemm_skinny(a, stream);
     const bool f16 = a.out_kind == OUT_F16;
     if (a.group_size == 64)
-        return f16 ? launch_group<64, OUT_F16>(a, stream) : launch_group<64, OUT_I32>(a, stream);
+        return f16 ? launch_group_bits<64, OUT_F16>(a, stream) : launch_group_bits<64, OUT_I32>(a, stream);
     if (a.group_size == 128)
-        return f16 ? launch_group<128, OUT_F16>(a, stream) : launch_group<128, OUT_I32>(a, stream);
+        return f16 ? launch_group_bits<128, OUT_F16>(a, stream) : launch_group_bits<128, OUT_I32>(a, stream);
     if (a.bits == 8)
         return f16 ? launch_bits<8, OUT_F16>(a, stream) : launch_bits<8, OUT_I32>(a, stream);
     return f16 ? launch_bits<4, OUT_F16>(a, stream) : launch_bits<4, OUT_I32>(a, stream);

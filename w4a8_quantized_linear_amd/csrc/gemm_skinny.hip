@@ -329,16 +329,20 @@ hipError_t launch_mode(const ProductArgs &a, hipStream_t stream)
 
 // Per-group products only: per channel, the large-M kernel's 64 x 128 tile
 // with its deep copy ring is faster at these M (measured).
+template <int BITS, int OUT>
+hipError_t launch_group(const ProductArgs &a, hipStream_t stream)
+{
+    switch (a.group_size) {
+    case 64: return launch_mode<BITS, 64, OUT>(a, stream);
+    case 128: return launch_mode<BITS, 128, OUT>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int OUT>
 hipError_t launch_out(const ProductArgs &a, hipStream_t stream)
 {
-    if (a.bits != 8)
-        return hipErrorInvalidValue;
-    switch (a.group_size) {
-    case 64: return launch_mode<8, 64, OUT>(a, stream);
-    case 128: return launch_mode<8, 128, OUT>(a, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return a.bits == 8 ? launch_group<8, OUT>(a, stream) : launch_group<4, OUT>(a, stream);
 }
 
 }  // namespace

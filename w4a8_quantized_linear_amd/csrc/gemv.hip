@@ -20,7 +20,8 @@
 //     (even k) and the high nibbles (odd k) are masked out as unsigned bytes
 //     u = q + 8 and dotted with the token codes stored in LDS as, per block of
 //     32 k, the 16 even-k codes then the 16 odd-k codes; sum(q x) is then
-//     sum(u x) - 8 sum(x), with sum(x) taken once per token;
+//     sum(u x) - 8 sum(x), with sum(x) taken once per token (per group: once
+//     per token and group);
 //   * per-group scaling reduces each group's exact int32 sum over the 4 or 8
 //     lanes that hold it before scaling it; per-channel keeps int32 to the end;
 //   * each unit's sum goes to LDS, and one thread per output adds a row's
@@ -37,6 +38,7 @@ constexpr int kMaxM = 8;
 constexpr int kMaxUnitsPerWave = 5;
 constexpr int kMaxChunksPerLane = 3;  // per unit: SEG <= 192
 constexpr int kEarlyUnits = 2;        // units whose loads go out before the token is quantized
+constexpr int kMaxGroupSums = 1024;   // int4 per group: (token, group) sums of the token codes
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor: raw 32-bit dwords, range-checked
 constexpr uint32_t kDead = 0x80000000u;  // an offset past every buffer: the load returns zero
 
@@ -78,13 +80,14 @@ constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kHalfMirror = 0x141;  // lane i <- lane 7-i within 8
 constexpr int kMirror = 0x140;      // lane i <- lane 15-i within 16
 
-// Sum over aligned groups of L lanes (L = 4, 8 or 16); every lane of a group
-// ends with the group's sum.
+// Sum over aligned groups of L lanes (L = 2, 4, 8 or 16); every lane of a
+// group ends with the group's sum.
 template <int L>
 __device__ __forceinline__ int group_sum(int v)
 {
     v += dpp<kXor1>(v);
-    v += dpp<kXor2>(v);
+    if constexpr (L >= 4)
+        v += dpp<kXor2>(v);
     if constexpr (L >= 8)
         v += dpp<kHalfMirror>(v);
     if constexpr (L >= 16)
@@ -138,12 +141,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
 {
     constexpr int KPC = BITS == 8 ? 16 : 32;  // k values per 16-byte weight chunk
     constexpr int LPG = GS ? GS / KPC : 1;    // lanes holding one group (chunks per group)
-    constexpr bool kXSum = BITS == 4;         // the -8 sum(x) correction
+    constexpr bool kXSum = BITS == 4 && GS == 0;   // the -8 sum(x) correction, per token
+    constexpr bool kGXSum = BITS == 4 && GS != 0;  // the same per token and group
     extern __shared__ __attribute__((aligned(16))) uint8_t sx[];  // [M][K] int8 codes
     __shared__ float part[kMaxM * 64];                            // [m][unit] partials
     __shared__ int ipart[kMaxM * 64];
     __shared__ uint32_t red[kWaves];
     __shared__ int xsum[kMaxM];
+    __shared__ int xg[kGXSum ? kMaxGroupSums : 1];                // [m][g] group sums of x
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -243,6 +248,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
 #pragma unroll
         for (int j = 0; j < XR; ++j) {
             const int64_t c = tid + (int64_t)j * kThreads;
+            int csum = 0;  // sum of this chunk's codes (int4 weights)
             if (c < nch) {
                 const uint2 q = quantize_chunk<8>(xr[j], s, rs);
                 if constexpr (BITS == 8) {
@@ -252,11 +258,18 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
                     uint8_t *blk = sx + (c >> 2) * 32 + (c & 3) * 4;
                     *reinterpret_cast<uint32_t *>(blk) = __builtin_amdgcn_perm(q.y, q.x, kEvenBytes);
                     *reinterpret_cast<uint32_t *>(blk + 16) = __builtin_amdgcn_perm(q.y, q.x, kOddBytes);
-                    tsum = __builtin_amdgcn_sdot4((int)q.x, 0x01010101, tsum, false);
-                    tsum = __builtin_amdgcn_sdot4((int)q.y, 0x01010101, tsum, false);
+                    csum = __builtin_amdgcn_sdot4((int)q.x, 0x01010101, 0, false);
+                    csum = __builtin_amdgcn_sdot4((int)q.y, 0x01010101, csum, false);
                 }
                 if (keep)
                     *reinterpret_cast<uint2 *>(p.xq_out + c * 8) = q;
+            }
+            tsum += csum;
+            if constexpr (kGXSum) {
+                // the GS / 8 chunks of a group sit on consecutive lanes
+                const int gsum = group_sum<GS / 8>(csum);
+                if ((tid & (GS / 8 - 1)) == 0 && c < nch)
+                    xg[(c * 8) / GS] = gsum;
             }
         }
         if constexpr (kXSum) {
@@ -271,6 +284,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
 #pragma unroll
         for (int j = 0; j < XR; ++j) {
             const int64_t c = tid + (int64_t)j * kThreads;
+            int csum = 0;
             if (c < nch) {
                 if constexpr (BITS == 8) {
                     *reinterpret_cast<uint4 *>(sx + c * 16) = xr[j];
@@ -286,8 +300,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
                     t = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, t, false);
                     t = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, t, false);
                     t = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, t, false);
-                    atomicAdd(&xsum[(c * 16) / K], t);
+                    if constexpr (kXSum)
+                        atomicAdd(&xsum[(c * 16) / K], t);
+                    csum = t;
                 }
+            }
+            if constexpr (kGXSum) {
+                // the GS / 16 chunks of a (token, group) sit on consecutive lanes
+                const int gsum = group_sum<GS / 16>(csum);
+                if ((tid & (GS / 16 - 1)) == 0 && c < nch)
+                    xg[(c * 16) / GS] = gsum;
             }
         }
     }
@@ -339,9 +361,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
                     isum += d;
                 } else {
                     // the LPG lanes of one group: exact group sum, then scale
-                    const int gsum = group_sum<LPG>(d);
+                    int gsum = group_sum<LPG>(d);
                     const int64_t g = kc / LPG;
                     if ((lane & (LPG - 1)) == 0 && live && n < N) {
+                        if constexpr (kGXSum)
+                            gsum -= 8 * xg[m * G + g];
                         if constexpr (OUT == OUT_I32)
                             static_cast<int32_t *>(p.out)[(m * N + n) * G + g] = gsum;
                         else
@@ -424,6 +448,8 @@ hipError_t launch_one(GemvParams p, hipStream_t stream)
     plan(p, BITS, GS);
     if (p.R < 1 || p.SEG > 64 * kMaxChunksPerLane)
         return hipErrorInvalidValue;  // K too long for the per-lane register budget
+    if (BITS == 4 && GS != 0 && (FUSED ? 1 : p.M) * p.K / (GS ? GS : 1) > kMaxGroupSums)
+        return hipErrorInvalidValue;
     const int64_t xchunks = FUSED ? p.K / 8 : p.M * p.K / 16;
     const int64_t per_thread = (xchunks + kThreads - 1) / kThreads;
     if (per_thread <= 2)
@@ -446,9 +472,12 @@ hipError_t dispatch(const GemvParams &p, int bits, int group_size, hipStream_t s
         default: return hipErrorInvalidValue;
         }
     }
-    if (group_size == 0)
-        return launch_one<4, 0, OUT, FUSED>(p, stream);
-    return hipErrorInvalidValue;
+    switch (group_size) {
+    case 0: return launch_one<4, 0, OUT, FUSED>(p, stream);
+    case 64: return launch_one<4, 64, OUT, FUSED>(p, stream);
+    case 128: return launch_one<4, 128, OUT, FUSED>(p, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
