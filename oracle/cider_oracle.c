@@ -28,6 +28,9 @@
  *   - int4 nibble u = q + 8 (zero-point 8); byte j of a packed row holds
  *     k = 2j in its low nibble and k = 2j + 1 in its high nibble;
  *   - per-group scales are stored [N, K / group_size], row-major;
+ *   - percentile clipping (weights only): the range replacing the absmax is
+ *     the numpy-default linear-interpolation percentile of |w| over the row
+ *     or group, computed in fp64 and rounded to fp32;
  *   - dequant is evaluated in fp64 and rounded once to fp16 (round to nearest
  *     even, overflow to infinity).  Per-group: y = s_tok * sum_g s_w[n,g]*acc_g.
  *
@@ -41,6 +44,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -109,18 +113,13 @@ float oracle_half_to_float(uint16_t h) { return (float)oracle_half_to_double(h);
 
 /* ------------------------------------------------------- quantization --- */
 
-/* Symmetric absmax quantization of n consecutive fp16 values.
+/* Symmetric quantization of n consecutive fp16 values over the range
+   [-range, range]: s = range / qmax, codes clamped to [lo, hi].
    Writes the integer codes to q[0..n) and returns the fp32 scale. */
-static float quantize_run(const uint16_t *x, int64_t n, float qmax, int lo, int hi,
-                          int *q)
+static float quantize_range(const uint16_t *x, int64_t n, float range, float qmax, int lo,
+                            int hi, int *q)
 {
-    float absmax = 0.0f;
-    for (int64_t i = 0; i < n; ++i) {
-        float a = fabsf(oracle_half_to_float(x[i]));
-        if (a > absmax)
-            absmax = a;
-    }
-    float s = absmax / qmax;                       /* fp32, correctly rounded */
+    float s = range / qmax;                        /* fp32, correctly rounded */
     for (int64_t i = 0; i < n; ++i) {
         if (s == 0.0f) {
             q[i] = 0;
@@ -134,6 +133,46 @@ static float quantize_run(const uint16_t *x, int64_t n, float qmax, int lo, int 
         q[i] = c;
     }
     return s;
+}
+
+/* Symmetric absmax quantization of n consecutive fp16 values. */
+static float quantize_run(const uint16_t *x, int64_t n, float qmax, int lo, int hi,
+                          int *q)
+{
+    float absmax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(oracle_half_to_float(x[i]));
+        if (a > absmax)
+            absmax = a;
+    }
+    return quantize_range(x, n, absmax, qmax, lo, hi, q);
+}
+
+static int cmp_double(const void *a, const void *b)
+{
+    double x = *(const double *)a, y = *(const double *)b;
+    return (x > y) - (x < y);
+}
+
+/* The p-th percentile (0 < p <= 100) of |x| over n fp16 values, by linear
+   interpolation between the two order statistics around the fractional rank
+   h = (n - 1) * (p / 100) -- the default method of numpy.percentile, whose
+   fp64 steps are followed here: a = v[floor(h)], b = the next value (the last
+   one past the end), d = b - a, g = h - floor(h); the result is a + d*g for
+   g < 0.5 and b - d*(1 - g) otherwise.  buf holds n doubles. */
+double oracle_percentile_abs(const uint16_t *x, int64_t n, double p, double *buf)
+{
+    for (int64_t i = 0; i < n; ++i)
+        buf[i] = fabs(oracle_half_to_double(x[i]));
+    qsort(buf, (size_t)n, sizeof(double), cmp_double);
+    double h = (double)(n - 1) * (p / 100.0);
+    double j = floor(h);
+    double g = h - j;
+    int64_t i0 = (int64_t)j;
+    int64_t i1 = i0 + 1 < n ? i0 + 1 : n - 1;
+    double a = buf[i0], b = buf[i1];
+    double d = b - a;
+    return g >= 0.5 ? b - d * (1.0 - g) : a + d * g;
 }
 
 /* Per-token activation quantization: X fp16 [M, K] with row stride ldx.
@@ -157,21 +196,33 @@ int oracle_quantize_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
    bits = 8: wq int8 [N, K];   bits = 4: wq uint8 [N, K/2] packed nibbles.
    group_size = 0: one scale per output channel, s_w fp32 [N];
    group_size = g: one scale per (n, k-group of g), s_w fp32 [N, K/g]. */
-int oracle_quantize_weight(const uint16_t *w, int64_t N, int64_t K, int bits,
-                           int group_size, uint8_t *wq, float *s_w)
+static int quantize_weight(const uint16_t *w, int64_t N, int64_t K, int bits,
+                           int group_size, double clip_percentile, uint8_t *wq, float *s_w)
 {
     if (!w || !wq || !s_w || N < 0 || !shape_ok(K, bits, group_size))
+        return ORACLE_BAD_ARG;
+    if (!(clip_percentile > 0.0 && clip_percentile <= 100.0))
         return ORACLE_BAD_ARG;
     int64_t gs = group_size ? group_size : K;
     int64_t G = K / gs;
     float qmax = bits == 8 ? 127.0f : 7.0f;
     int lo = bits == 8 ? -127 : -8, hi = bits == 8 ? 127 : 7;
+    int clip = clip_percentile < 100.0;
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
         int qbuf[K];
-        for (int64_t g = 0; g < G; ++g)
-            s_w[n * G + g] = quantize_run(w + n * K + g * gs, gs, qmax, lo, hi,
-                                          qbuf + g * gs);
+        double *buf = clip ? (double *)malloc((size_t)gs * sizeof(double)) : NULL;
+        for (int64_t g = 0; g < G; ++g) {
+            const uint16_t *run = w + n * K + g * gs;
+            if (clip) {
+                /* the range is the percentile of |w| over the run, in fp32 */
+                float range = (float)oracle_percentile_abs(run, gs, clip_percentile, buf);
+                s_w[n * G + g] = quantize_range(run, gs, range, qmax, lo, hi, qbuf + g * gs);
+            } else {
+                s_w[n * G + g] = quantize_run(run, gs, qmax, lo, hi, qbuf + g * gs);
+            }
+        }
+        free(buf);
         if (bits == 8) {
             for (int64_t k = 0; k < K; ++k)
                 wq[n * K + k] = (uint8_t)(int8_t)qbuf[k];
@@ -184,6 +235,24 @@ int oracle_quantize_weight(const uint16_t *w, int64_t N, int64_t K, int bits,
         }
     }
     return ORACLE_OK;
+}
+
+int oracle_quantize_weight(const uint16_t *w, int64_t N, int64_t K, int bits,
+                           int group_size, uint8_t *wq, float *s_w)
+{
+    return quantize_weight(w, N, K, bits, group_size, 100.0, wq, s_w);
+}
+
+/* The same with percentile clipping (Cider README, "LLM Quantization:
+   Precision vs. Speed" note: besides plain min-max, a percentile method,
+   clip_percentile=99.9): each row's (or group's) range is the
+   clip_percentile-th percentile of its |w| instead of its absmax, so the
+   largest values saturate at the end codes.  100 is plain absmax. */
+int oracle_quantize_weight_clipped(const uint16_t *w, int64_t N, int64_t K, int bits,
+                                   int group_size, double clip_percentile, uint8_t *wq,
+                                   float *s_w)
+{
+    return quantize_weight(w, N, K, bits, group_size, clip_percentile, wq, s_w);
 }
 
 /* ------------------------------------------------------ accumulation --- */

@@ -63,11 +63,15 @@ class Oracle:
         L.oracle_double_to_half.restype = ctypes.c_uint16
         L.oracle_quantize_act.argtypes = [P, I64, I64, I64, P, P]
         L.oracle_quantize_weight.argtypes = [P, I64, I64, I, I, P, P]
+        L.oracle_quantize_weight_clipped.argtypes = [P, I64, I64, I, I, ctypes.c_double, P, P]
+        L.oracle_percentile_abs.argtypes = [P, I64, ctypes.c_double, P]
+        L.oracle_percentile_abs.restype = ctypes.c_double
         L.oracle_gemm_acc.argtypes = [P, P, I, I64, I64, I64, I, P]
         L.oracle_dequant.argtypes = [P, P, P, I64, I64, I64, P]
         L.oracle_linear.argtypes = [P, I64, I64, I64, P, P, I, I64, I, P, P, P]
         for f in ("oracle_quantize_act", "oracle_quantize_weight", "oracle_gemm_acc",
-                  "oracle_dequant", "oracle_linear", "oracle_num_threads"):
+                  "oracle_dequant", "oracle_linear", "oracle_num_threads",
+                  "oracle_quantize_weight_clipped"):
             getattr(L, f).restype = ctypes.c_int
 
     @staticmethod
@@ -110,6 +114,26 @@ class Oracle:
         self._check(self.lib.oracle_quantize_weight(_ptr(wb), N, K, bits, group_size,
                                                     _ptr(wq), _ptr(s)), "quantize_weight")
         return wq, s
+
+    def quantize_weight_clipped(self, w: np.ndarray, bits: int, group_size: int,
+                                clip_percentile: float):
+        """As quantize_weight, with each row's (group's) range the
+        clip_percentile-th percentile of its |w| instead of its absmax."""
+        wb = _half_bits(w)
+        N, K = wb.shape
+        G = 1 if group_size == 0 else K // group_size
+        wq = np.empty((N, K) if bits == 8 else (N, K // 2), np.int8 if bits == 8 else np.uint8)
+        s = np.empty((N,) if group_size == 0 else (N, G), np.float32)
+        self._check(self.lib.oracle_quantize_weight_clipped(
+            _ptr(wb), N, K, bits, group_size, float(clip_percentile), _ptr(wq), _ptr(s)),
+            "quantize_weight_clipped")
+        return wq, s
+
+    def percentile_abs(self, x: np.ndarray, p: float) -> float:
+        """The p-th percentile of |x| (fp16 values) as the clipping uses it."""
+        xb = _half_bits(np.ascontiguousarray(x).reshape(-1))
+        buf = np.empty(xb.size, np.float64)
+        return float(self.lib.oracle_percentile_abs(_ptr(xb), xb.size, float(p), _ptr(buf)))
 
     def gemm_acc(self, xq: np.ndarray, wq: np.ndarray, bits: int = 8,
                  group_size: int = 0) -> np.ndarray:

@@ -263,6 +263,68 @@ def pin_strided_rows(orc):
     assert np.array_equal(a, b) and np.array_equal(sa, sb)
 
 
+# ------------------------------------------------------------- clipping ---
+
+def pin_percentile_vs_numpy(orc):
+    """The clipping range is numpy.percentile (default linear method) of |w|
+    in float64, to the bit, over rows with ties, zeros and random values, for
+    several percentiles and row lengths."""
+    rng = np.random.default_rng(21)
+    for n in (64, 128, 1000, 2560):
+        half_zero = rng.standard_normal(n)
+        half_zero[: n // 2] = 0
+        rows = [rng.standard_normal(n), np.round(rng.standard_normal(n) * 4) / 4, np.zeros(n),
+                half_zero, 0.02 * rng.standard_normal(n)]
+        for row in rows:
+            h = _f16(row)
+            a = np.abs(h.astype(np.float64))
+            for p in (99.9, 99.0, 99.99, 50.0, 37.3, 0.1, 100.0):
+                assert orc.percentile_abs(h, p) == float(np.percentile(a, p)), (n, p)
+
+
+def pin_clip_100_is_absmax(orc):
+    """clip_percentile = 100 reproduces plain absmax quantization in every
+    weight mode, bit for bit."""
+    w = _f16(np.random.default_rng(22).standard_normal((6, 256)))
+    for bits, gs in ((8, 0), (8, 64), (8, 128), (4, 0), (4, 64), (4, 128)):
+        a, sa = orc.quantize_weight(w, bits, gs)
+        b, sb = orc.quantize_weight_clipped(w, bits, gs, 100.0)
+        assert np.array_equal(a, b) and np.array_equal(sa, sb), (bits, gs)
+
+
+def pin_clip_closed_forms(orc):
+    """Rows whose percentile is known in closed form.  int8: |w| = k/1024,
+    k = 0..1024, shuffled with random signs: the 90th percentile is 0.9, so
+    s = fp32(0.9)/127 and every |w| past 0.9 + s/2 saturates at +-127.
+    int4, groups of 64: |w| = k/64, k = 0..63: the 50th percentile is
+    31.5/64, s = (31.5/64)/7, and the large values saturate at 7 (positive)
+    and -8 (negative)."""
+    rng = np.random.default_rng(23)
+    k = rng.permutation(1025)
+    sign = np.where(rng.integers(0, 2, 1025) == 1, 1.0, -1.0)
+    w = _f16(sign * k / 1024.0)[None, :]
+    wq, s = orc.quantize_weight_clipped(w, 8, 0, 90.0)
+    s_exp = np.float32(np.float32(0.9) / np.float32(127.0))
+    assert s[0] == s_exp
+    big = np.abs(w[0].astype(np.float64)) > 0.9 + float(s_exp) / 2 + 1e-9
+    assert np.array_equal(wq[0][big].astype(np.int64), (127 * sign[big]).astype(np.int64))
+    assert np.all(np.abs(wq[0][~big].astype(np.int64)) <= 127)
+    assert np.all(wq[0][k == 0] == 0)
+    order = np.argsort(np.abs(w[0].astype(np.float64)), kind="stable")
+    assert np.all(np.diff(np.abs(wq[0].astype(np.int64))[order]) >= 0)
+    # int4, one group of 64 per row, two rows
+    kk = np.stack([rng.permutation(64), rng.permutation(64)])
+    sg = np.where(rng.integers(0, 2, (2, 64)) == 1, 1.0, -1.0)
+    w4 = _f16(sg * kk / 64.0)
+    wq4, s4 = orc.quantize_weight_clipped(w4, 4, 64, 50.0)
+    assert np.all(s4 == np.float32(np.float32(31.5 / 64.0) / np.float32(7.0)))
+    q = _unpack4(wq4)
+    ratio = (sg * kk / 64.0) / float(s4[0, 0])
+    assert np.array_equal(q[ratio >= 7.5], np.full(int((ratio >= 7.5).sum()), 7))
+    assert np.array_equal(q[ratio <= -8.5], np.full(int((ratio <= -8.5).sum()), -8))
+    assert (ratio <= -8.5).any() and (ratio >= 7.5).any()
+
+
 # ---------------------------------------------------------- accumulation ---
 
 def _brute_acc(xq, wcodes, gs):

@@ -15,7 +15,7 @@ from oracle.oracle import SOURCE, Oracle, compile_oracle
 from tests import oracle_pins
 
 MUTATIONS = {
-    "scale_divisor_128": ("float s = absmax / qmax;", "float s = absmax / (qmax + 1.0f);"),
+    "scale_divisor_128": ("float s = range / qmax;", "float s = range / (qmax + 1.0f);"),
     "round_half_away": ("float r = nearbyintf(t);", "float r = roundf(t);"),
     "reciprocal_multiply": ("/ s;  /* fp32 quotient */", "* (1.0f / s);"),
     "truncate_not_round": ("float r = nearbyintf(t);", "float r = truncf(t);"),
@@ -28,7 +28,7 @@ MUTATIONS = {
     "int4_divisor_8": ("float qmax = bits == 8 ? 127.0f : 7.0f;", "float qmax = bits == 8 ? 127.0f : 8.0f;"),
     "weight_row_index": ("s += (int64_t)xrow[k] * weight_code(wq, bits, K, n, k);",
                          "s += (int64_t)xrow[k] * weight_code(wq, bits, K, n ? n - 1 : 0, k);"),
-    "group_offset_dropped": ("quantize_run(w + n * K + g * gs, gs,", "quantize_run(w + n * K, gs,"),
+    "group_offset_dropped": ("const uint16_t *run = w + n * K + g * gs;", "const uint16_t *run = w + n * K;"),
     "group_range_off_by_one": ("g * gs, (g + 1) * gs);", "g * gs, (g + 1) * gs - 1);"),
     "group_scale_transposed": ("t += (double)s_w_row[g] * (double)acc_row[g];",
                                "t += (double)s_w_row[0] * (double)acc_row[g];"),
@@ -38,7 +38,13 @@ MUTATIONS = {
     "half_encode_ties_away": ("double m = nearbyint(ldexp(a, -q));", "double m = round(ldexp(a, -q));"),
     "half_encode_quantum": ("? -24 : e - 11;", "? -24 : e - 10;"),
     "half_encode_subnormal_quantum": ("? -24 : e - 11;", "? -23 : e - 11;"),
-    "scale_in_fp16": ("float s = absmax / qmax;", "float s = (float)oracle_half_to_double(oracle_double_to_half(absmax / qmax));"),
+    "scale_in_fp16": ("float s = range / qmax;", "float s = (float)oracle_half_to_double(oracle_double_to_half(range / qmax));"),
+    "percentile_rank_n": ("double h = (double)(n - 1) * (p / 100.0);", "double h = (double)n * (p / 100.0);"),
+    "percentile_lower_value": ("return g >= 0.5 ? b - d * (1.0 - g) : a + d * g;", "return a;"),
+    "percentile_one_formula": ("return g >= 0.5 ? b - d * (1.0 - g) : a + d * g;", "return a + d * g;"),
+    "percentile_signed": ("buf[i] = fabs(oracle_half_to_double(x[i]));", "buf[i] = oracle_half_to_double(x[i]);"),
+    "clip_range_not_rounded": ("float range = (float)oracle_percentile_abs(run, gs, clip_percentile, buf);",
+                               "float range = (float)(oracle_percentile_abs(run, gs, clip_percentile, buf) * (1.0 + 1e-7));"),
     "dequant_via_float": ("return oracle_double_to_half((double)s_tok * t);",
                           "return oracle_double_to_half((double)(float)((float)s_tok * (float)t) * 1.0001);"),
 }
