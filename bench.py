@@ -178,6 +178,41 @@ def cpu_baseline(M, N, K, x_np, w_np, budget_s):
                       "int8 product + dequant, %.2f s wall" % (rows, M, N, K, dt)}
 
 
+def weight_quant_bench(torch, cider, si, reps=20):
+    """Offline weight quantization on the operator shapes: plain absmax and
+    99.9th-percentile clipping, time per call (events around back-to-back
+    calls) and the fp16 weight read rate."""
+    records = []
+    cases = [(10240, 2560, 8, 0), (10240, 2560, 4, 0), (2560, 10240, 8, 64),
+             (2560, 10240, 8, 128), (2560, 10240, 4, 64), (2560, 10240, 4, 128)]
+    stream = torch.cuda.current_stream()
+    for N, K, bits, gs in cases:
+        w = torch.from_numpy(si.weights(N, K).view("int16")).cuda().view(torch.float16)
+        wq = torch.empty((N, K) if bits == 8 else (N, K // 2),
+                         dtype=torch.int8 if bits == 8 else torch.uint8, device="cuda")
+        sw = torch.empty((N,) if gs == 0 else (N, K // gs), dtype=torch.float32, device="cuda")
+        rec = {"N": N, "K": K, "weight_bits": bits, "group_size": gs}
+        for name, call in (("absmax", lambda: cider.cider_quantize_weight(w, N, K, bits, gs, wq, sw)),
+                           ("clip_99.9", lambda: cider.cider_quantize_weight_clipped(
+                               w, N, K, bits, gs, 99.9, wq, sw))):
+            call()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                call()
+            e1.record(stream)
+            e1.synchronize()
+            t = e0.elapsed_time(e1) / 1e3 / reps
+            rec[name + "_us"] = round(t * 1e6, 2)
+            rec[name + "_gbps"] = round(2.0 * N * K / t / 1e9, 1)
+        log("weight quantize %dx%d bits=%d gs=%d: absmax %.1f us, clipped %.1f us"
+            % (N, K, bits, gs, rec["absmax_us"], rec["clip_99.9_us"]))
+        records.append(rec)
+        del w, wq, sw
+    torch.cuda.empty_cache()
+    return records
+
+
 class DecoderStack:
     """The layer at model scale: the four W8A8 per-channel linears of each of
     `layers` decoder layers of an 8B-class model (QKV 6144x4096, O 4096x4096,
@@ -391,6 +426,10 @@ def main():
     # ------------------------------------------------------------- sweep ---
     if not args.no_sweep:
         result["sweep"] = sweep(torch, cider, si)
+
+    # ------------------------------------------- offline weight quantization ---
+    if not args.no_sweep:
+        result["weight_quantize"] = weight_quant_bench(torch, cider, si)
 
     # ------------------------------------------------------------- stack ---
     if not args.no_stack:

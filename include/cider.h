@@ -100,6 +100,20 @@ const char *cider_status_str(int status);
 cider_status cider_quantize_weight(const void *w_f16, int64_t N, int64_t K, int bits,
                                    int group_size, void *wq, float *s_w, void *stream);
 
+/* Weight quantization with percentile clipping (Cider README, "LLM
+   Quantization: Precision vs. Speed" note: a percentile method besides plain
+   min-max, clip_percentile=99.9).  As cider_quantize_weight, except that each
+   row's (group's) range -- the absmax in s = range / 127 or / 7 -- is the
+   clip_percentile-th percentile of its |w|: linear interpolation between the
+   order statistics around the fractional rank (n - 1) * p / 100, numpy's
+   default method, evaluated in fp64 and rounded to fp32.  Values beyond the
+   range saturate at the end codes (+-127; int4: 7 and -8).
+   0 < clip_percentile <= 100 (else CIDER_ERR_INVALID_ARG); 100 gives exactly
+   cider_quantize_weight's result. */
+cider_status cider_quantize_weight_clipped(const void *w_f16, int64_t N, int64_t K, int bits,
+                                           int group_size, double clip_percentile, void *wq,
+                                           float *s_w, void *stream);
+
 /* Per-token activation quantization (Cider README "Metal Kernel Pipeline",
    step quantize_per_token; "Quantization" table, Activations row).
    x: fp16 [M, K] with row stride ldx.  xq: int8 [M, K]; s_tok: fp32 [M]. */

@@ -126,6 +126,18 @@ def test_quantize_argument_codes():
     assert qw(P, 64, 320, 8, 128, P2, P3, stream=0, check=False) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
 
 
+def test_quantize_weight_clipped_argument_codes():
+    qc = cider.cider_quantize_weight_clipped
+    assert qc(P, 64, 256, 8, 0, 99.9, P2, P3, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert qc(P, 64, 256, 4, 128, 100.0, P2, P3, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    for p in (0.0, -1.0, 100.5, float("nan"), float("inf")):
+        assert qc(P, 64, 256, 8, 0, p, P2, P3, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    assert qc(P, 64, 256, 8, 96, 99.9, P2, P3, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    assert qc(P, 64, 320, 8, 128, 99.9, P2, P3, stream=0, check=False) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
+    assert qc(BAD, 64, 256, 8, 0, 99.9, P2, P3, stream=0, check=False) == cider.CIDER_ERR_MISALIGNED
+    assert qc(P, 0, 256, 8, 0, 99.9, None, None, stream=0, check=False) == cider.CIDER_OK
+
+
 def test_linear_argument_codes():
     f = cider.cider_w8a8_linear
     ws = cider.cider_linear_workspace_bytes(16, 256)

@@ -137,6 +137,39 @@ def test_quantize_weight_bitexact(N, K, bits, gs):
     assert np.array_equal(gu.to_host(wq), rq)
 
 
+CLIP_CASES = [(512, 1024, 8, 0), (512, 1024, 8, 64), (512, 1024, 8, 128), (512, 1024, 4, 0),
+              (512, 1024, 4, 64), (512, 1024, 4, 128), (10240, 2560, 8, 0), (2560, 10240, 8, 64),
+              (2560, 10240, 4, 128), (64, 20480, 8, 0), (128, 10240, 4, 0)]
+
+
+@pytest.mark.parametrize("p", [99.9, 99.0, 50.0, 100.0])
+@pytest.mark.parametrize("N,K,bits,gs", CLIP_CASES)
+def test_quantize_weight_clipped_bitexact(N, K, bits, gs, p):
+    """Percentile clipping: codes and scales bit-exact, with rows / groups of
+    zeros, of many ties, of 99.9% zeros (range 0) and a row of equal values."""
+    if N * K > 4 * 2 ** 20 and p not in (99.9,):
+        pytest.skip("full-size shapes at the default percentile only")
+    import torch
+    orc = get_oracle()
+    w = si.weights(N, K, seed=N + K)
+    L = gs if gs else K
+    w[3, :] = 0
+    w[5, :] = np.round(w[5, :].astype(np.float32) * 100) / 100     # many ties
+    w[6, :] = 0
+    w[6, 7] = np.float16(0.5)                                       # one nonzero per row
+    w[7, :L] = np.float16(-0.03)                                    # one value repeated
+    wd = gu.to_dev(w)
+    wq = gu.empty((N, K) if bits == 8 else (N, K // 2), torch.int8 if bits == 8 else torch.uint8)
+    sw = gu.empty((N,) if gs == 0 else (N, K // gs), torch.float32)
+    cider.cider_quantize_weight_clipped(wd, N, K, bits, gs, p, wq, sw)
+    rq, rs = orc.quantize_weight_clipped(w, bits, gs, p)
+    assert np.array_equal(gu.to_host(sw), rs)
+    assert np.array_equal(gu.to_host(wq), rq)
+    if p == 100.0:
+        pq, ps = orc.quantize_weight(w, bits, gs)
+        assert np.array_equal(rq, pq) and np.array_equal(rs, ps)
+
+
 # ----------------------------------------------------------------- product ---
 
 PRODUCT_SHAPES = [(64, 512, 1024), (300, 320, 1024), (700, 576, 512), (513, 1024, 2560),

@@ -32,6 +32,7 @@ EXPORTS = (
     "cider_is_available", "cider_status_str", "cider_quantize_weight", "cider_quantize_act",
     "cider_w8a8_gemm", "cider_w4a8_gemm", "cider_w8a8_gemm_i32", "cider_w4a8_gemm_i32",
     "cider_linear_workspace_bytes", "cider_w8a8_linear", "cider_w4a8_linear", "cider_set_path",
+    "cider_quantize_weight_clipped",
 )
 
 
@@ -62,6 +63,7 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         "cider_status_str": ([I], ctypes.c_char_p),
         "cider_quantize_weight": ([P, I64, I64, I, I, P, P, P], I),
         "cider_quantize_act": ([P, I64, I64, I64, P, P, P], I),
+        "cider_quantize_weight_clipped": ([P, I64, I64, I, I, ctypes.c_double, P, P, P], I),
         "cider_w8a8_gemm": ([P, P, P, P, I64, I64, I64, I, P, P], I),
         "cider_w4a8_gemm": ([P, P, P, P, I64, I64, I64, I, P, P], I),
         "cider_w8a8_gemm_i32": ([P, P, I64, I64, I64, I, P, P], I),
@@ -116,6 +118,14 @@ def cider_quantize_weight(w_f16, N, K, bits, group_size, wq, s_w, stream=None, c
     st = load().cider_quantize_weight(_ptr(w_f16), N, K, bits, group_size, _ptr(wq), _ptr(s_w),
                                       _stream(stream))
     return _ret(st, "cider_quantize_weight", check)
+
+
+def cider_quantize_weight_clipped(w_f16, N, K, bits, group_size, clip_percentile, wq, s_w,
+                                  stream=None, check=True):
+    st = load().cider_quantize_weight_clipped(_ptr(w_f16), N, K, bits, group_size,
+                                              float(clip_percentile), _ptr(wq), _ptr(s_w),
+                                              _stream(stream))
+    return _ret(st, "cider_quantize_weight_clipped", check)
 
 
 def cider_quantize_act(x_f16, M, K, ldx, xq, s_tok, stream=None, check=True):

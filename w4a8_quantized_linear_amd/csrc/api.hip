@@ -6,6 +6,7 @@
 // INT8 GEMM, seq_len == 1 -> INT8 MV kernel), and the launches on the
 // caller's stream.  No allocation, no synchronization.
 #include <atomic>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 
@@ -230,6 +231,38 @@ cider_status cider_quantize_weight(const void *w_f16, int64_t N, int64_t K, int 
     return from_hip(cider::launch_quantize_rows(static_cast<const uint16_t *>(w_f16), rows, len,
                                                 len, bits, wq, s_w,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+cider_status cider_quantize_weight_clipped(const void *w_f16, int64_t N, int64_t K, int bits,
+                                           int group_size, double clip_percentile, void *wq,
+                                           float *s_w, void *stream)
+{
+    if (N < 0 || K <= 0 || (bits != 8 && bits != 4))
+        return CIDER_ERR_INVALID_ARG;
+    if (group_size != 0 && group_size != 64 && group_size != 128)
+        return CIDER_ERR_INVALID_ARG;
+    if (!(clip_percentile > 0.0 && clip_percentile <= 100.0))  // NaN fails too
+        return CIDER_ERR_INVALID_ARG;
+    if (K % 64 != 0 || K > kMaxK || (group_size && K % group_size != 0))
+        return CIDER_ERR_UNSUPPORTED_SHAPE;
+    if (N == 0)
+        return CIDER_OK;
+    if (!w_f16 || !wq || !s_w)
+        return CIDER_ERR_INVALID_ARG;
+    if (!aligned16(w_f16) || !aligned16(wq) || (reinterpret_cast<uintptr_t>(s_w) & 3u))
+        return CIDER_ERR_MISALIGNED;
+    if (!device_usable())
+        return CIDER_ERR_NO_DEVICE;
+    const int64_t len = group_size ? group_size : K;
+    const int64_t rows = N * (K / len);
+    // fractional rank h = (len - 1) * (p / 100) in fp64, as numpy.percentile
+    const double h = (double)(len - 1) * (clip_percentile / 100.0);
+    const double j = std::floor(h);
+    const int64_t r0 = (int64_t)j;
+    const int64_t r1 = r0 + 1 < len ? r0 + 1 : len - 1;
+    return from_hip(cider::launch_clip_quantize_rows(static_cast<const uint16_t *>(w_f16), rows, len,
+                                                     r0, r1, h - j, bits, wq, s_w,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 cider_status cider_quantize_act(const void *x_f16, int64_t M, int64_t K, int64_t ldx,

@@ -16,6 +16,13 @@ namespace cider {
 hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t len, int64_t ld,
                                 int bits, void *out, float *scale, hipStream_t stream);
 
+// The same with each row's range the percentile of its |w| (percentile
+// clipping): ranks r0 <= r1 of the two order statistics and the
+// interpolation weight g, computed by the caller.  len % 8 == 0, len < 2^31.
+hipError_t launch_clip_quantize_rows(const uint16_t *w, int64_t rows, int64_t len, int64_t r0,
+                                     int64_t r1, double g, int bits, void *out, float *scale,
+                                     hipStream_t stream);
+
 // Output of the product kernels.
 enum OutKind { OUT_F16 = 0, OUT_I32 = 1 };
 
