@@ -19,6 +19,10 @@
  *   "LLM Quantization: Precision vs. Speed" note (scales by plain min-max).
  *   Same README, "Metal Kernel Pipeline": FP16 activations -> INT8 + per-token
  *   scales, then INT8 x INT8 -> INT32 -> FP16.
+ *   Same README: automatic dtype handling (float16 / bfloat16) among the
+ *   features; SmoothQuant named as the preprocessing that makes activations
+ *   quantization-friendly (activations divided per input channel by a
+ *   smoothing factor, the weights multiplied by it).
  *
  * Readings taken where the pages are silent:
  *   - scale s = absmax / 127 (int8) or absmax / 7 (int4), computed in fp32;
@@ -31,8 +35,12 @@
  *   - percentile clipping (weights only): the range replacing the absmax is
  *     the numpy-default linear-interpolation percentile of |w| over the row
  *     or group, computed in fp64 and rounded to fp32;
- *   - dequant is evaluated in fp64 and rounded once to fp16 (round to nearest
- *     even, overflow to infinity).  Per-group: y = s_tok * sum_g s_w[n,g]*acc_g.
+ *   - bf16 activations / weights are widened exactly like fp16 ones;
+ *   - smoothing: x' = fp32(x / smooth[k]) before the absmax; the weight fold
+ *     is w' = w * smooth[k] exactly, rounded once to the weight's type;
+ *   - dequant is evaluated in fp64 and rounded once to fp16 or bf16 (round to
+ *     nearest even, overflow to infinity).  Per-group:
+ *     y = s_tok * sum_g s_w[n,g]*acc_g.
  *
  * Quantization decisions are taken in fp32 because the scales are fp32
  * values; everything after the integer accumulation is fp64.
@@ -45,11 +53,15 @@
 #include <stdint.h>
 #include <stddef.h>
 #include <stdlib.h>
+#include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
 
 enum { ORACLE_OK = 0, ORACLE_BAD_ARG = 1, ORACLE_OVERFLOW = 2 };
+
+/* Element types of activations, weights and outputs. */
+enum { DT_F16 = 0, DT_BF16 = 1 };
 
 /* K > 0; bits 8 or 4; group_size 0 (per channel) or a divisor of K; int4
    packs two codes per byte, so K is even. */
@@ -111,12 +123,83 @@ uint16_t oracle_double_to_half(double v)
 
 float oracle_half_to_float(uint16_t h) { return (float)oracle_half_to_double(h); }
 
+/* --------------------------------------------------------------- bf16 --- */
+
+/* Exact widening of a bfloat16 bit pattern: bfloat16 is the upper half of an
+   IEEE binary32, so the pattern shifted into the high 16 bits is the value. */
+double oracle_bf16_to_double(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bfloat16 value, ties to even; overflow -> inf. */
+uint16_t oracle_double_to_bf16(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7fc0);
+    /* Quantum at a: 2^-133 below the smallest normal 2^-126, else 2^(e-8)
+       where a = f * 2^e, f in [0.5, 1) (8 significant bits). */
+    int e = 0;
+    frexp(a, &e);
+    int q = (a < ldexp(1.0, -126)) ? -133 : e - 8;
+    double m = nearbyint(ldexp(a, -q));           /* count of quanta, ties to even */
+    if (q == -133)                                 /* subnormal (m == 128 is 2^-126) */
+        return (uint16_t)(sign | (uint16_t)m);
+    if (m == 256.0) {                              /* rounded up into the next binade */
+        m = 128.0;
+        q += 1;
+    }
+    /* value = m * 2^q with m in [128, 256): biased exponent = q + 134 */
+    if (q + 134 >= 255)
+        return (uint16_t)(sign | 0x7f80);
+    return (uint16_t)(sign | ((q + 134) << 7) | ((int)m - 128));
+}
+
+static float widen(uint16_t h, int dtype)
+{
+    return dtype == DT_BF16 ? (float)oracle_bf16_to_double(h) : oracle_half_to_float(h);
+}
+
+static uint16_t narrow(double v, int dtype)
+{
+    return dtype == DT_BF16 ? oracle_double_to_bf16(v) : oracle_double_to_half(v);
+}
+
+static int dtype_ok(int dtype) { return dtype == DT_F16 || dtype == DT_BF16; }
+
 /* ------------------------------------------------------- quantization --- */
 
-/* Symmetric quantization of n consecutive fp16 values over the range
-   [-range, range]: s = range / qmax, codes clamped to [lo, hi].
+/* n consecutive fp16 / bf16 values as fp32 (exact).  With a smoothing vector
+   (SmoothQuant's per-input-channel factors, one per k), each value is first
+   divided by its channel's factor: an fp32 quotient, before any absmax. */
+static void widen_run(const uint16_t *x, int dtype, int64_t n, const float *smooth, float *v)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float f = widen(x[i], dtype);
+        v[i] = smooth ? f / smooth[i] : f;
+    }
+}
+
+static float absmax_of(const float *v, int64_t n)
+{
+    float absmax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(v[i]);
+        if (a > absmax)
+            absmax = a;
+    }
+    return absmax;
+}
+
+/* Symmetric quantization of n fp32 values over the range [-range, range]:
+   s = range / qmax, codes clamped to [lo, hi].
    Writes the integer codes to q[0..n) and returns the fp32 scale. */
-static float quantize_range(const uint16_t *x, int64_t n, float range, float qmax, int lo,
+static float quantize_range(const float *v, int64_t n, float range, float qmax, int lo,
                             int hi, int *q)
 {
     float s = range / qmax;                        /* fp32, correctly rounded */
@@ -125,7 +208,7 @@ static float quantize_range(const uint16_t *x, int64_t n, float range, float qma
             q[i] = 0;
             continue;
         }
-        float t = oracle_half_to_float(x[i]) / s;  /* fp32 quotient */
+        float t = v[i] / s;  /* fp32 quotient */
         float r = nearbyintf(t);                   /* round half to even */
         int c = (int)r;
         if (c < lo) c = lo;
@@ -135,35 +218,22 @@ static float quantize_range(const uint16_t *x, int64_t n, float range, float qma
     return s;
 }
 
-/* Symmetric absmax quantization of n consecutive fp16 values. */
-static float quantize_run(const uint16_t *x, int64_t n, float qmax, int lo, int hi,
-                          int *q)
-{
-    float absmax = 0.0f;
-    for (int64_t i = 0; i < n; ++i) {
-        float a = fabsf(oracle_half_to_float(x[i]));
-        if (a > absmax)
-            absmax = a;
-    }
-    return quantize_range(x, n, absmax, qmax, lo, hi, q);
-}
-
 static int cmp_double(const void *a, const void *b)
 {
     double x = *(const double *)a, y = *(const double *)b;
     return (x > y) - (x < y);
 }
 
-/* The p-th percentile (0 < p <= 100) of |x| over n fp16 values, by linear
+/* The p-th percentile (0 < p <= 100) of |v| over n values, by linear
    interpolation between the two order statistics around the fractional rank
    h = (n - 1) * (p / 100) -- the default method of numpy.percentile, whose
    fp64 steps are followed here: a = v[floor(h)], b = the next value (the last
    one past the end), d = b - a, g = h - floor(h); the result is a + d*g for
    g < 0.5 and b - d*(1 - g) otherwise.  buf holds n doubles. */
-double oracle_percentile_abs(const uint16_t *x, int64_t n, double p, double *buf)
+static double percentile_abs(const float *v, int64_t n, double p, double *buf)
 {
     for (int64_t i = 0; i < n; ++i)
-        buf[i] = fabs(oracle_half_to_double(x[i]));
+        buf[i] = fabs((double)v[i]);
     qsort(buf, (size_t)n, sizeof(double), cmp_double);
     double h = (double)(n - 1) * (p / 100.0);
     double j = floor(h);
@@ -175,31 +245,56 @@ double oracle_percentile_abs(const uint16_t *x, int64_t n, double p, double *buf
     return g >= 0.5 ? b - d * (1.0 - g) : a + d * g;
 }
 
-/* Per-token activation quantization: X fp16 [M, K] with row stride ldx.
-   xq int8 [M, K] (row stride K), s_tok fp32 [M]. */
-int oracle_quantize_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
-                        int8_t *xq, float *s_tok)
+/* The same over n fp16 values (exposed for the tests). */
+double oracle_percentile_abs(const uint16_t *x, int64_t n, double p, double *buf)
 {
-    if (!x || !xq || !s_tok || M < 0 || K <= 0 || ldx < K)
+    float *v = (float *)malloc((size_t)n * sizeof(float));
+    widen_run(x, DT_F16, n, NULL, v);
+    double r = percentile_abs(v, n, p, buf);
+    free(v);
+    return r;
+}
+
+/* Per-token activation quantization: X [M, K] (fp16 or bf16) with row stride
+   ldx, optionally divided by a smoothing vector smooth [K] first.
+   xq int8 [M, K] (row stride K), s_tok fp32 [M]. */
+int oracle_quantize_act_ex(const uint16_t *x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                           const float *smooth, int8_t *xq, float *s_tok)
+{
+    if (!x || !xq || !s_tok || M < 0 || K <= 0 || ldx < K || !dtype_ok(dtype))
         return ORACLE_BAD_ARG;
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
-        int qbuf[K];
-        s_tok[m] = quantize_run(x + m * ldx, K, 127.0f, -127, 127, qbuf);
+        float *v = (float *)malloc((size_t)K * sizeof(float));
+        int *q = (int *)malloc((size_t)K * sizeof(int));
+        widen_run(x + m * ldx, dtype, K, smooth, v);
+        s_tok[m] = quantize_range(v, K, absmax_of(v, K), 127.0f, -127, 127, q);
         for (int64_t k = 0; k < K; ++k)
-            xq[m * K + k] = (int8_t)qbuf[k];
+            xq[m * K + k] = (int8_t)q[k];
+        free(q);
+        free(v);
     }
     return ORACLE_OK;
 }
 
-/* Weight quantization, W fp16 [N, K] (row stride K).
+int oracle_quantize_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *xq,
+                        float *s_tok)
+{
+    return oracle_quantize_act_ex(x, DT_F16, M, K, ldx, NULL, xq, s_tok);
+}
+
+/* Weight quantization, W [N, K] (fp16 or bf16, row stride K).
    bits = 8: wq int8 [N, K];   bits = 4: wq uint8 [N, K/2] packed nibbles.
    group_size = 0: one scale per output channel, s_w fp32 [N];
-   group_size = g: one scale per (n, k-group of g), s_w fp32 [N, K/g]. */
-static int quantize_weight(const uint16_t *w, int64_t N, int64_t K, int bits,
-                           int group_size, double clip_percentile, uint8_t *wq, float *s_w)
+   group_size = g: one scale per (n, k-group of g), s_w fp32 [N, K/g].
+   clip_percentile < 100 replaces each run's absmax by that percentile of its
+   |w| (Cider README, "LLM Quantization: Precision vs. Speed" note: besides
+   plain min-max, a percentile method, clip_percentile=99.9), so the largest
+   values saturate at the end codes. */
+int oracle_quantize_weight_ex(const uint16_t *w, int dtype, int64_t N, int64_t K, int bits,
+                              int group_size, double clip_percentile, uint8_t *wq, float *s_w)
 {
-    if (!w || !wq || !s_w || N < 0 || !shape_ok(K, bits, group_size))
+    if (!w || !wq || !s_w || N < 0 || !shape_ok(K, bits, group_size) || !dtype_ok(dtype))
         return ORACLE_BAD_ARG;
     if (!(clip_percentile > 0.0 && clip_percentile <= 100.0))
         return ORACLE_BAD_ARG;
@@ -210,19 +305,17 @@ static int quantize_weight(const uint16_t *w, int64_t N, int64_t K, int bits,
     int clip = clip_percentile < 100.0;
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
-        int qbuf[K];
+        int *qbuf = (int *)malloc((size_t)K * sizeof(int));
+        float *v = (float *)malloc((size_t)gs * sizeof(float));
         double *buf = clip ? (double *)malloc((size_t)gs * sizeof(double)) : NULL;
         for (int64_t g = 0; g < G; ++g) {
             const uint16_t *run = w + n * K + g * gs;
-            if (clip) {
-                /* the range is the percentile of |w| over the run, in fp32 */
-                float range = (float)oracle_percentile_abs(run, gs, clip_percentile, buf);
-                s_w[n * G + g] = quantize_range(run, gs, range, qmax, lo, hi, qbuf + g * gs);
-            } else {
-                s_w[n * G + g] = quantize_run(run, gs, qmax, lo, hi, qbuf + g * gs);
-            }
+            widen_run(run, dtype, gs, NULL, v);
+            /* the range: the run's absmax, or the percentile of its |w| in fp32 */
+            float range = clip ? (float)percentile_abs(v, gs, clip_percentile, buf)
+                               : absmax_of(v, gs);
+            s_w[n * G + g] = quantize_range(v, gs, range, qmax, lo, hi, qbuf + g * gs);
         }
-        free(buf);
         if (bits == 8) {
             for (int64_t k = 0; k < K; ++k)
                 wq[n * K + k] = (uint8_t)(int8_t)qbuf[k];
@@ -233,6 +326,9 @@ static int quantize_weight(const uint16_t *w, int64_t N, int64_t K, int bits,
                 wq[n * (K / 2) + j] = (uint8_t)(u_even | (u_odd << 4));
             }
         }
+        free(buf);
+        free(v);
+        free(qbuf);
     }
     return ORACLE_OK;
 }
@@ -240,19 +336,30 @@ static int quantize_weight(const uint16_t *w, int64_t N, int64_t K, int bits,
 int oracle_quantize_weight(const uint16_t *w, int64_t N, int64_t K, int bits,
                            int group_size, uint8_t *wq, float *s_w)
 {
-    return quantize_weight(w, N, K, bits, group_size, 100.0, wq, s_w);
+    return oracle_quantize_weight_ex(w, DT_F16, N, K, bits, group_size, 100.0, wq, s_w);
 }
 
-/* The same with percentile clipping (Cider README, "LLM Quantization:
-   Precision vs. Speed" note: besides plain min-max, a percentile method,
-   clip_percentile=99.9): each row's (or group's) range is the
-   clip_percentile-th percentile of its |w| instead of its absmax, so the
-   largest values saturate at the end codes.  100 is plain absmax. */
 int oracle_quantize_weight_clipped(const uint16_t *w, int64_t N, int64_t K, int bits,
                                    int group_size, double clip_percentile, uint8_t *wq,
                                    float *s_w)
 {
-    return quantize_weight(w, N, K, bits, group_size, clip_percentile, wq, s_w);
+    return oracle_quantize_weight_ex(w, DT_F16, N, K, bits, group_size, clip_percentile, wq,
+                                     s_w);
+}
+
+/* SmoothQuant's weight side, folded offline: W' = W diag(smooth), i.e.
+   w'[n, k] = w[n, k] * smooth[k], the exact product (fp64 holds it: at most
+   11 + 24 significant bits) rounded once, to nearest even, to W's type. */
+int oracle_smooth_fold_weight(const uint16_t *w, int dtype, int64_t N, int64_t K,
+                              const float *smooth, uint16_t *w_out)
+{
+    if (!w || !smooth || !w_out || N < 0 || K <= 0 || !dtype_ok(dtype))
+        return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            w_out[n * K + k] = narrow((double)widen(w[n * K + k], dtype) * (double)smooth[k], dtype);
+    return ORACLE_OK;
 }
 
 /* ------------------------------------------------------ accumulation --- */
@@ -304,52 +411,63 @@ int oracle_gemm_acc(const int8_t *xq, const uint8_t *wq, int bits, int64_t M,
 
 /* ------------------------------------------------------------ dequant --- */
 
-/* fp16( s_tok * sum_g s_w[g] * acc[g] ), evaluated in fp64.  With G = 1 this
-   is acc * s_tok * s_w, the per-channel form of the 'Output dequant' row. */
-static uint16_t dequant_one(float s_tok, const float *s_w_row, const int32_t *acc_row,
-                            int64_t G)
+/* s_tok * sum_g s_w[g] * acc[g], evaluated in fp64.  With G = 1 this is
+   acc * s_tok * s_w, the per-channel form of the 'Output dequant' row. */
+static double dequant_value(float s_tok, const float *s_w_row, const int32_t *acc_row, int64_t G)
 {
     double t = 0.0;
     for (int64_t g = 0; g < G; ++g)
         t += (double)s_w_row[g] * (double)acc_row[g];
-    return oracle_double_to_half((double)s_tok * t);
+    return (double)s_tok * t;
 }
 
-/* y fp16 [M, N] from acc int32 [M, N, G], s_tok [M], s_w [N, G]. */
-int oracle_dequant(const int32_t *acc, const float *s_tok, const float *s_w,
-                   int64_t M, int64_t N, int64_t G, uint16_t *y)
+/* y [M, N] (fp16 or bf16, rounded once to nearest even) from acc int32
+   [M, N, G], s_tok [M], s_w [N, G]. */
+int oracle_dequant_ex(const int32_t *acc, const float *s_tok, const float *s_w, int64_t M,
+                      int64_t N, int64_t G, int y_dtype, uint16_t *y)
 {
-    if (!acc || !s_tok || !s_w || !y || M < 0 || N < 0 || G <= 0)
+    if (!acc || !s_tok || !s_w || !y || M < 0 || N < 0 || G <= 0 || !dtype_ok(y_dtype))
         return ORACLE_BAD_ARG;
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n)
-            y[m * N + n] = dequant_one(s_tok[m], s_w + n * G, acc + (m * N + n) * G, G);
+            y[m * N + n] = narrow(dequant_value(s_tok[m], s_w + n * G, acc + (m * N + n) * G, G),
+                                  y_dtype);
     return ORACLE_OK;
+}
+
+int oracle_dequant(const int32_t *acc, const float *s_tok, const float *s_w,
+                   int64_t M, int64_t N, int64_t G, uint16_t *y)
+{
+    return oracle_dequant_ex(acc, s_tok, s_w, M, N, G, DT_F16, y);
 }
 
 /* --------------------------------------------------------- whole path --- */
 
-/* X fp16 [M, K] (row stride ldx) through quantize_act, the integer product
-   with an already-quantized weight and the dequant, one row at a time.
-   xq / s_tok receive the quantized activations; y fp16 [M, N]. */
-int oracle_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
-                  const uint8_t *wq, const float *s_w, int bits, int64_t N,
-                  int group_size, int8_t *xq, float *s_tok, uint16_t *y)
+/* X [M, K] (fp16 or bf16, row stride ldx, optionally smoothed) through
+   quantize_act, the integer product with an already-quantized weight and the
+   dequant, one row at a time.  xq / s_tok receive the quantized activations;
+   y [M, N] in y_dtype. */
+int oracle_linear_ex(const uint16_t *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                     const float *smooth, const uint8_t *wq, const float *s_w, int bits,
+                     int64_t N, int group_size, int y_dtype, int8_t *xq, float *s_tok,
+                     uint16_t *y)
 {
     if (!x || !wq || !s_w || !xq || !s_tok || !y || M < 0 || N < 0 || ldx < K ||
-        !shape_ok(K, bits, group_size))
+        !shape_ok(K, bits, group_size) || !dtype_ok(x_dtype) || !dtype_ok(y_dtype))
         return ORACLE_BAD_ARG;
     int64_t gs = group_size ? group_size : K;
     int64_t G = K / gs;
     int overflow = 0;
 #pragma omp parallel for schedule(static) reduction(| : overflow)
     for (int64_t m = 0; m < M; ++m) {
-        int qbuf[K];
-        int32_t accs[G];
-        s_tok[m] = quantize_run(x + m * ldx, K, 127.0f, -127, 127, qbuf);
+        float *v = (float *)malloc((size_t)K * sizeof(float));
+        int *q = (int *)malloc((size_t)K * sizeof(int));
+        int32_t *accs = (int32_t *)malloc((size_t)G * sizeof(int32_t));
+        widen_run(x + m * ldx, x_dtype, K, smooth, v);
+        s_tok[m] = quantize_range(v, K, absmax_of(v, K), 127.0f, -127, 127, q);
         for (int64_t k = 0; k < K; ++k)
-            xq[m * K + k] = (int8_t)qbuf[k];
+            xq[m * K + k] = (int8_t)q[k];
         for (int64_t n = 0; n < N; ++n) {
             for (int64_t g = 0; g < G; ++g) {
                 int64_t s = dot_range(xq + m * K, wq, bits, K, n, g * gs, (g + 1) * gs);
@@ -357,10 +475,21 @@ int oracle_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                     overflow = 1;
                 accs[g] = (int32_t)s;
             }
-            y[m * N + n] = dequant_one(s_tok[m], s_w + n * G, accs, G);
+            y[m * N + n] = narrow(dequant_value(s_tok[m], s_w + n * G, accs, G), y_dtype);
         }
+        free(accs);
+        free(q);
+        free(v);
     }
     return overflow ? ORACLE_OVERFLOW : ORACLE_OK;
+}
+
+int oracle_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                  const uint8_t *wq, const float *s_w, int bits, int64_t N,
+                  int group_size, int8_t *xq, float *s_tok, uint16_t *y)
+{
+    return oracle_linear_ex(x, DT_F16, M, K, ldx, NULL, wq, s_w, bits, N, group_size, DT_F16, xq,
+                            s_tok, y);
 }
 
 /* Threads the OpenMP loops above use. */

@@ -40,6 +40,8 @@ def _ptr(a: np.ndarray):
 
 
 def _half_bits(x: np.ndarray) -> np.ndarray:
+    """uint16 bit patterns of fp16 values (or of bf16 values already given as
+    uint16 patterns)."""
     if x.dtype == np.float16:
         x = x.view(np.uint16)
     assert x.dtype == np.uint16, x.dtype
@@ -66,12 +68,24 @@ class Oracle:
         L.oracle_quantize_weight_clipped.argtypes = [P, I64, I64, I, I, ctypes.c_double, P, P]
         L.oracle_percentile_abs.argtypes = [P, I64, ctypes.c_double, P]
         L.oracle_percentile_abs.restype = ctypes.c_double
+        D = ctypes.c_double
+        L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_double.restype = D
+        L.oracle_double_to_bf16.argtypes = [D]
+        L.oracle_double_to_bf16.restype = ctypes.c_uint16
+        L.oracle_quantize_act_ex.argtypes = [P, I, I64, I64, I64, P, P, P]
+        L.oracle_quantize_weight_ex.argtypes = [P, I, I64, I64, I, I, D, P, P]
+        L.oracle_smooth_fold_weight.argtypes = [P, I, I64, I64, P, P]
+        L.oracle_dequant_ex.argtypes = [P, P, P, I64, I64, I64, I, P]
+        L.oracle_linear_ex.argtypes = [P, I, I64, I64, I64, P, P, P, I, I64, I, I, P, P, P]
         L.oracle_gemm_acc.argtypes = [P, P, I, I64, I64, I64, I, P]
         L.oracle_dequant.argtypes = [P, P, P, I64, I64, I64, P]
         L.oracle_linear.argtypes = [P, I64, I64, I64, P, P, I, I64, I, P, P, P]
         for f in ("oracle_quantize_act", "oracle_quantize_weight", "oracle_gemm_acc",
                   "oracle_dequant", "oracle_linear", "oracle_num_threads",
-                  "oracle_quantize_weight_clipped"):
+                  "oracle_quantize_weight_clipped", "oracle_quantize_act_ex",
+                  "oracle_quantize_weight_ex", "oracle_smooth_fold_weight", "oracle_dequant_ex",
+                  "oracle_linear_ex"):
             getattr(L, f).restype = ctypes.c_int
 
     @staticmethod
@@ -87,6 +101,85 @@ class Oracle:
 
     def double_to_half(self, v: float) -> int:
         return self.lib.oracle_double_to_half(float(v))
+
+    def bf16_to_double(self, h: int) -> float:
+        return self.lib.oracle_bf16_to_double(int(h))
+
+    def double_to_bf16(self, v: float) -> int:
+        return self.lib.oracle_double_to_bf16(float(v))
+
+    @staticmethod
+    def _smooth(smooth):
+        if smooth is None:
+            return None, None
+        a = np.ascontiguousarray(smooth, dtype=np.float32)
+        return a, _ptr(a)
+
+    def quantize_act_ex(self, xbits: np.ndarray, dtype: int, K: int | None = None, smooth=None):
+        """xbits: uint16 patterns [M, ldx] of fp16 (dtype 0) or bf16 (dtype 1)
+        values; smooth: optional fp32 [K] divisors.  Returns (xq, s_tok)."""
+        xb = _half_bits(xbits)
+        M, ldx = xb.shape
+        K = ldx if K is None else K
+        sm, sp = self._smooth(smooth)
+        xq = np.empty((M, K), np.int8)
+        s = np.empty((M,), np.float32)
+        self._check(self.lib.oracle_quantize_act_ex(_ptr(xb), dtype, M, K, ldx, sp, _ptr(xq),
+                                                    _ptr(s)), "quantize_act_ex")
+        return xq, s
+
+    def quantize_weight_ex(self, wbits: np.ndarray, dtype: int, bits: int = 8,
+                           group_size: int = 0, clip_percentile: float = 100.0):
+        wb = _half_bits(wbits)
+        N, K = wb.shape
+        G = 1 if group_size == 0 else K // group_size
+        wq = np.empty((N, K) if bits == 8 else (N, K // 2), np.int8 if bits == 8 else np.uint8)
+        s = np.empty((N,) if group_size == 0 else (N, G), np.float32)
+        self._check(self.lib.oracle_quantize_weight_ex(_ptr(wb), dtype, N, K, bits, group_size,
+                                                       float(clip_percentile), _ptr(wq), _ptr(s)),
+                    "quantize_weight_ex")
+        return wq, s
+
+    def smooth_fold_weight(self, wbits: np.ndarray, dtype: int, smooth) -> np.ndarray:
+        """w * smooth[k], rounded once to the weight's type; uint16 patterns."""
+        wb = _half_bits(wbits)
+        N, K = wb.shape
+        sm, sp = self._smooth(smooth)
+        out = np.empty((N, K), np.uint16)
+        self._check(self.lib.oracle_smooth_fold_weight(_ptr(wb), dtype, N, K, sp, _ptr(out)),
+                    "smooth_fold_weight")
+        return out
+
+    def dequant_ex(self, acc: np.ndarray, s_tok: np.ndarray, s_w: np.ndarray, y_dtype: int):
+        """uint16 patterns [M, N] of the fp16 / bf16 outputs."""
+        a = acc if acc.ndim == 3 else acc[:, :, None]
+        a = np.ascontiguousarray(a, dtype=np.int32)
+        M, N, G = a.shape
+        st = np.ascontiguousarray(s_tok, dtype=np.float32)
+        sw = np.ascontiguousarray(np.asarray(s_w, dtype=np.float32).reshape(N, G))
+        y = np.empty((M, N), np.uint16)
+        self._check(self.lib.oracle_dequant_ex(_ptr(a), _ptr(st), _ptr(sw), M, N, G, y_dtype,
+                                               _ptr(y)), "dequant_ex")
+        return y
+
+    def linear_ex(self, xbits: np.ndarray, x_dtype: int, wq: np.ndarray, s_w: np.ndarray,
+                  bits: int = 8, group_size: int = 0, K: int | None = None, smooth=None,
+                  y_dtype: int = 0):
+        """Whole path; returns (y uint16 patterns [M, N], xq, s_tok)."""
+        xb = _half_bits(xbits)
+        M, ldx = xb.shape
+        K = ldx if K is None else K
+        N = wq.shape[0]
+        wq = np.ascontiguousarray(wq)
+        sw = np.ascontiguousarray(s_w, dtype=np.float32)
+        sm, sp = self._smooth(smooth)
+        xq = np.empty((M, K), np.int8)
+        st = np.empty((M,), np.float32)
+        y = np.empty((M, N), np.uint16)
+        self._check(self.lib.oracle_linear_ex(_ptr(xb), x_dtype, M, K, ldx, sp, _ptr(wq), _ptr(sw),
+                                              bits, N, group_size, y_dtype, _ptr(xq), _ptr(st),
+                                              _ptr(y)), "linear_ex")
+        return y, xq, st
 
     def quantize_act(self, x: np.ndarray, K: int | None = None):
         """x: fp16 [M, ldx]; quantizes the first K (default: all) columns of

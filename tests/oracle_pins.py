@@ -325,6 +325,164 @@ def pin_clip_closed_forms(orc):
     assert (ratio <= -8.5).any() and (ratio >= 7.5).any()
 
 
+# ------------------------------------------------- bf16 and smoothing ---
+
+def _torch_bf16_bits(values_f32):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(values_f32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def pin_bf16_decode_exhaustive(orc):
+    """All 2^16 bf16 patterns widen to the value torch's bfloat16 type gives."""
+    import torch
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([orc.bf16_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def pin_bf16_encode(orc):
+    """Rounding to bf16 agrees with torch's float32 -> bfloat16 conversion
+    (round to nearest even) on fp32-exact inputs: every bf16 value, the
+    midpoints between neighbours (ties), their float32 neighbours, random
+    values, the overflow edge and subnormals; plus hand-worked fp64 inputs
+    that fp32 cannot hold (golden fixture)."""
+    rng = np.random.default_rng(31)
+    b = np.arange(0, 0x7F80, dtype=np.uint32)
+    vals = (b << 16).view(np.float32)
+    mids = ((b << 16) + 0x8000).view(np.float32)
+    xs = np.concatenate([vals, mids, np.nextafter(mids, np.float32(np.inf)),
+                         np.nextafter(mids, np.float32(0)), rng.standard_normal(20000).astype(np.float32),
+                         np.float32([3.3895314e38, 3.3961775e38, 3.4028235e38, 1e-40, 9.2e-41])])
+    xs = np.concatenate([xs, -xs])
+    ref = _torch_bf16_bits(xs)
+    got = np.array([orc.double_to_bf16(float(v)) for v in xs], np.uint16)
+    assert np.array_equal(got, ref)
+    g = _golden("bf16_rounding.json")
+    for case in g["cases"]:
+        v = float.fromhex(case["value_hex"])
+        assert orc.double_to_bf16(v) == int(case["bits"], 16), case
+
+
+def pin_bf16_activations_match_fp16(orc):
+    """Values held exactly by both types (at most 8 significant bits, within
+    fp16's normal range) quantize identically from either type."""
+    rng = np.random.default_rng(32)
+    m = rng.integers(-255, 256, size=(6, 512)).astype(np.float64)
+    e = rng.integers(-6, 4, size=(6, 512)).astype(np.float64)
+    x = m * 2.0 ** e
+    h = _f16(x)
+    assert np.array_equal(h.astype(np.float64), x)
+    bb = _torch_bf16_bits(x.astype(np.float32))
+    a, sa = orc.quantize_act(h)
+    b, sb = orc.quantize_act_ex(bb, 1)
+    assert np.array_equal(a, b) and np.array_equal(sa, sb)
+    wa, wsa = orc.quantize_weight(h, 4, 64)
+    wb, wsb = orc.quantize_weight_ex(bb, 1, 4, 64)
+    assert np.array_equal(wa, wb) and np.array_equal(wsa, wsb)
+
+
+def pin_smoothing_closed_forms(orc):
+    """Smoothing divides each channel before the absmax: factors of 1 change
+    nothing; power-of-two factors equal quantizing the exactly rescaled
+    values; a lone outlier channel divided by its own size stops dominating
+    the scale (the whole row then quantizes to 127)."""
+    from synth_inputs import activations
+    x = activations(5, 256, seed=7)
+    a, sa = orc.quantize_act(x)
+    b, sb = orc.quantize_act_ex(x, 0, smooth=np.ones(256, np.float32))
+    assert np.array_equal(a, b) and np.array_equal(sa, sb)
+    rng = np.random.default_rng(33)
+    j = rng.integers(-2, 3, 256)
+    xs = _f16(np.round(rng.standard_normal((5, 256)) * 64) / 64)
+    scaled = _f16(xs.astype(np.float64) * 2.0 ** -j)
+    assert np.array_equal(scaled.astype(np.float64), xs.astype(np.float64) * 2.0 ** -j)
+    c, sc = orc.quantize_act_ex(xs, 0, smooth=(2.0 ** j).astype(np.float32))
+    d, sd = orc.quantize_act(scaled)
+    assert np.array_equal(c, d) and np.array_equal(sc, sd)
+    row = np.ones((1, 64), np.float16)
+    row[0, 0] = 100
+    lam = np.ones(64, np.float32)
+    lam[0] = 100
+    q, s = orc.quantize_act_ex(row, 0, smooth=lam)
+    assert np.all(q == 127) and s[0] == np.float32(1.0) / np.float32(127.0)
+    q0, _ = orc.quantize_act(row)
+    assert q0[0, 0] == 127 and np.all(q0[0, 1:] == 1)
+
+
+def pin_smooth_fold(orc):
+    """The weight fold w * smooth[k] is rounded once: power-of-two factors
+    scale exactly; general fp32 factors match numpy's correctly rounded
+    float64 -> float16 conversion; bf16 weights with factors whose products
+    fit fp32 match torch's float32 -> bfloat16 conversion."""
+    rng = np.random.default_rng(34)
+    N, K = 64, 4096
+    w = _f16(0.05 * rng.standard_normal((N, K)))
+    j = rng.integers(0, 4, K)  # upward: no fp16 subnormal loses bits
+    out = orc.smooth_fold_weight(w, 0, (2.0 ** j).astype(np.float32)).view(np.float16)
+    assert np.array_equal(out.astype(np.float64), w.astype(np.float64) * 2.0 ** j)
+    lam = rng.uniform(0.05, 20.0, K).astype(np.float32)
+    out = orc.smooth_fold_weight(w, 0, lam)
+    ref = (w.astype(np.float64) * lam.astype(np.float64)).astype(np.float16).view(np.uint16)
+    assert np.array_equal(out, ref)
+    wb = _torch_bf16_bits(0.05 * rng.standard_normal((N, K)))
+    lam16 = (rng.integers(1, 2 ** 16, K) * 2.0 ** -12).astype(np.float32)    # 16 significant bits
+    wb_val = (wb.astype(np.uint32) << 16).view(np.float32)
+    prod = wb_val.astype(np.float64) * lam16.astype(np.float64)
+    assert np.array_equal(prod.astype(np.float32).astype(np.float64), prod)  # exact in fp32
+    out = orc.smooth_fold_weight(wb, 1, lam16)
+    assert np.array_equal(out, _torch_bf16_bits(prod.astype(np.float32)))
+
+
+def pin_bf16_output_nearest(orc):
+    """bf16 outputs are the nearest bf16 values of the float64 dequant that
+    the fp16 outputs are pinned on: for every output, no other bf16 value is
+    closer to numpy's float64 (xq * s_tok) @ (wq * s_w)^T."""
+    from synth_inputs import activations, weights
+    x = activations(8, 512, seed=12)
+    w = weights(40, 512, seed=12)
+    for bits, gs in ((8, 0), (8, 64), (4, 128)):
+        wq, sw = orc.quantize_weight(w, bits, gs)
+        yb, xq, st = orc.linear_ex(x, 0, wq, sw, bits, gs, y_dtype=1)
+        codes = wq.astype(np.int64) if bits == 8 else _unpack4(wq)
+        L = 512 if gs == 0 else gs
+        swf = np.repeat(np.asarray(sw, np.float64).reshape(40, -1), L, axis=1)
+        ref = (xq.astype(np.float64) * st.astype(np.float64)[:, None]) @ (codes * swf).T
+        got = (yb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        up = (((yb.astype(np.uint32) + 1) << 16).view(np.float32)).astype(np.float64)
+        dn = (((yb.astype(np.uint32) - 1) << 16).view(np.float32)).astype(np.float64)
+        err = np.abs(got - ref)
+        assert np.all(err <= np.abs(up - ref) * (1 + 1e-9)) and np.all(err <= np.abs(dn - ref) * (1 + 1e-9))
+        assert np.array_equal(orc.dequant_ex(orc.gemm_acc(xq, wq, bits, gs), st, sw, 1), yb)
+        yh, _, _ = orc.linear_ex(x, 0, wq, sw, bits, gs, y_dtype=0)
+        assert np.array_equal(yh.view(np.float16), orc.linear(x, wq, sw, bits, gs)[0])
+
+
+def pin_smoothing_improves_outlier_workload(orc):
+    """What smoothing is for: on the outlier workload (1% of input channels
+    20x larger), SmoothQuant factors lam_k = sqrt(max|X_k| / max|W_k|) with
+    the weights folded bring the quantized layer much closer to the fp16
+    product than plain W8A8."""
+    from synth_inputs import activations, weights
+    x = activations(64, 1024)
+    w = weights(256, 1024)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    wq, sw = orc.quantize_weight(w, 8, 0)
+    y0 = orc.linear(x, wq, sw)[0].astype(np.float64)
+    ax = np.abs(x.astype(np.float64)).max(0)
+    aw = np.abs(w.astype(np.float64)).max(0)
+    lam = np.sqrt(ax / aw).astype(np.float32)
+    wf = orc.smooth_fold_weight(w, 0, lam).view(np.float16)
+    wq1, sw1 = orc.quantize_weight(wf, 8, 0)
+    y1 = orc.linear_ex(x, 0, wq1, sw1, smooth=lam)[0].view(np.float16).astype(np.float64)
+    e0 = np.linalg.norm(y0 - ref) / np.linalg.norm(ref)
+    e1 = np.linalg.norm(y1 - ref) / np.linalg.norm(ref)
+    assert e1 < 0.6 * e0, (e0, e1)
+
+
 # ---------------------------------------------------------- accumulation ---
 
 def _brute_acc(xq, wcodes, gs):

@@ -19,8 +19,7 @@ MUTATIONS = {
     "round_half_away": ("float r = nearbyintf(t);", "float r = roundf(t);"),
     "reciprocal_multiply": ("/ s;  /* fp32 quotient */", "* (1.0f / s);"),
     "truncate_not_round": ("float r = nearbyintf(t);", "float r = truncf(t);"),
-    "signed_absmax": ("float a = fabsf(oracle_half_to_float(x[i]));",
-                      "float a = oracle_half_to_float(x[i]);"),
+    "signed_absmax": ("float a = fabsf(v[i]);", "float a = v[i];"),
     "nibble_order_pack": ("(uint8_t)(u_even | (u_odd << 4))", "(uint8_t)(u_odd | (u_even << 4))"),
     "nibble_order_unpack": ("(k % 2 == 0) ? (b & 0xf) : (b >> 4)", "(k % 2 == 1) ? (b & 0xf) : (b >> 4)"),
     "zero_point_7": ("return u - 8;", "return u - 7;"),
@@ -32,8 +31,7 @@ MUTATIONS = {
     "group_range_off_by_one": ("g * gs, (g + 1) * gs);", "g * gs, (g + 1) * gs - 1);"),
     "group_scale_transposed": ("t += (double)s_w_row[g] * (double)acc_row[g];",
                                "t += (double)s_w_row[0] * (double)acc_row[g];"),
-    "token_scale_dropped": ("return oracle_double_to_half((double)s_tok * t);",
-                            "return oracle_double_to_half(t);"),
+    "token_scale_dropped": ("return (double)s_tok * t;", "return t;"),
     "half_decode_exponent": ("ldexp((double)(1024 + man), e - 25)", "ldexp((double)(1024 + man), e - 24)"),
     "half_encode_ties_away": ("double m = nearbyint(ldexp(a, -q));", "double m = round(ldexp(a, -q));"),
     "half_encode_quantum": ("? -24 : e - 11;", "? -24 : e - 10;"),
@@ -42,11 +40,24 @@ MUTATIONS = {
     "percentile_rank_n": ("double h = (double)(n - 1) * (p / 100.0);", "double h = (double)n * (p / 100.0);"),
     "percentile_lower_value": ("return g >= 0.5 ? b - d * (1.0 - g) : a + d * g;", "return a;"),
     "percentile_one_formula": ("return g >= 0.5 ? b - d * (1.0 - g) : a + d * g;", "return a + d * g;"),
-    "percentile_signed": ("buf[i] = fabs(oracle_half_to_double(x[i]));", "buf[i] = oracle_half_to_double(x[i]);"),
-    "clip_range_not_rounded": ("float range = (float)oracle_percentile_abs(run, gs, clip_percentile, buf);",
-                               "float range = (float)(oracle_percentile_abs(run, gs, clip_percentile, buf) * (1.0 + 1e-7));"),
-    "dequant_via_float": ("return oracle_double_to_half((double)s_tok * t);",
-                          "return oracle_double_to_half((double)(float)((float)s_tok * (float)t) * 1.0001);"),
+    "percentile_signed": ("buf[i] = fabs((double)v[i]);", "buf[i] = (double)v[i];"),
+    "clip_range_not_rounded": ("float range = clip ? (float)percentile_abs(v, gs, clip_percentile, buf)",
+                               "float range = clip ? (float)(percentile_abs(v, gs, clip_percentile, buf) * (1.0 + 1e-7))"),
+    "smooth_multiplies": ("v[i] = smooth ? f / smooth[i] : f;", "v[i] = smooth ? f * smooth[i] : f;"),
+    "smooth_ignored": ("v[i] = smooth ? f / smooth[i] : f;", "v[i] = f;"),
+    "smooth_channel_shifted": ("v[i] = smooth ? f / smooth[i] : f;", "v[i] = smooth ? f / smooth[i ? i - 1 : 0] : f;"),
+    "fold_divides": ("* (double)smooth[k], dtype);", "/ (double)smooth[k], dtype);"),
+    "fold_via_fp32": ("narrow((double)widen(w[n * K + k], dtype) * (double)smooth[k], dtype);",
+                      "narrow((double)(widen(w[n * K + k], dtype) * smooth[k]), dtype);"),
+    "bf16_decode_shift": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
+    "bf16_encode_quantum": ("-133 : e - 8;", "-133 : e - 7;"),
+    "bf16_encode_ties_away": ("double m = nearbyint(ldexp(a, -q));           /* count of quanta, ties to even */\n    if (q == -133)",
+                              "double m = round(ldexp(a, -q));\n    if (q == -133)"),
+    "bf16_encode_bias": ("((q + 134) << 7)", "((q + 133) << 7)"),
+    "output_dtype_ignored": ("narrow(dequant_value(s_tok[m], s_w + n * G, acc + (m * N + n) * G, G),\n                                  y_dtype);",
+                             "narrow(dequant_value(s_tok[m], s_w + n * G, acc + (m * N + n) * G, G),\n                                  DT_F16);"),
+    "dequant_via_float": ("return (double)s_tok * t;",
+                          "return (double)(float)((float)s_tok * (float)t) * 1.0001;"),
 }
 
 
