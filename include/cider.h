@@ -83,6 +83,15 @@ typedef enum {
     CIDER_ERR_WORKSPACE = 6          /* workspace missing or smaller than cider_linear_workspace_bytes */
 } cider_status;
 
+/* Element type of 16-bit activations, weights and outputs (Cider README
+   feature list: automatic dtype handling, float16 / bfloat16).  Values of
+   either type are widened exactly to fp32; outputs are rounded once from the
+   fp32 result to nearest even. */
+typedef enum {
+    CIDER_DTYPE_F16 = 0,
+    CIDER_DTYPE_BF16 = 1
+} cider_dtype;
+
 /* 1 if the current HIP device is a gfx950 GPU that the library can use, else 0.
    Never crashes: returns 0 when the runtime finds no device.  The environment
    variable CIDER_FORCE_UNAVAILABLE=1 makes it return 0 (a test hook for the
@@ -114,6 +123,32 @@ cider_status cider_quantize_weight_clipped(const void *w_f16, int64_t N, int64_t
                                            int group_size, double clip_percentile, void *wq,
                                            float *s_w, void *stream);
 
+/* Weight quantization for either 16-bit type, with optional percentile
+   clipping: cider_quantize_weight / cider_quantize_weight_clipped for a w of
+   type w_dtype (bf16 magnitudes order like fp16 ones, so clipping finds the
+   same order statistics).  clip_percentile = 100 is plain absmax. */
+cider_status cider_quantize_weight_ex(const void *w, int w_dtype, int64_t N, int64_t K, int bits,
+                                      int group_size, double clip_percentile, void *wq, float *s_w,
+                                      void *stream);
+
+/* SmoothQuant's weight fold (Cider README: SmoothQuant named among the
+   preprocessing methods for quantization-friendly models).  With smoothing
+   factors s [K] (fp32, positive, 16-byte aligned) the activations are
+   divided by s inside cider_quantize_act_ex / cider_linear_ex and the weights
+   absorb it offline: w_out[n, k] = w[n, k] * s[k], the exact product rounded
+   once to nearest even in w's own type.  w, w_out [N, K] of type w_dtype,
+   16-byte aligned; K % 8 == 0; w_out may equal w. */
+cider_status cider_smooth_fold_weight(const void *w, int w_dtype, int64_t N, int64_t K,
+                                      const float *smooth, void *w_out, void *stream);
+
+/* Per-token activation quantization of fp16 or bf16 activations, with an
+   optional SmoothQuant smoothing vector smooth [K] (fp32, 16-byte aligned,
+   NULL for none): x'[m, k] = fp32(x[m, k] / smooth[k]) (correctly rounded)
+   before the absmax, and the codes are those of x'.  Otherwise as
+   cider_quantize_act. */
+cider_status cider_quantize_act_ex(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                   const float *smooth, int8_t *xq, float *s_tok, void *stream);
+
 /* Per-token activation quantization (Cider README "Metal Kernel Pipeline",
    step quantize_per_token; "Quantization" table, Activations row).
    x: fp16 [M, K] with row stride ldx.  xq: int8 [M, K]; s_tok: fp32 [M]. */
@@ -136,6 +171,12 @@ cider_status cider_w8a8_gemm(const int8_t *xq, const float *s_tok, const int8_t 
 cider_status cider_w4a8_gemm(const int8_t *xq, const float *s_tok, const uint8_t *wq4,
                              const float *s_w, int64_t M, int64_t N, int64_t K,
                              int group_size, void *y_f16, void *stream);
+
+/* Either product (bits 8: wq int8 [N, K]; bits 4: packed uint8 [N, K/2]) with
+   the output rounded to y_dtype (fp16 or bf16): y [M, N]. */
+cider_status cider_gemm_ex(const int8_t *xq, const float *s_tok, const void *wq, const float *s_w,
+                           int64_t M, int64_t N, int64_t K, int bits, int group_size, int y_dtype,
+                           void *y, void *stream);
 
 /* Test hooks: the same kernels with the dequant epilogue replaced by a raw
    store of the int32 accumulators ("Quantization" table, Accumulation INT32):
@@ -162,6 +203,16 @@ cider_status cider_w4a8_linear(const void *x_f16, int64_t M, int64_t K, int64_t 
                                const uint8_t *wq4, const float *s_w, int64_t N, int group_size,
                                void *workspace, size_t workspace_bytes, void *y_f16,
                                void *stream);
+
+/* The whole layer for any input / output type, with optional smoothing:
+   cider_quantize_act_ex into `workspace`, then cider_gemm_ex.  An fp16 token
+   (M = 1) without smoothing is quantized inside the matrix-vector kernel and
+   needs no workspace; every other call needs cider_linear_workspace_bytes(M,
+   K) bytes of it. */
+cider_status cider_linear_ex(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             const float *smooth, const void *wq, const float *s_w, int64_t N,
+                             int bits, int group_size, int y_dtype, void *workspace,
+                             size_t workspace_bytes, void *y, void *stream);
 
 /* Test hook: force the product path for subsequent calls in this process.
    0 = automatic (M = 1 with K <= 32768 -> matrix-vector, else matrix cores),

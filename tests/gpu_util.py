@@ -150,3 +150,43 @@ def assert_every_output(y_dev, xq: np.ndarray, s_tok: np.ndarray, wcodes: np.nda
         ref = (t * st[r0:r1, None]).cpu().numpy().astype(np.float16)
         assert_f16_close(y[r0:r1], ref, "%s rows %d..%d" % (what, r0, r1))
     del W, sw, st
+
+
+def bf16_bits(values) -> np.ndarray:
+    """uint16 patterns of fp32 values rounded to bf16 (torch's conversion)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(values, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bits_to_dev(a: np.ndarray):
+    """uint16 patterns onto the device (as an int16 tensor)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+def bits_to_host(t) -> np.ndarray:
+    import torch
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bits_to_f64(bits: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == 1:
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return bits.view(np.float16).astype(np.float64)
+
+
+def assert_out_close(got_bits: np.ndarray, ref_bits: np.ndarray, dtype: int, what: str = ""):
+    """fp16 outputs: |d| <= 1e-3 + 2^-10 |ref|.  bf16 outputs (8 significant
+    bits): within one bf16 ulp of the reference, |d| <= 1e-3 + 2^-7 |ref|."""
+    if dtype == 0:
+        return assert_f16_close(got_bits.view(np.float16), ref_bits.view(np.float16), what)
+    g, r = bits_to_f64(got_bits, 1), bits_to_f64(ref_bits, 1)
+    assert np.array_equal(np.isnan(g), np.isnan(r)), what + ": NaN pattern differs"
+    fin = np.isfinite(r)
+    assert np.array_equal(g[~fin & ~np.isnan(r)], r[~fin & ~np.isnan(r)]), what + ": Inf differs"
+    err = np.abs(g[fin] - r[fin])
+    bound = 1e-3 + 2.0 ** -7 * np.abs(r[fin])
+    bad = err > bound
+    assert not bad.any(), "%s: %d of %d bf16 outputs outside tolerance (worst |d|=%.3g)" % (
+        what, int(bad.sum()), bad.size, float(err.max()))

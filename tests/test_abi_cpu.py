@@ -138,6 +138,39 @@ def test_quantize_weight_clipped_argument_codes():
     assert qc(P, 0, 256, 8, 0, 99.9, None, None, stream=0, check=False) == cider.CIDER_OK
 
 
+def test_dtype_and_smoothing_argument_codes():
+    D16, B16 = cider.CIDER_DTYPE_F16, cider.CIDER_DTYPE_BF16
+    qa = cider.cider_quantize_act_ex
+    assert qa(P, B16, 4, 256, 256, P4, P2, P3, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert qa(P, D16, 4, 256, 256, None, P2, P3, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert qa(P, 2, 4, 256, 256, None, P2, P3, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    assert qa(P, B16, 4, 256, 256, BAD, P2, P3, stream=0, check=False) == cider.CIDER_ERR_MISALIGNED
+    qw = cider.cider_quantize_weight_ex
+    assert qw(P, B16, 64, 256, 4, 64, 99.9, P2, P3, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert qw(P, 3, 64, 256, 8, 0, 100.0, P2, P3, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    fw = cider.cider_smooth_fold_weight
+    assert fw(P, B16, 64, 256, P4, P2, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert fw(P, D16, 64, 252, P4, P2, stream=0, check=False) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
+    assert fw(P, D16, 64, 256, None, P2, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    assert fw(P, D16, 64, 256, BAD, P2, stream=0, check=False) == cider.CIDER_ERR_MISALIGNED
+    assert fw(P, 5, 64, 256, P4, P2, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    ge = cider.cider_gemm_ex
+    assert ge(P, P2, P3, P4, 16, 128, 256, 8, 0, B16, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert ge(P, P2, P3, P4, 16, 128, 256, 4, 64, D16, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert ge(P, P2, P3, P4, 16, 128, 256, 8, 0, 2, P, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    le = cider.cider_linear_ex
+    ws = cider.cider_linear_workspace_bytes(1, 256)
+    # one bf16 token is not fused: it needs the workspace
+    assert le(P, B16, 1, 256, 256, None, P3, P4, 128, 8, 0, D16, None, 0, P, stream=0,
+              check=False) == cider.CIDER_ERR_WORKSPACE
+    assert le(P, D16, 1, 256, 256, P4, P3, P4, 128, 8, 0, D16, None, 0, P, stream=0,
+              check=False) == cider.CIDER_ERR_WORKSPACE
+    assert le(P, B16, 1, 256, 256, P4, P3, P4, 128, 8, 0, B16, P2, ws, P, stream=0,
+              check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert le(P, 7, 1, 256, 256, None, P3, P4, 128, 8, 0, D16, P2, ws, P, stream=0,
+              check=False) == cider.CIDER_ERR_INVALID_ARG
+
+
 def test_linear_argument_codes():
     f = cider.cider_w8a8_linear
     ws = cider.cider_linear_workspace_bytes(16, 256)

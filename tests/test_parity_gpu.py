@@ -170,6 +170,124 @@ def test_quantize_weight_clipped_bitexact(N, K, bits, gs, p):
         assert np.array_equal(rq, pq) and np.array_equal(rs, ps)
 
 
+# ------------------------------------------------- bf16 and smoothing ---
+
+def _smoothing(K, seed):
+    rng = np.random.default_rng([seed, 77])
+    return rng.uniform(0.05, 20.0, K).astype(np.float32)
+
+
+@pytest.mark.parametrize("smooth", [False, True])
+@pytest.mark.parametrize("dtype", [0, 1])
+@pytest.mark.parametrize("M,K,ldx", [(64, 1024, 1024), (37, 2560, 2624), (5, 10240, 10240),
+                                     (3, 20480, 20480), (130, 256, 264), (1, 64, 64)])
+def test_quantize_act_ex_bitexact(M, K, ldx, dtype, smooth):
+    """fp16 / bf16 activations, with and without a smoothing vector:
+    codes and scales bit-exact (including a zero token and exact ties)."""
+    orc = get_oracle()
+    x = si.activations(M, ldx, seed=M + K).astype(np.float32)
+    if M >= 3:
+        x[1] = 0
+        x[2, :16] = [0.5, 1.5, 2.5, -0.5, -2.5, 126.5, 3.25, -3.75, 0.0, -127.0, 1, 2, 3, 4, 5, 6]
+    xb = gu.bf16_bits(x) if dtype == 1 else x.astype(np.float16).view(np.uint16)
+    sm = _smoothing(K, M) if smooth else None
+    import torch
+    xq = gu.empty((M, K), torch.int8)
+    st = gu.empty((M,), torch.float32)
+    smd = gu.to_dev(sm) if smooth else None
+    cider.cider_quantize_act_ex(gu.bits_to_dev(xb), dtype, M, K, ldx, smd, xq, st)
+    rq, rs = orc.quantize_act_ex(xb, dtype, K=K, smooth=sm)
+    assert np.array_equal(gu.to_host(st), rs)
+    assert np.array_equal(gu.to_host(xq), rq)
+
+
+@pytest.mark.parametrize("p", [100.0, 99.9])
+@pytest.mark.parametrize("N,K,bits,gs", [(512, 1024, 8, 0), (512, 1024, 4, 64), (512, 1024, 8, 128),
+                                         (2560, 10240, 4, 128), (10240, 2560, 8, 0)])
+def test_quantize_weight_bf16_bitexact(N, K, bits, gs, p):
+    import torch
+    orc = get_oracle()
+    wb = gu.bf16_bits(si.weights(N, K, seed=N).astype(np.float32))
+    wb[3] = 0
+    wq = gu.empty((N, K) if bits == 8 else (N, K // 2), torch.int8 if bits == 8 else torch.uint8)
+    sw = gu.empty((N,) if gs == 0 else (N, K // gs), torch.float32)
+    cider.cider_quantize_weight_ex(gu.bits_to_dev(wb), 1, N, K, bits, gs, p, wq, sw)
+    rq, rs = orc.quantize_weight_ex(wb, 1, bits, gs, p)
+    assert np.array_equal(gu.to_host(sw), rs)
+    assert np.array_equal(gu.to_host(wq), rq)
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+@pytest.mark.parametrize("N,K", [(512, 1024), (2560, 10240), (64, 8)])
+def test_smooth_fold_bitexact(N, K, dtype):
+    """w * s_k rounded once to the weight type, bit-exact; also in place."""
+    orc = get_oracle()
+    w = si.weights(N, K, seed=K).astype(np.float32)
+    wb = gu.bf16_bits(w) if dtype == 1 else w.astype(np.float16).view(np.uint16)
+    sm = _smoothing(K, N)
+    sm[:4] = [1.0, 2.0 ** -20, 3.0e4, 0.5]      # identity, tiny (subnormal products), large
+    ref = orc.smooth_fold_weight(wb, dtype, sm)
+    wd = gu.bits_to_dev(wb)
+    out = gu.bits_to_dev(np.zeros_like(wb))
+    cider.cider_smooth_fold_weight(wd, dtype, N, K, gu.to_dev(sm), out)
+    assert np.array_equal(gu.bits_to_host(out), ref)
+    cider.cider_smooth_fold_weight(wd, dtype, N, K, gu.to_dev(sm), wd)
+    assert np.array_equal(gu.bits_to_host(wd), ref)
+
+
+@pytest.mark.parametrize("path", [cider.PATH_GEMM, cider.PATH_AUTO])
+@pytest.mark.parametrize("bits,gs", MODES, ids=MODE_IDS)
+@pytest.mark.parametrize("M,N,K", [(1, 512, 1024), (64, 512, 1024), (300, 320, 1024),
+                                   (1100, 704, 1024), (200, 192, 1344)])
+def test_product_bf16_output(M, N, K, bits, gs, path):
+    """bf16 outputs of every product kernel within one bf16 ulp of the
+    oracle (which rounds the exact dequant once)."""
+    if gs and K % gs:
+        pytest.skip("K not a multiple of the group size")
+    import torch
+    cider.cider_set_path(path)
+    orc = get_oracle()
+    _, _, xq, st, wq, sw = _inputs(M, N, K, bits, gs, seed=M * 5 + N)
+    y = gu.empty((M, N), torch.int16)
+    cider.cider_gemm_ex(gu.to_dev(xq), gu.to_dev(st), gu.to_dev(wq), gu.to_dev(sw), M, N, K, bits,
+                        gs, 1, y)
+    ref = orc.dequant_ex(orc.gemm_acc(xq, wq, bits, gs), st, sw, 1)
+    gu.assert_out_close(gu.bits_to_host(y), ref, 1, "bf16 M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("bits,gs", MODES, ids=MODE_IDS)
+@pytest.mark.parametrize("x_dtype,y_dtype,smooth", [(1, 1, False), (0, 0, True), (1, 1, True),
+                                                    (1, 0, False), (0, 1, False)])
+@pytest.mark.parametrize("M,N,K,ldx", [(1, 512, 1024, 1024), (1, 2560, 10240, 10240),
+                                       (64, 512, 1024, 1088), (130, 640, 2560, 2560)])
+def test_linear_ex_whole_path(M, N, K, ldx, x_dtype, y_dtype, smooth, bits, gs):
+    """The whole layer for bf16 / fp16 inputs and outputs, with SmoothQuant
+    smoothing (activations divided inside the quantizer, weights folded by
+    the library's fold kernel), against the oracle's whole path."""
+    if gs and K % gs:
+        pytest.skip("K not a multiple of the group size")
+    import torch
+    orc = get_oracle()
+    x = si.activations(M, ldx, seed=K).astype(np.float32)
+    xb = gu.bf16_bits(x) if x_dtype == 1 else x.astype(np.float16).view(np.uint16)
+    w = si.weights(N, K, seed=K)
+    sm = _smoothing(K, 3) if smooth else None
+    wbits = w.view(np.uint16)
+    if smooth:
+        wbits = orc.smooth_fold_weight(wbits, 0, sm)
+        wd = gu.bits_to_dev(w.view(np.uint16))
+        cider.cider_smooth_fold_weight(wd, 0, N, K, gu.to_dev(sm), wd)
+        assert np.array_equal(gu.bits_to_host(wd), wbits)
+    wq, sw = orc.quantize_weight(wbits.view(np.float16), bits, gs)
+    ws_bytes = cider.cider_linear_workspace_bytes(M, K)
+    ws = gu.empty((max(ws_bytes, 16),), torch.uint8)
+    y = gu.empty((M, N), torch.int16)
+    cider.cider_linear_ex(gu.bits_to_dev(xb), x_dtype, M, K, ldx, gu.to_dev(sm) if smooth else None,
+                          gu.to_dev(wq), gu.to_dev(sw), N, bits, gs, y_dtype, ws, ws_bytes, y)
+    ref, _, _ = orc.linear_ex(xb, x_dtype, wq, sw, bits, gs, K=K, smooth=sm, y_dtype=y_dtype)
+    gu.assert_out_close(gu.bits_to_host(y), ref, y_dtype, "linear_ex M=%d" % M)
+
+
 # ----------------------------------------------------------------- product ---
 
 PRODUCT_SHAPES = [(64, 512, 1024), (300, 320, 1024), (700, 576, 512), (513, 1024, 2560),

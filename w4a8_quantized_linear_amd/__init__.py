@@ -32,8 +32,12 @@ EXPORTS = (
     "cider_is_available", "cider_status_str", "cider_quantize_weight", "cider_quantize_act",
     "cider_w8a8_gemm", "cider_w4a8_gemm", "cider_w8a8_gemm_i32", "cider_w4a8_gemm_i32",
     "cider_linear_workspace_bytes", "cider_w8a8_linear", "cider_w4a8_linear", "cider_set_path",
-    "cider_quantize_weight_clipped",
+    "cider_quantize_weight_clipped", "cider_quantize_weight_ex", "cider_smooth_fold_weight",
+    "cider_quantize_act_ex", "cider_gemm_ex", "cider_linear_ex",
 )
+
+CIDER_DTYPE_F16 = 0
+CIDER_DTYPE_BF16 = 1
 
 
 class CiderError(RuntimeError):
@@ -64,6 +68,11 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         "cider_quantize_weight": ([P, I64, I64, I, I, P, P, P], I),
         "cider_quantize_act": ([P, I64, I64, I64, P, P, P], I),
         "cider_quantize_weight_clipped": ([P, I64, I64, I, I, ctypes.c_double, P, P, P], I),
+        "cider_quantize_weight_ex": ([P, I, I64, I64, I, I, ctypes.c_double, P, P, P], I),
+        "cider_smooth_fold_weight": ([P, I, I64, I64, P, P, P], I),
+        "cider_quantize_act_ex": ([P, I, I64, I64, I64, P, P, P, P], I),
+        "cider_gemm_ex": ([P, P, P, P, I64, I64, I64, I, I, I, P, P], I),
+        "cider_linear_ex": ([P, I, I64, I64, I64, P, P, P, I64, I, I, I, P, SZ, P, P], I),
         "cider_w8a8_gemm": ([P, P, P, P, I64, I64, I64, I, P, P], I),
         "cider_w4a8_gemm": ([P, P, P, P, I64, I64, I64, I, P, P], I),
         "cider_w8a8_gemm_i32": ([P, P, I64, I64, I64, I, P, P], I),
@@ -126,6 +135,41 @@ def cider_quantize_weight_clipped(w_f16, N, K, bits, group_size, clip_percentile
                                               float(clip_percentile), _ptr(wq), _ptr(s_w),
                                               _stream(stream))
     return _ret(st, "cider_quantize_weight_clipped", check)
+
+
+def cider_quantize_weight_ex(w, w_dtype, N, K, bits, group_size, clip_percentile, wq, s_w,
+                             stream=None, check=True):
+    st = load().cider_quantize_weight_ex(_ptr(w), w_dtype, N, K, bits, group_size,
+                                         float(clip_percentile), _ptr(wq), _ptr(s_w),
+                                         _stream(stream))
+    return _ret(st, "cider_quantize_weight_ex", check)
+
+
+def cider_smooth_fold_weight(w, w_dtype, N, K, smooth, w_out, stream=None, check=True):
+    st = load().cider_smooth_fold_weight(_ptr(w), w_dtype, N, K, _ptr(smooth), _ptr(w_out),
+                                         _stream(stream))
+    return _ret(st, "cider_smooth_fold_weight", check)
+
+
+def cider_quantize_act_ex(x, x_dtype, M, K, ldx, smooth, xq, s_tok, stream=None, check=True):
+    st = load().cider_quantize_act_ex(_ptr(x), x_dtype, M, K, ldx, _ptr(smooth), _ptr(xq),
+                                      _ptr(s_tok), _stream(stream))
+    return _ret(st, "cider_quantize_act_ex", check)
+
+
+def cider_gemm_ex(xq, s_tok, wq, s_w, M, N, K, bits, group_size, y_dtype, y, stream=None,
+                  check=True):
+    st = load().cider_gemm_ex(_ptr(xq), _ptr(s_tok), _ptr(wq), _ptr(s_w), M, N, K, bits,
+                              group_size, y_dtype, _ptr(y), _stream(stream))
+    return _ret(st, "cider_gemm_ex", check)
+
+
+def cider_linear_ex(x, x_dtype, M, K, ldx, smooth, wq, s_w, N, bits, group_size, y_dtype,
+                    workspace, workspace_bytes, y, stream=None, check=True):
+    st = load().cider_linear_ex(_ptr(x), x_dtype, M, K, ldx, _ptr(smooth), _ptr(wq), _ptr(s_w),
+                                N, bits, group_size, y_dtype, _ptr(workspace), workspace_bytes,
+                                _ptr(y), _stream(stream))
+    return _ret(st, "cider_linear_ex", check)
 
 
 def cider_quantize_act(x_f16, M, K, ldx, xq, s_tok, stream=None, check=True):

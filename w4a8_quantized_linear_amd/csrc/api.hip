@@ -109,10 +109,10 @@ cider_status run_product(const int8_t *xq, const float *s_tok, const void *wq, c
         return st;
     if (M == 0 || N == 0)
         return CIDER_OK;
-    if (!xq || !wq || !out || (kind == cider::OUT_F16 && (!s_tok || !s_w)))
+    const bool scaled = kind != cider::OUT_I32;
+    if (!xq || !wq || !out || (scaled && (!s_tok || !s_w)))
         return CIDER_ERR_INVALID_ARG;
-    if (!aligned16(xq) || !aligned16(wq) || !aligned16(out) ||
-        (kind == cider::OUT_F16 && (!aligned16(s_w))))
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(out) || (scaled && !aligned16(s_w)))
         return CIDER_ERR_MISALIGNED;
     int path = PATH_GEMM;
     st = pick_path(M, K, &path);
@@ -136,26 +136,36 @@ cider_status run_product(const int8_t *xq, const float *s_tok, const void *wq, c
     return from_hip(path == PATH_GEMV ? cider::launch_gemv(a, s) : cider::launch_gemm(a, s));
 }
 
-cider_status run_linear(const void *x, int64_t M, int64_t K, int64_t ldx, const void *wq,
-                        const float *s_w, int64_t N, int bits, int group_size, void *ws,
-                        size_t ws_bytes, void *y, void *stream)
+bool dtype_ok(int d) { return d == CIDER_DTYPE_F16 || d == CIDER_DTYPE_BF16; }
+
+cider::OutKind out_kind_of(int y_dtype)
+{
+    return y_dtype == CIDER_DTYPE_BF16 ? cider::OUT_BF16 : cider::OUT_F16;
+}
+
+cider_status run_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                        const float *smooth, const void *wq, const float *s_w, int64_t N, int bits,
+                        int group_size, int y_dtype, void *ws, size_t ws_bytes, void *y,
+                        void *stream)
 {
     cider_status st = check_shape(M, N, K, bits, group_size);
     if (st != CIDER_OK)
         return st;
-    if (ldx < K)
+    if (ldx < K || !dtype_ok(x_dtype) || !dtype_ok(y_dtype))
         return CIDER_ERR_INVALID_ARG;
     if (M == 0 || N == 0)
         return CIDER_OK;
     if (!x || !wq || !s_w || !y)
         return CIDER_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(wq) || !aligned16(s_w) || !aligned16(y) || ldx % 8 != 0)
+    if (!aligned16(x) || !aligned16(wq) || !aligned16(s_w) || !aligned16(y) || ldx % 8 != 0 ||
+        (smooth && !aligned16(smooth)))
         return CIDER_ERR_MISALIGNED;
     int path = PATH_GEMM;
     st = pick_path(M, K, &path);
     if (st != CIDER_OK)
         return st;
-    const bool fused = path == PATH_GEMV && M == 1;
+    // one fp16 token without smoothing: quantized inside the matrix-vector kernel
+    const bool fused = path == PATH_GEMV && M == 1 && x_dtype == CIDER_DTYPE_F16 && !smooth;
     if (!fused) {
         if (!ws || ws_bytes < cider_linear_workspace_bytes(M, K))
             return CIDER_ERR_WORKSPACE;
@@ -167,11 +177,12 @@ cider_status run_linear(const void *x, int64_t M, int64_t K, int64_t ldx, const 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (fused)
         return from_hip(cider::launch_gemv_fused(static_cast<const uint16_t *>(x), K, wq, s_w, N,
-                                                 bits, group_size, y, nullptr, nullptr, s));
+                                                 bits, group_size, y, nullptr, nullptr,
+                                                 out_kind_of(y_dtype), s));
     int8_t *xq = static_cast<int8_t *>(ws);
     float *s_tok = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + round256((size_t)(M * K)));
-    hipError_t e = cider::launch_quantize_rows(static_cast<const uint16_t *>(x), M, K, ldx, 8, xq,
-                                               s_tok, s);
+    hipError_t e = cider::launch_quantize_rows(static_cast<const uint16_t *>(x), x_dtype, M, K, ldx,
+                                               smooth, 8, xq, s_tok, s);
     if (e != hipSuccess)
         return CIDER_ERR_HIP;
     cider::ProductArgs a{};
@@ -184,9 +195,45 @@ cider_status run_linear(const void *x, int64_t M, int64_t K, int64_t ldx, const 
     a.K = K;
     a.bits = bits;
     a.group_size = group_size;
-    a.out_kind = cider::OUT_F16;
+    a.out_kind = out_kind_of(y_dtype);
     a.out = y;
     return from_hip(path == PATH_GEMV ? cider::launch_gemv(a, s) : cider::launch_gemm(a, s));
+}
+
+cider_status run_quantize_weight(const void *w_f16, int w_dtype, int64_t N, int64_t K, int bits,
+                                 int group_size, double clip_percentile, void *wq, float *s_w,
+                                 void *stream)
+{
+    if (N < 0 || K <= 0 || (bits != 8 && bits != 4) || !dtype_ok(w_dtype))
+        return CIDER_ERR_INVALID_ARG;
+    if (group_size != 0 && group_size != 64 && group_size != 128)
+        return CIDER_ERR_INVALID_ARG;
+    if (!(clip_percentile > 0.0 && clip_percentile <= 100.0))  // NaN fails too
+        return CIDER_ERR_INVALID_ARG;
+    if (K % 64 != 0 || K > kMaxK || (group_size && K % group_size != 0))
+        return CIDER_ERR_UNSUPPORTED_SHAPE;
+    if (N == 0)
+        return CIDER_OK;
+    if (!w_f16 || !wq || !s_w)
+        return CIDER_ERR_INVALID_ARG;
+    if (!aligned16(w_f16) || !aligned16(wq) || (reinterpret_cast<uintptr_t>(s_w) & 3u))
+        return CIDER_ERR_MISALIGNED;
+    if (!device_usable())
+        return CIDER_ERR_NO_DEVICE;
+    const int64_t len = group_size ? group_size : K;
+    const int64_t rows = N * (K / len);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t *w = static_cast<const uint16_t *>(w_f16);
+    if (clip_percentile == 100.0)
+        return from_hip(cider::launch_quantize_rows(w, w_dtype, rows, len, len, nullptr, bits, wq,
+                                                    s_w, s));
+    // fractional rank h = (len - 1) * (p / 100) in fp64, as numpy.percentile
+    const double h = (double)(len - 1) * (clip_percentile / 100.0);
+    const double j = std::floor(h);
+    const int64_t r0 = (int64_t)j;
+    const int64_t r1 = r0 + 1 < len ? r0 + 1 : len - 1;
+    return from_hip(cider::launch_clip_quantize_rows(w, w_dtype, rows, len, r0, r1, h - j, bits, wq,
+                                                     s_w, s));
 }
 
 }  // namespace
@@ -212,77 +259,71 @@ const char *cider_status_str(int status)
 cider_status cider_quantize_weight(const void *w_f16, int64_t N, int64_t K, int bits,
                                    int group_size, void *wq, float *s_w, void *stream)
 {
-    if (N < 0 || K <= 0 || (bits != 8 && bits != 4))
-        return CIDER_ERR_INVALID_ARG;
-    if (group_size != 0 && group_size != 64 && group_size != 128)
-        return CIDER_ERR_INVALID_ARG;
-    if (K % 64 != 0 || K > kMaxK || (group_size && K % group_size != 0))
-        return CIDER_ERR_UNSUPPORTED_SHAPE;
-    if (N == 0)
-        return CIDER_OK;
-    if (!w_f16 || !wq || !s_w)
-        return CIDER_ERR_INVALID_ARG;
-    if (!aligned16(w_f16) || !aligned16(wq) || (reinterpret_cast<uintptr_t>(s_w) & 3u))
-        return CIDER_ERR_MISALIGNED;
-    if (!device_usable())
-        return CIDER_ERR_NO_DEVICE;
-    const int64_t len = group_size ? group_size : K;
-    const int64_t rows = N * (K / len);
-    return from_hip(cider::launch_quantize_rows(static_cast<const uint16_t *>(w_f16), rows, len,
-                                                len, bits, wq, s_w,
-                                                static_cast<hipStream_t>(stream)));
+    return run_quantize_weight(w_f16, CIDER_DTYPE_F16, N, K, bits, group_size, 100.0, wq, s_w,
+                               stream);
 }
 
 cider_status cider_quantize_weight_clipped(const void *w_f16, int64_t N, int64_t K, int bits,
                                            int group_size, double clip_percentile, void *wq,
                                            float *s_w, void *stream)
 {
-    if (N < 0 || K <= 0 || (bits != 8 && bits != 4))
+    return run_quantize_weight(w_f16, CIDER_DTYPE_F16, N, K, bits, group_size, clip_percentile, wq,
+                               s_w, stream);
+}
+
+cider_status cider_quantize_weight_ex(const void *w, int w_dtype, int64_t N, int64_t K, int bits,
+                                      int group_size, double clip_percentile, void *wq, float *s_w,
+                                      void *stream)
+{
+    return run_quantize_weight(w, w_dtype, N, K, bits, group_size, clip_percentile, wq, s_w,
+                               stream);
+}
+
+cider_status cider_smooth_fold_weight(const void *w, int w_dtype, int64_t N, int64_t K,
+                                      const float *smooth, void *w_out, void *stream)
+{
+    if (N < 0 || K <= 0 || !dtype_ok(w_dtype))
         return CIDER_ERR_INVALID_ARG;
-    if (group_size != 0 && group_size != 64 && group_size != 128)
-        return CIDER_ERR_INVALID_ARG;
-    if (!(clip_percentile > 0.0 && clip_percentile <= 100.0))  // NaN fails too
-        return CIDER_ERR_INVALID_ARG;
-    if (K % 64 != 0 || K > kMaxK || (group_size && K % group_size != 0))
+    if (K % 8 != 0)
         return CIDER_ERR_UNSUPPORTED_SHAPE;
     if (N == 0)
         return CIDER_OK;
-    if (!w_f16 || !wq || !s_w)
+    if (!w || !smooth || !w_out)
         return CIDER_ERR_INVALID_ARG;
-    if (!aligned16(w_f16) || !aligned16(wq) || (reinterpret_cast<uintptr_t>(s_w) & 3u))
+    if (!aligned16(w) || !aligned16(smooth) || !aligned16(w_out))
         return CIDER_ERR_MISALIGNED;
     if (!device_usable())
         return CIDER_ERR_NO_DEVICE;
-    const int64_t len = group_size ? group_size : K;
-    const int64_t rows = N * (K / len);
-    // fractional rank h = (len - 1) * (p / 100) in fp64, as numpy.percentile
-    const double h = (double)(len - 1) * (clip_percentile / 100.0);
-    const double j = std::floor(h);
-    const int64_t r0 = (int64_t)j;
-    const int64_t r1 = r0 + 1 < len ? r0 + 1 : len - 1;
-    return from_hip(cider::launch_clip_quantize_rows(static_cast<const uint16_t *>(w_f16), rows, len,
-                                                     r0, r1, h - j, bits, wq, s_w,
-                                                     static_cast<hipStream_t>(stream)));
+    return from_hip(cider::launch_smooth_fold(static_cast<const uint16_t *>(w), w_dtype, N, K, smooth,
+                                              static_cast<uint16_t *>(w_out),
+                                              static_cast<hipStream_t>(stream)));
 }
 
-cider_status cider_quantize_act(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
-                                int8_t *xq, float *s_tok, void *stream)
+cider_status cider_quantize_act_ex(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                   const float *smooth, int8_t *xq, float *s_tok, void *stream)
 {
-    if (M < 0 || K <= 0 || ldx < K)
+    if (M < 0 || K <= 0 || ldx < K || !dtype_ok(x_dtype))
         return CIDER_ERR_INVALID_ARG;
     if (K % 64 != 0 || K > kMaxK)
         return CIDER_ERR_UNSUPPORTED_SHAPE;
     if (M == 0)
         return CIDER_OK;
-    if (!x_f16 || !xq || !s_tok)
+    if (!x || !xq || !s_tok)
         return CIDER_ERR_INVALID_ARG;
-    if (!aligned16(x_f16) || !aligned16(xq) || ldx % 8 != 0 ||
-        (reinterpret_cast<uintptr_t>(s_tok) & 3u))
+    if (!aligned16(x) || !aligned16(xq) || ldx % 8 != 0 ||
+        (reinterpret_cast<uintptr_t>(s_tok) & 3u) || (smooth && !aligned16(smooth)))
         return CIDER_ERR_MISALIGNED;
     if (!device_usable())
         return CIDER_ERR_NO_DEVICE;
-    return from_hip(cider::launch_quantize_rows(static_cast<const uint16_t *>(x_f16), M, K, ldx, 8,
-                                                xq, s_tok, static_cast<hipStream_t>(stream)));
+    return from_hip(cider::launch_quantize_rows(static_cast<const uint16_t *>(x), x_dtype, M, K, ldx,
+                                                smooth, 8, xq, s_tok,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+cider_status cider_quantize_act(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
+                                int8_t *xq, float *s_tok, void *stream)
+{
+    return cider_quantize_act_ex(x_f16, CIDER_DTYPE_F16, M, K, ldx, nullptr, xq, s_tok, stream);
 }
 
 cider_status cider_w8a8_gemm(const int8_t *xq, const float *s_tok, const int8_t *wq,
@@ -297,6 +338,16 @@ cider_status cider_w4a8_gemm(const int8_t *xq, const float *s_tok, const uint8_t
                              void *y_f16, void *stream)
 {
     return run_product(xq, s_tok, wq4, s_w, M, N, K, 4, group_size, cider::OUT_F16, y_f16, stream);
+}
+
+cider_status cider_gemm_ex(const int8_t *xq, const float *s_tok, const void *wq, const float *s_w,
+                           int64_t M, int64_t N, int64_t K, int bits, int group_size, int y_dtype,
+                           void *y, void *stream)
+{
+    if (!dtype_ok(y_dtype))
+        return CIDER_ERR_INVALID_ARG;
+    return run_product(xq, s_tok, wq, s_w, M, N, K, bits, group_size, out_kind_of(y_dtype), y,
+                       stream);
 }
 
 cider_status cider_w8a8_gemm_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N,
@@ -324,16 +375,25 @@ cider_status cider_w8a8_linear(const void *x_f16, int64_t M, int64_t K, int64_t 
                                const int8_t *wq, const float *s_w, int64_t N, int group_size,
                                void *workspace, size_t workspace_bytes, void *y_f16, void *stream)
 {
-    return run_linear(x_f16, M, K, ldx, wq, s_w, N, 8, group_size, workspace, workspace_bytes,
-                      y_f16, stream);
+    return run_linear(x_f16, CIDER_DTYPE_F16, M, K, ldx, nullptr, wq, s_w, N, 8, group_size,
+                      CIDER_DTYPE_F16, workspace, workspace_bytes, y_f16, stream);
 }
 
 cider_status cider_w4a8_linear(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
                                const uint8_t *wq4, const float *s_w, int64_t N, int group_size,
                                void *workspace, size_t workspace_bytes, void *y_f16, void *stream)
 {
-    return run_linear(x_f16, M, K, ldx, wq4, s_w, N, 4, group_size, workspace, workspace_bytes,
-                      y_f16, stream);
+    return run_linear(x_f16, CIDER_DTYPE_F16, M, K, ldx, nullptr, wq4, s_w, N, 4, group_size,
+                      CIDER_DTYPE_F16, workspace, workspace_bytes, y_f16, stream);
+}
+
+cider_status cider_linear_ex(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             const float *smooth, const void *wq, const float *s_w, int64_t N,
+                             int bits, int group_size, int y_dtype, void *workspace,
+                             size_t workspace_bytes, void *y, void *stream)
+{
+    return run_linear(x, x_dtype, M, K, ldx, smooth, wq, s_w, N, bits, group_size, y_dtype,
+                      workspace, workspace_bytes, y, stream);
 }
 
 int cider_set_path(int path)

@@ -8,23 +8,48 @@
 
 namespace cider {
 
-// Symmetric absmax quantization of `rows` rows of `len` fp16 values (row
-// stride `ld` elements).  bits 8: out int8 [rows, len]; bits 4: out uint8
-// [rows, len/2] packed nibbles.  scale fp32 [rows].  len % 8 == 0.
+// Symmetric absmax quantization of `rows` rows of `len` fp16 (dtype 0) or
+// bf16 (dtype 1) values (row stride `ld` elements).  bits 8: out int8
+// [rows, len]; bits 4: out uint8 [rows, len/2] packed nibbles.  scale fp32
+// [rows].  len % 8 == 0.  smooth (fp32 [len], 16-byte aligned, bits 8 only)
+// or null: each element divided by its column's factor before the absmax.
 // Per-token activations are rows = M, len = K; per-channel weights rows = N;
 // per-group weights are the [N * K/gs, gs] view of W.
-hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t len, int64_t ld,
-                                int bits, void *out, float *scale, hipStream_t stream);
+hipError_t launch_quantize_rows(const uint16_t *x, int dtype, int64_t rows, int64_t len, int64_t ld,
+                                const float *smooth, int bits, void *out, float *scale,
+                                hipStream_t stream);
 
 // The same with each row's range the percentile of its |w| (percentile
 // clipping): ranks r0 <= r1 of the two order statistics and the
 // interpolation weight g, computed by the caller.  len % 8 == 0, len < 2^31.
-hipError_t launch_clip_quantize_rows(const uint16_t *w, int64_t rows, int64_t len, int64_t r0,
-                                     int64_t r1, double g, int bits, void *out, float *scale,
-                                     hipStream_t stream);
+hipError_t launch_clip_quantize_rows(const uint16_t *w, int dtype, int64_t rows, int64_t len,
+                                     int64_t r0, int64_t r1, double g, int bits, void *out,
+                                     float *scale, hipStream_t stream);
 
-// Output of the product kernels.
-enum OutKind { OUT_F16 = 0, OUT_I32 = 1 };
+// SmoothQuant's offline weight fold: w_out[n, k] = w[n, k] * smooth[k], the
+// exact product rounded once (to nearest even) to the weight's type.
+hipError_t launch_smooth_fold(const uint16_t *w, int dtype, int64_t N, int64_t K,
+                              const float *smooth, uint16_t *w_out, hipStream_t stream);
+
+// Output of the product kernels: fp16 or bf16 results, or the raw int32
+// accumulators (test hook).
+enum OutKind { OUT_F16 = 0, OUT_I32 = 1, OUT_BF16 = 2 };
+
+// Bit pattern of an fp32 result rounded to the output type, to nearest even
+// (fp16: the hardware conversion; bf16: the upper half of the fp32 pattern
+// after adding half an ulp, ties to even; NaN stays a quiet NaN).
+template <int OUT>
+__device__ __forceinline__ uint16_t out_bits(float y)
+{
+    if constexpr (OUT == OUT_BF16) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, y);
+        if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+            return (uint16_t)((u >> 16) | 0x40u);
+        return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+    } else {
+        return __builtin_bit_cast(uint16_t, (_Float16)y);
+    }
+}
 
 struct ProductArgs {
     const int8_t *xq;      // [M, K]
@@ -47,10 +72,10 @@ hipError_t launch_gemm_skinny(const ProductArgs &a, hipStream_t stream);
 hipError_t launch_gemv(const ProductArgs &a, hipStream_t stream);
 
 // One-token layer: quantizes the fp16 row x [K] inside the matrix-vector
-// kernel and writes y fp16 [N].  xq_out / s_tok_out may be null; when given,
+// kernel and writes y [N] (fp16 or bf16 by out_kind).  xq_out / s_tok_out may be null; when given,
 // the quantized row and its scale are written there as well.
 hipError_t launch_gemv_fused(const uint16_t *x, int64_t K, const void *wq, const float *s_w,
                              int64_t N, int bits, int group_size, void *y, int8_t *xq_out,
-                             float *s_tok_out, hipStream_t stream);
+                             float *s_tok_out, int out_kind, hipStream_t stream);
 
 }  // namespace cider

@@ -77,7 +77,7 @@ __device__ __attribute__((noinline)) double lerp_percentile(double a, double b, 
     return g >= 0.5 ? b - d * (1.0 - g) : a + d * g;
 }
 
-template <int BITS>
+template <int BITS, int DT>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void clip_quantize_kernel(
     const uint16_t *__restrict__ w, int64_t rows, int len, int r0, int r1, double g,
     uint8_t *__restrict__ out, float *__restrict__ scale)
@@ -132,14 +132,14 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void clip_quantize_kernel(
         locate<2>(h2, r1 - below0, lane, l1, unused);
     else
         locate<2>(h2 + 128, r1 - below1, lane, l1, unused);
-    const double a = (double)half_bits_to_float((uint32_t)((b0 << 7) | l0));
-    const double b = (double)half_bits_to_float((uint32_t)((b1 << 7) | l1));
+    const double a = (double)widen_bits<DT>((uint32_t)((b0 << 7) | l0));
+    const double b = (double)widen_bits<DT>((uint32_t)((b1 << 7) | l1));
     const float range = (float)lerp_percentile(a, b, g);
     const float s = range / quant_divisor<BITS>();
     if (lane == 0)
         scale[row] = s;
     for (int c = lane; c < nch; c += 64) {
-        const uint2 q = quantize_chunk_div<BITS>(*reinterpret_cast<const uint4 *>(xr + (int64_t)c * 8), s);
+        const uint2 q = quantize_chunk_div<BITS, DT>(*reinterpret_cast<const uint4 *>(xr + (int64_t)c * 8), s);
         if constexpr (BITS == 8)
             *reinterpret_cast<uint2 *>(out + row * len + (int64_t)c * 8) = q;
         else
@@ -147,22 +147,29 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void clip_quantize_kernel(
     }
 }
 
+template <int BITS, int DT>
+hipError_t launch_clip(const uint16_t *w, int64_t rows, int64_t len, int64_t r0, int64_t r1,
+                       double g, void *out, float *scale, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(64 * kRowsPerBlock);
+    hipLaunchKernelGGL((clip_quantize_kernel<BITS, DT>), grid, block, 0, stream, w, rows, (int)len,
+                       (int)r0, (int)r1, g, static_cast<uint8_t *>(out), scale);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_clip_quantize_rows(const uint16_t *w, int64_t rows, int64_t len, int64_t r0,
-                                     int64_t r1, double g, int bits, void *out, float *scale,
-                                     hipStream_t stream)
+hipError_t launch_clip_quantize_rows(const uint16_t *w, int dtype, int64_t rows, int64_t len,
+                                     int64_t r0, int64_t r1, double g, int bits, void *out,
+                                     float *scale, hipStream_t stream)
 {
     if (rows == 0)
         return hipSuccess;
-    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(64 * kRowsPerBlock);
-    if (bits == 8)
-        hipLaunchKernelGGL((clip_quantize_kernel<8>), grid, block, 0, stream, w, rows, (int)len,
-                           (int)r0, (int)r1, g, static_cast<uint8_t *>(out), scale);
-    else
-        hipLaunchKernelGGL((clip_quantize_kernel<4>), grid, block, 0, stream, w, rows, (int)len,
-                           (int)r0, (int)r1, g, static_cast<uint8_t *>(out), scale);
-    return hipGetLastError();
+    if (dtype == DT_BF16)
+        return bits == 8 ? launch_clip<8, DT_BF16>(w, rows, len, r0, r1, g, out, scale, stream)
+                         : launch_clip<4, DT_BF16>(w, rows, len, r0, r1, g, out, scale, stream);
+    return bits == 8 ? launch_clip<8, DT_F16>(w, rows, len, r0, r1, g, out, scale, stream)
+                     : launch_clip<4, DT_F16>(w, rows, len, r0, r1, g, out, scale, stream);
 }
 
 }  // namespace cider

@@ -205,7 +205,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     // tile's group, one dword each, copied with the operands (256-byte
     // blocks), padded to 1 KB.  The int32 hook has no scales (s_w is null):
     // no scale copies at all.
-    constexpr bool SCOPY = PG && OUT == OUT_F16;
+    constexpr bool SCOPY = PG && OUT != OUT_I32;
     constexpr int SB = SCOPY ? (TN * 4 + 255) / 256 : 0;  // the last block may run past TN
     constexpr int SBYTES = SCOPY ? (SB * 256 + 1023) / 1024 * 1024 : 0;
     constexpr int STAGE = XBYTES + WBYTES + SBYTES;
@@ -223,11 +223,11 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     // The fp16 per-channel epilogue reuses the stage ring to stage its rows
     // (rows of 2 * WN bytes padded by 16); it may need more than the ring.
     constexpr int ROWB = WN * 2 + 16;
-    constexpr int OSTAGE = OUT == OUT_F16 && !PG ? NW * 32 * ROWB : 0;
+    constexpr int OSTAGE = OUT != OUT_I32 && !PG ? NW * 32 * ROWB : 0;
     constexpr int SMEM = STAGES * STAGE > OSTAGE ? STAGES * STAGE : OSTAGE;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
-    __shared__ __attribute__((aligned(16))) float s_sw[OUT == OUT_F16 && !PG ? TN : 4];  // s_w tile
-    __shared__ __attribute__((aligned(16))) float s_st[OUT == OUT_F16 ? TM : 4];         // s_tok tile
+    __shared__ __attribute__((aligned(16))) float s_sw[OUT != OUT_I32 && !PG ? TN : 4];  // s_w tile
+    __shared__ __attribute__((aligned(16))) float s_st[OUT != OUT_I32 ? TM : 4];         // s_tok tile
 
     const int64_t M = args.M, N = args.N, K = args.K;
     int tn, tm;
@@ -326,7 +326,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     i32x16 acc[FN][FM];
     // Per group (fp16 output): facc accumulates each group's int32 sums
     // times the group's channel scales, in group order.
-    constexpr bool SCALED = PG && OUT == OUT_F16;
+    constexpr bool SCALED = PG && OUT != OUT_I32;
     float facc[SCALED ? FN : 1][SCALED ? FM : 1][SCALED ? 16 : 1];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
@@ -381,7 +381,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     // The dequant scales of this tile's channels and tokens, staged in LDS at
     // the start (plain loads whose latency hides under the prologue copies);
     // indices are clamped into range, values past the edge are never used.
-    if constexpr (OUT == OUT_F16) {
+    if constexpr (OUT != OUT_I32) {
         constexpr int TSW = PG ? 0 : TN;  // per group, channel scales come with the tiles
         for (int t = threadIdx.x; t < TSW + TM; t += NW * 64) {
             if (t < TSW)
@@ -512,7 +512,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
                     const int64_t m = m0 + t;
                     const float y = s_st[t] * facc[i][j][e];
                     if (full || (m < M && n < N))
-                        yout[m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
+                        yout[m * N + n] = out_bits<OUT>(y);
                 }
         }
     } else if constexpr (OUT == OUT_I32) {
@@ -554,10 +554,8 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
                     for (int e = 0; e < 4; ++e)
                         y[e] = (float)acc[i][j][4 * q + e] * st * sw[e];
                     uint2 packed;
-                    packed.x = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[0]) |
-                               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[1]) << 16);
-                    packed.y = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[2]) |
-                               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[3]) << 16);
+                    packed.x = (uint32_t)out_bits<OUT>(y[0]) | ((uint32_t)out_bits<OUT>(y[1]) << 16);
+                    packed.y = (uint32_t)out_bits<OUT>(y[2]) | ((uint32_t)out_bits<OUT>(y[3]) << 16);
                     *reinterpret_cast<uint2 *>(ob + frow * ROWB + c * 2) = packed;
                 }
             constexpr int CHUNKS = 32 * CPRO;
@@ -663,18 +661,27 @@ hipError_t launch_group_bits(const ProductArgs &a, hipStream_t stream)
 
 }  // namespace
 
+template <int OUT>
+hipError_t launch_kind(const ProductArgs &a, hipStream_t stream)
+{
+    if (a.group_size == 64)
+        return launch_group_bits<64, OUT>(a, stream);
+    if (a.group_size == 128)
+        return launch_group_bits<128, OUT>(a, stream);
+    if (a.bits == 8)
+        return launch_bits<8, OUT>(a, stream);
+    return launch_bits<4, OUT>(a, stream);
+}
+
 hipError_t launch_gemm(const ProductArgs &a, hipStream_t stream)
 {
     if (a.M <= 256 && a.group_size != 0)
         return launch_gemm_skinny(a, stream);
-    const bool f16 = a.out_kind == OUT_F16;
-    if (a.group_size == 64)
-        return f16 ? launch_group_bits<64, OUT_F16>(a, stream) : launch_group_bits<64, OUT_I32>(a, stream);
-    if (a.group_size == 128)
-        return f16 ? launch_group_bits<128, OUT_F16>(a, stream) : launch_group_bits<128, OUT_I32>(a, stream);
-    if (a.bits == 8)
-        return f16 ? launch_bits<8, OUT_F16>(a, stream) : launch_bits<8, OUT_I32>(a, stream);
-    return f16 ? launch_bits<4, OUT_F16>(a, stream) : launch_bits<4, OUT_I32>(a, stream);
+    switch (a.out_kind) {
+    case OUT_F16: return launch_kind<OUT_F16>(a, stream);
+    case OUT_BF16: return launch_kind<OUT_BF16>(a, stream);
+    default: return launch_kind<OUT_I32>(a, stream);
+    }
 }
 
 }  // namespace cider

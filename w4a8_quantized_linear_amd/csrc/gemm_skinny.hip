@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(ProductArgs args, int 
     if constexpr (!PG)
         for (int o = threadIdx.x; o < TM * TS; o += kThreads)
             part[o] = 0;
-    if constexpr (OUT == OUT_F16) {
+    if constexpr (OUT != OUT_I32) {
         for (int o = threadIdx.x; o < TM + TN; o += kThreads) {
             if (o < TM)
                 s_st[o] = args.s_tok[min(m0 + o, M - 1)];
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(ProductArgs args, int 
     const auto rx = __builtin_amdgcn_make_buffer_rsrc((void *)args.xq, (short)0, (int)(M * K), kRsrcWord3);
     const auto rw = __builtin_amdgcn_make_buffer_rsrc((void *)args.wq, (short)0, (int)(N * wld), kRsrcWord3);
     const auto rs = __builtin_amdgcn_make_buffer_rsrc((void *)args.s_w, (short)0,
-                                                      (OUT == OUT_F16 && PG) ? (int)(N * G * 4) : 0,
+                                                      (OUT != OUT_I32 && PG) ? (int)(N * G * 4) : 0,
                                                       kRsrcWord3);
 
     // This wavefront's units: wave, wave + 8, ... (at any moment the 8
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(ProductArgs args, int 
                     t.wp[s][i] = load8(rw, ls ? wrow[i] + kw + s * WSTEP : kDead);
             }
         }
-        if constexpr (PG && OUT == OUT_F16) {
+        if constexpr (PG && OUT != OUT_I32) {
 #pragma unroll
             for (int q = 0; q < GPU; ++q)
 #pragma unroll
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(ProductArgs args, int 
                             for (int j = 0; j < FM; ++j)
 #pragma unroll
                                 for (int e = 0; e < 4; ++e) {
-                                    if constexpr (OUT == OUT_F16) {
+                                    if constexpr (OUT != OUT_I32) {
                                         facc[i][j][e] += (float)acc[i][j][e] * t.sw[q][i];
                                     } else {
                                         const int64_t m = m0 + j * 16 + fq * 4 + e;
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(ProductArgs args, int 
                 static_cast<int32_t *>(args.out)[m * N + n] = total;
             } else {
                 const float y = (float)total * s_st[t] * s_sw[c];
-                static_cast<uint16_t *>(args.out)[m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
+                static_cast<uint16_t *>(args.out)[m * N + n] = out_bits<OUT>(y);
             }
         } else {
             float total = 0.f;
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(ProductArgs args, int 
             for (int w = 0; w < kWaves; ++w)
                 total += __builtin_bit_cast(float, part[w * TM * TS + t * TS + c]);
             const float y = s_st[t] * total;
-            static_cast<uint16_t *>(args.out)[m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
+            static_cast<uint16_t *>(args.out)[m * N + n] = out_bits<OUT>(y);
         }
     }
 }
@@ -349,7 +349,11 @@ hipError_t launch_out(const ProductArgs &a, hipStream_t stream)
 
 hipError_t launch_gemm_skinny(const ProductArgs &a, hipStream_t stream)
 {
-    return a.out_kind == OUT_F16 ? launch_out<OUT_F16>(a, stream) : launch_out<OUT_I32>(a, stream);
+    switch (a.out_kind) {
+    case OUT_F16: return launch_out<OUT_F16>(a, stream);
+    case OUT_BF16: return launch_out<OUT_BF16>(a, stream);
+    default: return launch_out<OUT_I32>(a, stream);
+    }
 }
 
 }  // namespace cider

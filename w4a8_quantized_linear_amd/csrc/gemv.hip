@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
             const uint32_t kc = (uint32_t)(sg * SEG + c);
             const bool live = valid && c < SEG && kc < (uint32_t)KC;
             wv[u][i] = load16(rw, live ? n * (uint32_t)wld + kc * 16u : kDead);
-            if constexpr (GS != 0 && OUT == OUT_F16)
+            if constexpr (GS != 0 && OUT != OUT_I32)
                 swv[u][i] = __builtin_bit_cast(
                     float, __builtin_amdgcn_raw_buffer_load_b32(rsw, live ? (n * G + kc / LPG) * 4u : kDead, 0, 0));
         }
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
     const int fin_r = tid % R;  // the output this thread finishes: (tid / R, tid % R)
     const bool fin = tid < M * R && n0 + fin_r < N;
     float fin_sw = 0.f;
-    if constexpr (GS == 0 && OUT == OUT_F16)
+    if constexpr (GS == 0 && OUT != OUT_I32)
         fin_sw = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(rsw, fin ? (uint32_t)(n0 + fin_r) * 4u : kDead, 0, 0));
 
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
                 const int t = wave_sum_i32(isum);
                 if (lane == 0)
                     ipart[m * 64 + unit] = t;
-            } else if constexpr (OUT == OUT_F16) {
+            } else if constexpr (OUT != OUT_I32) {
                 const float t = wave_sum_f32(fsum);
                 if (lane == 0)
                     part[m * 64 + unit] = t;
@@ -403,14 +403,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
             } else {
                 const float st = FUSED ? s_fused : p.s_tok[m];
                 const float y = (float)total * st * fin_sw;
-                static_cast<uint16_t *>(p.out)[m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
+                static_cast<uint16_t *>(p.out)[m * N + n] = out_bits<OUT>(y);
             }
         } else {
             float tot = 0.f;
             for (int sg = 0; sg < NSEG; ++sg)
                 tot += part[m * 64 + r * NSEG + sg];
             const float st = FUSED ? s_fused : p.s_tok[m];
-            static_cast<uint16_t *>(p.out)[m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)(st * tot));
+            static_cast<uint16_t *>(p.out)[m * N + n] = out_bits<OUT>(st * tot);
         }
     }
 }
@@ -495,12 +495,14 @@ hipError_t launch_gemv(const ProductArgs &a, hipStream_t stream)
     p.out = a.out;
     if (a.out_kind == OUT_F16)
         return dispatch<OUT_F16, false>(p, a.bits, a.group_size, stream);
+    if (a.out_kind == OUT_BF16)
+        return dispatch<OUT_BF16, false>(p, a.bits, a.group_size, stream);
     return dispatch<OUT_I32, false>(p, a.bits, a.group_size, stream);
 }
 
 hipError_t launch_gemv_fused(const uint16_t *x, int64_t K, const void *wq, const float *s_w,
                              int64_t N, int bits, int group_size, void *y, int8_t *xq_out,
-                             float *s_tok_out, hipStream_t stream)
+                             float *s_tok_out, int out_kind, hipStream_t stream)
 {
     GemvParams p{};
     p.x = x;
@@ -512,6 +514,8 @@ hipError_t launch_gemv_fused(const uint16_t *x, int64_t K, const void *wq, const
     p.out = y;
     p.xq_out = xq_out;
     p.s_tok_out = s_tok_out;
+    if (out_kind == OUT_BF16)
+        return dispatch<OUT_BF16, true>(p, bits, group_size, stream);
     return dispatch<OUT_F16, true>(p, bits, group_size, stream);
 }
 

@@ -1,5 +1,5 @@
-// Device-side quantization arithmetic shared by the quantize kernel and the
-// fused one-token matrix-vector kernel, so both produce identical codes.
+// Device-side quantization arithmetic shared by the quantize kernels and the
+// fused one-token matrix-vector kernel, so all produce identical codes.
 //
 // Cider README (ossradar.top repo page), "Quantization" table: symmetric INT8
 // per token for activations, symmetric INT8 / INT4 (zero-point 8) for weights.
@@ -19,9 +19,22 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// Largest magnitude among the 8 fp16 values of a 16-byte chunk, as fp16
-// magnitude bits.  For finite inputs the order of |x| equals the order of the
-// bit patterns with the sign bit cleared.
+// Element types of the fp16 / bf16 inputs.
+enum { DT_F16 = 0, DT_BF16 = 1 };
+
+// Exact fp32 value of a 16-bit element (bf16 is the upper half of an fp32).
+template <int DT>
+__device__ __forceinline__ float widen_bits(uint32_t h)
+{
+    if constexpr (DT == DT_BF16)
+        return __builtin_bit_cast(float, (h & 0xFFFFu) << 16);
+    else
+        return half_bits_to_float(h & 0xFFFFu);
+}
+
+// Largest magnitude among the 8 fp16 (or bf16) values of a 16-byte chunk, as
+// magnitude bits.  For finite inputs of either type the order of |x| equals
+// the order of the bit patterns with the sign bit cleared.
 __device__ __forceinline__ uint32_t chunk_absmax_bits(uint4 v)
 {
     typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -84,7 +97,7 @@ __device__ __forceinline__ uint2 pack_codes(const int (&q)[8])
 // rint(fl(x / s)) unless t lies within that distance of a half-integer.  A
 // chunk with a value within 2^-14 of a half-integer (about 1 value in 8000)
 // is recomputed with correctly rounded divisions.
-template <int BITS>
+template <int BITS, int DT = DT_F16>
 __device__ __forceinline__ uint2 quantize_chunk(uint4 v, float s, float rs)
 {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -92,8 +105,8 @@ __device__ __forceinline__ uint2 quantize_chunk(uint4 v, float s, float rs)
     bool near_half = false;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        f[2 * j] = half_bits_to_float(w[j] & 0xFFFFu);
-        f[2 * j + 1] = half_bits_to_float(w[j] >> 16);
+        f[2 * j] = widen_bits<DT>(w[j]);
+        f[2 * j + 1] = widen_bits<DT>(w[j] >> 16);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -115,16 +128,56 @@ __device__ __forceinline__ uint2 quantize_chunk(uint4 v, float s, float rs)
 
 // The same codes with a correctly rounded division for every value (fewer
 // live registers: for kernels that hold long rows in registers).
-template <int BITS>
+template <int BITS, int DT = DT_F16>
 __device__ __forceinline__ uint2 quantize_chunk_div(uint4 v, float s)
 {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     int q[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        q[2 * j] = code_of<BITS>(half_bits_to_float(w[j] & 0xFFFFu) / s, s);
-        q[2 * j + 1] = code_of<BITS>(half_bits_to_float(w[j] >> 16) / s, s);
+        q[2 * j] = code_of<BITS>(widen_bits<DT>(w[j]) / s, s);
+        q[2 * j + 1] = code_of<BITS>(widen_bits<DT>(w[j] >> 16) / s, s);
     }
+    return pack_codes<BITS>(q);
+}
+
+// Smoothed values of a chunk: the 8 elements at k .. k+7 divided by their
+// smoothing factors sm[0..7] (correctly rounded fp32 quotients).
+template <int DT>
+__device__ __forceinline__ void smooth_chunk(uint4 v, const float (&sm)[8], float (&f)[8])
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = widen_bits<DT>(w[j]) / sm[2 * j];
+        f[2 * j + 1] = widen_bits<DT>(w[j] >> 16) / sm[2 * j + 1];
+    }
+}
+
+// Codes of 8 fp32 values, packed: rint of the correctly rounded quotients by
+// s, through the product with rs = 1 / s and the same near-half fallback as
+// quantize_chunk.  (fp32 values, so the bound on |f / s| is 127.5 again: the
+// scale comes from their own absmax.)
+template <int BITS>
+__device__ __forceinline__ uint2 quantize_values(const float (&f)[8], float s, float rs)
+{
+    float t[8];
+    bool near_half = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        t[e] = f[e] * rs;
+        const float d = t[e] - __builtin_rintf(t[e]);
+        near_half |= __builtin_fabsf(__builtin_fabsf(d) - 0.5f) < 0x1p-14f;
+    }
+    if (near_half) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            t[e] = f[e] / s;
+    }
+    int q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        q[e] = code_of<BITS>(t[e], s);
     return pack_codes<BITS>(q);
 }
 

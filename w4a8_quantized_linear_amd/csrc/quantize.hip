@@ -12,60 +12,161 @@
 // teams of 8 / 16 lanes so a wavefront still covers 512 bytes per load.
 // Rows longer than the register budget take a two-pass kernel that re-reads
 // the row from cache.
+//
+// Inputs are fp16 or bf16 (README feature list: fp16 / bf16 dtype handling),
+// widened exactly.  Activations may carry a SmoothQuant smoothing vector
+// (README: SmoothQuant named as the preprocessing that makes activations
+// quantization-friendly): each element is divided by its channel's factor
+// (correctly rounded fp32 quotient) before the absmax, and the quotients are
+// what gets quantized; the factors are re-read per chunk (cache hits: every
+// row uses the same K factors).
 #include "cider_kernels.h"
 #include "quant_common.h"
 
 namespace cider {
 namespace {
 
-template <int TS, int NCH, int BITS>
+// Smoothing factors of the 8 elements at chunk c (k = 8c .. 8c+7).
+__device__ __forceinline__ void load_smooth(const float *__restrict__ sm, int64_t c, float (&f)[8])
+{
+    const float4 a = *reinterpret_cast<const float4 *>(sm + c * 8);
+    const float4 b = *reinterpret_cast<const float4 *>(sm + c * 8 + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// Magnitude bits of the largest |value| of a chunk.  Without smoothing: the
+// 16-bit elements' own magnitude bits; with it: the fp32 quotients' bits
+// (for finite values both orders are the value order).
+template <int DT, bool SMOOTH>
+__device__ __forceinline__ uint32_t chunk_amax(uint4 v, const float *__restrict__ sm, int64_t c)
+{
+    if constexpr (!SMOOTH) {
+        return chunk_absmax_bits(v);
+    } else {
+        float l[8], f[8];
+        load_smooth(sm, c, l);
+        smooth_chunk<DT>(v, l, f);
+        uint32_t m = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t b = __builtin_bit_cast(uint32_t, f[e]) & 0x7FFFFFFFu;
+            m = b > m ? b : m;
+        }
+        return m;
+    }
+}
+
+template <int DT, bool SMOOTH>
+__device__ __forceinline__ float amax_value(uint32_t bits)
+{
+    if constexpr (SMOOTH)
+        return __builtin_bit_cast(float, bits);
+    else
+        return widen_bits<DT>(bits);
+}
+
+// Codes of a chunk for scale s (rs = 1 / s): the product with rs and the
+// exact near-half fallback when the row's chunks fit in registers (FAST),
+// else a division per value (fewer live registers for long rows).
+template <int BITS, int DT, bool SMOOTH, bool FAST>
+__device__ __forceinline__ uint2 chunk_codes(uint4 v, const float *__restrict__ sm, int64_t c, float s,
+                                             float rs)
+{
+    if constexpr (SMOOTH) {
+        float l[8], f[8];
+        load_smooth(sm, c, l);
+        smooth_chunk<DT>(v, l, f);
+        return quantize_values<BITS>(f, s, rs);
+    } else if constexpr (FAST) {
+        return quantize_chunk<BITS, DT>(v, s, rs);
+    } else {
+        return quantize_chunk_div<BITS, DT>(v, s);
+    }
+}
+
+template <int TS, int NCH, int BITS, int DT, bool SMOOTH, bool STREAM>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__restrict__ x,
                                                             int64_t rows, int64_t len, int64_t ld,
+                                                            const float *__restrict__ smooth,
                                                             uint8_t *__restrict__ out,
                                                             float *__restrict__ scale)
 {
     constexpr int TEAMS = 256 / TS;
     const int lane = threadIdx.x % TS;
-    const int64_t row = (int64_t)blockIdx.x * TEAMS + threadIdx.x / TS;
+    int64_t row = (int64_t)blockIdx.x * TEAMS + threadIdx.x / TS;
     if (row >= rows)
         return;  // a team never straddles a wavefront, so whole teams leave together
-    const uint16_t *xr = x + row * ld;
     const int nch = (int)(len >> 3);
+    // Every load of a row is issued before any is used: a lane past the row
+    // end re-reads the row's last chunk (an address that is always valid) and
+    // its result is masked out, so no branch separates the loads (a branch
+    // would make the compiler wait for each load at the join).
+    auto load_row = [&](uint4 (&d)[NCH], int64_t r) {
+        const uint16_t *xr = x + r * ld;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = min(i * TS + lane, nch - 1);
+            d[i] = *reinterpret_cast<const uint4 *>(xr + (int64_t)c * 8);
+        }
+    };
     uint4 v[NCH];
-    uint32_t amax = 0;
+    load_row(v, row);
+    // STREAM: teams walk the rows with a grid-wide stride, loading the next
+    // row (the last row again at the end: a cache hit, never used) while the
+    // current one is reduced, quantized and stored.
+    const int64_t stride = (int64_t)gridDim.x * TEAMS;
+    for (;;) {
+        const int64_t next = row + stride;  // team-uniform
+        uint4 nv[STREAM ? NCH : 1];
+        if constexpr (STREAM)
+            load_row(nv, min(next, rows - 1));
+        uint32_t amax = 0;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = i * TS + lane;
-        v[i] = c < nch ? *reinterpret_cast<const uint4 *>(xr + (int64_t)c * 8) : uint4{0, 0, 0, 0};
-        const uint32_t m = chunk_absmax_bits(v[i]);
-        amax = m > amax ? m : amax;
-    }
+        for (int i = 0; i < NCH; ++i) {
+            const int c = i * TS + lane;
+            const uint32_t m = chunk_amax<DT, SMOOTH>(v[i], smooth, min(c, nch - 1));
+            amax = (c < nch && m > amax) ? m : amax;
+        }
 #pragma unroll
-    for (int o = TS / 2; o > 0; o >>= 1) {
-        const uint32_t other = (uint32_t)__shfl_xor((int)amax, o, TS);
-        amax = other > amax ? other : amax;
-    }
-    const float s = half_bits_to_float(amax) / quant_divisor<BITS>();
-    if (lane == 0)
-        scale[row] = s;
+        for (int o = TS / 2; o > 0; o >>= 1) {
+            const uint32_t other = (uint32_t)__shfl_xor((int)amax, o, TS);
+            amax = other > amax ? other : amax;
+        }
+        const float s = amax_value<DT, SMOOTH>(amax) / quant_divisor<BITS>();
+        const float rs = 1.0f / s;
+        if (lane == 0)
+            scale[row] = s;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = i * TS + lane;
-        if (c < nch) {
-            const uint2 q = quantize_chunk_div<BITS>(v[i], s);
-            if constexpr (BITS == 8)
-                *reinterpret_cast<uint2 *>(out + row * len + (int64_t)c * 8) = q;
-            else
-                *reinterpret_cast<uint32_t *>(out + row * (len / 2) + (int64_t)c * 4) = q.x;
+        for (int i = 0; i < NCH; ++i) {
+            const int c = i * TS + lane;
+            if (c < nch) {
+                const uint2 q = chunk_codes<BITS, DT, SMOOTH, (NCH <= 8)>(v[i], smooth, c, s, rs);
+                if constexpr (BITS == 8)
+                    *reinterpret_cast<uint2 *>(out + row * len + (int64_t)c * 8) = q;
+                else
+                    *reinterpret_cast<uint32_t *>(out + row * (len / 2) + (int64_t)c * 4) = q.x;
+            }
+        }
+        if constexpr (!STREAM) {
+            break;
+        } else {
+            if (next >= rows)
+                break;
+            row = next;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i)
+                v[i] = nv[i];
         }
     }
 }
 
 // One workgroup per row, any length: absmax pass, then a quantize pass that
 // reads the row again.
-template <int BITS>
+template <int BITS, int DT, bool SMOOTH>
 __global__ __launch_bounds__(256) void quantize_long_rows_kernel(const uint16_t *__restrict__ x,
                                                                  int64_t len, int64_t ld,
+                                                                 const float *__restrict__ smooth,
                                                                  uint8_t *__restrict__ out,
                                                                  float *__restrict__ scale)
 {
@@ -75,7 +176,7 @@ __global__ __launch_bounds__(256) void quantize_long_rows_kernel(const uint16_t 
     const int64_t nch = len >> 3;
     uint32_t amax = 0;
     for (int64_t c = threadIdx.x; c < nch; c += 256) {
-        const uint32_t m = chunk_absmax_bits(*reinterpret_cast<const uint4 *>(xr + c * 8));
+        const uint32_t m = chunk_amax<DT, SMOOTH>(*reinterpret_cast<const uint4 *>(xr + c * 8), smooth, c);
         amax = m > amax ? m : amax;
     }
 #pragma unroll
@@ -90,12 +191,13 @@ __global__ __launch_bounds__(256) void quantize_long_rows_kernel(const uint16_t 
 #pragma unroll
     for (int w = 1; w < 4; ++w)
         amax = red[w] > amax ? red[w] : amax;
-    const float s = half_bits_to_float(amax) / quant_divisor<BITS>();
+    const float s = amax_value<DT, SMOOTH>(amax) / quant_divisor<BITS>();
     const float rs = 1.0f / s;
     if (threadIdx.x == 0)
         scale[row] = s;
     for (int64_t c = threadIdx.x; c < nch; c += 256) {
-        const uint2 q = quantize_chunk<BITS>(*reinterpret_cast<const uint4 *>(xr + c * 8), s, rs);
+        const uint2 q = chunk_codes<BITS, DT, SMOOTH, true>(*reinterpret_cast<const uint4 *>(xr + c * 8),
+                                                            smooth, c, s, rs);
         if constexpr (BITS == 8)
             *reinterpret_cast<uint2 *>(out + row * len + c * 8) = q;
         else
@@ -103,32 +205,60 @@ __global__ __launch_bounds__(256) void quantize_long_rows_kernel(const uint16_t 
     }
 }
 
-template <int TS, int NCH, int BITS>
-hipError_t launch_team(const uint16_t *x, int64_t rows, int64_t len, int64_t ld, void *out,
-                       float *scale, hipStream_t stream)
+int compute_units()
+{
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+constexpr int kStreamBlocksPerCu = 4;
+
+// Short rows (a team's row fits 8 chunks per lane) stream through a grid of
+// kStreamBlocksPerCu workgroups per compute unit when there are more rows
+// than that; other cases take one row per team.
+template <int TS, int NCH, int BITS, int DT, bool SMOOTH>
+hipError_t launch_team(const uint16_t *x, int64_t rows, int64_t len, int64_t ld, const float *smooth,
+                       void *out, float *scale, hipStream_t stream)
 {
     constexpr int TEAMS = 256 / TS;
     const int64_t blocks = (rows + TEAMS - 1) / TEAMS;
-    hipLaunchKernelGGL((quantize_rows_kernel<TS, NCH, BITS>), dim3((unsigned)blocks), dim3(256), 0,
-                       stream, x, rows, len, ld, static_cast<uint8_t *>(out), scale);
+    const int64_t cap = (int64_t)compute_units() * kStreamBlocksPerCu;
+    if (NCH <= 8 && blocks > cap) {
+        hipLaunchKernelGGL((quantize_rows_kernel<TS, NCH, BITS, DT, SMOOTH, (NCH <= 8)>),
+                           dim3((unsigned)cap), dim3(256), 0, stream, x, rows, len, ld, smooth,
+                           static_cast<uint8_t *>(out), scale);
+    } else {
+        hipLaunchKernelGGL((quantize_rows_kernel<TS, NCH, BITS, DT, SMOOTH, false>),
+                           dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, len, ld, smooth,
+                           static_cast<uint8_t *>(out), scale);
+    }
     return hipGetLastError();
 }
 
-template <int BITS>
-hipError_t launch_bits(const uint16_t *x, int64_t rows, int64_t len, int64_t ld, void *out,
-                       float *scale, hipStream_t stream)
+template <int BITS, int DT, bool SMOOTH>
+hipError_t launch_bits(const uint16_t *x, int64_t rows, int64_t len, int64_t ld, const float *smooth,
+                       void *out, float *scale, hipStream_t stream)
 {
     const int64_t nch = len / 8;
     if (nch <= 8)
-        return launch_team<8, 1, BITS>(x, rows, len, ld, out, scale, stream);
+        return launch_team<8, 1, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream);
     if (nch <= 16)
-        return launch_team<16, 1, BITS>(x, rows, len, ld, out, scale, stream);
+        return launch_team<16, 1, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream);
     if (nch <= 32)
-        return launch_team<32, 1, BITS>(x, rows, len, ld, out, scale, stream);
+        return launch_team<32, 1, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream);
     const int64_t per_lane = (nch + 63) / 64;
-#define CIDER_TEAM64(n)                                                                   \
-    if (per_lane <= n)                                                                    \
-        return launch_team<64, n, BITS>(x, rows, len, ld, out, scale, stream);
+#define CIDER_TEAM64(n)                                                                          \
+    if (per_lane <= n)                                                                           \
+        return launch_team<64, n, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream);
     CIDER_TEAM64(1)
     CIDER_TEAM64(2)
     CIDER_TEAM64(3)
@@ -142,20 +272,30 @@ hipError_t launch_bits(const uint16_t *x, int64_t rows, int64_t len, int64_t ld,
     CIDER_TEAM64(20)
     CIDER_TEAM64(24)
 #undef CIDER_TEAM64
-    hipLaunchKernelGGL((quantize_long_rows_kernel<BITS>), dim3((unsigned)rows), dim3(256), 0,
-                       stream, x, len, ld, static_cast<uint8_t *>(out), scale);
+    hipLaunchKernelGGL((quantize_long_rows_kernel<BITS, DT, SMOOTH>), dim3((unsigned)rows), dim3(256),
+                       0, stream, x, len, ld, smooth, static_cast<uint8_t *>(out), scale);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t len, int64_t ld,
-                                int bits, void *out, float *scale, hipStream_t stream)
+hipError_t launch_quantize_rows(const uint16_t *x, int dtype, int64_t rows, int64_t len, int64_t ld,
+                                const float *smooth, int bits, void *out, float *scale,
+                                hipStream_t stream)
 {
     if (rows == 0)
         return hipSuccess;
-    return bits == 8 ? launch_bits<8>(x, rows, len, ld, out, scale, stream)
-                     : launch_bits<4>(x, rows, len, ld, out, scale, stream);
+    if (smooth) {  // activations only: int8 codes
+        if (bits != 8)
+            return hipErrorInvalidValue;
+        return dtype == DT_BF16 ? launch_bits<8, DT_BF16, true>(x, rows, len, ld, smooth, out, scale, stream)
+                                : launch_bits<8, DT_F16, true>(x, rows, len, ld, smooth, out, scale, stream);
+    }
+    if (dtype == DT_BF16)
+        return bits == 8 ? launch_bits<8, DT_BF16, false>(x, rows, len, ld, nullptr, out, scale, stream)
+                         : launch_bits<4, DT_BF16, false>(x, rows, len, ld, nullptr, out, scale, stream);
+    return bits == 8 ? launch_bits<8, DT_F16, false>(x, rows, len, ld, nullptr, out, scale, stream)
+                     : launch_bits<4, DT_F16, false>(x, rows, len, ld, nullptr, out, scale, stream);
 }
 
 }  // namespace cider
