@@ -31,6 +31,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -213,6 +215,48 @@ def weight_quant_bench(torch, cider, si, reps=20):
     return records
 
 
+def dtype_variants_bench(torch, cider, si, steps=50):
+    """The headline layer (W8A8 per channel, N=10240, K=2560, M=4096) for
+    each input / output type with and without SmoothQuant smoothing: time per
+    cider_linear_ex call, calls back to back over rotating copies."""
+    M, N, K = 4096, 10240, 2560
+    x32 = si.activations(M, K).astype(np.float32)
+    x16 = torch.from_numpy(x32.astype(np.float16).view(np.int16)).cuda()
+    xbf = torch.from_numpy(x32).cuda().to(torch.bfloat16).view(torch.int16)
+    w = torch.from_numpy(si.weights(N, K).view(np.int16)).cuda().view(torch.float16)
+    wq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    sw = torch.empty((N,), dtype=torch.float32, device="cuda")
+    cider.cider_quantize_weight(w, N, K, 8, 0, wq, sw)
+    sm = torch.from_numpy(np.random.default_rng(5).uniform(0.5, 8.0, K).astype(np.float32)).cuda()
+    B = copies_for(8, 0, N, K, M)
+    xs = {0: [x16.clone() for _ in range(B)], 1: [xbf.clone() for _ in range(B)]}
+    ys = [torch.empty((M, N), dtype=torch.int16, device="cuda") for _ in range(B)]
+    ws_bytes = cider.cider_linear_workspace_bytes(M, K)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    records = []
+    for x_dt, y_dt, smooth in ((0, 0, False), (1, 1, False), (0, 0, True), (1, 1, True)):
+        def call(i):
+            cider.cider_linear_ex(xs[x_dt][i % B], x_dt, M, K, K, sm if smooth else None, wq, sw,
+                                  N, 8, 0, y_dt, ws, ws_bytes, ys[i % B])
+        for i in range(5):
+            call(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            call(i)
+        e1.record(stream)
+        e1.synchronize()
+        t = e0.elapsed_time(e1) / 1e3 / steps
+        rec = {"x": ("fp16", "bf16")[x_dt], "y": ("fp16", "bf16")[y_dt], "smoothing": smooth,
+               "us_per_call": round(t * 1e6, 2), "tops": round(2.0 * M * N * K / t / 1e12, 1)}
+        records.append(rec)
+        log("linear_ex x=%s y=%s smoothing=%s: %.2f us" % (rec["x"], rec["y"], smooth, t * 1e6))
+    del xs, ys, ws, wq, sw, w
+    torch.cuda.empty_cache()
+    return records
+
+
 class DecoderStack:
     """The layer at model scale: the four W8A8 per-channel linears of each of
     `layers` decoder layers of an 8B-class model (QKV 6144x4096, O 4096x4096,
@@ -326,7 +370,6 @@ def main():
         print("bench.py runs on one GPU only: this layer has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus)
         sys.exit(2)
-    import numpy as np
     import torch
 
     import synth_inputs as si
@@ -426,6 +469,10 @@ def main():
     # ------------------------------------------------------------- sweep ---
     if not args.no_sweep:
         result["sweep"] = sweep(torch, cider, si)
+
+    # ------------------------------------ input / output types, smoothing ---
+    if not args.no_sweep:
+        result["dtype_variants"] = dtype_variants_bench(torch, cider, si)
 
     # ------------------------------------------- offline weight quantization ---
     if not args.no_sweep:

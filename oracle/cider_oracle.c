@@ -492,6 +492,38 @@ int oracle_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                             s_tok, y);
 }
 
+/* ----------------------------------------------------- decode variant --- */
+
+/* The pages' decode kernel (Cider README, "Metal Kernel Pipeline", Decode
+   (M = 1): a direct matrix-vector product that dequantizes the weights on
+   the fly and does not quantize the activation):
+     y[n] = sum_g s_w[n, g] * (sum over k in group g of x[k] * q[n, k])
+   (one group of K for per-channel scales), x fp16 / bf16 [K], evaluated in
+   fp64 and rounded once to y_dtype.  Each product x * q is exact in fp64;
+   the sums are fp64 in k order. */
+int oracle_decode_linear(const uint16_t *x, int x_dtype, int64_t K, const uint8_t *wq,
+                         const float *s_w, int bits, int64_t N, int group_size, int y_dtype,
+                         uint16_t *y)
+{
+    if (!x || !wq || !s_w || !y || N < 0 || !shape_ok(K, bits, group_size) ||
+        !dtype_ok(x_dtype) || !dtype_ok(y_dtype))
+        return ORACLE_BAD_ARG;
+    int64_t gs = group_size ? group_size : K;
+    int64_t G = K / gs;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double t = 0.0;
+        for (int64_t g = 0; g < G; ++g) {
+            double a = 0.0;
+            for (int64_t k = g * gs; k < (g + 1) * gs; ++k)
+                a += (double)widen(x[k], x_dtype) * (double)weight_code(wq, bits, K, n, k);
+            t += (double)s_w[n * G + g] * a;
+        }
+        y[n] = narrow(t, y_dtype);
+    }
+    return ORACLE_OK;
+}
+
 /* Threads the OpenMP loops above use. */
 int oracle_num_threads(void)
 {

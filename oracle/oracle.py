@@ -78,6 +78,7 @@ class Oracle:
         L.oracle_smooth_fold_weight.argtypes = [P, I, I64, I64, P, P]
         L.oracle_dequant_ex.argtypes = [P, P, P, I64, I64, I64, I, P]
         L.oracle_linear_ex.argtypes = [P, I, I64, I64, I64, P, P, P, I, I64, I, I, P, P, P]
+        L.oracle_decode_linear.argtypes = [P, I, I64, P, P, I, I64, I, I, P]
         L.oracle_gemm_acc.argtypes = [P, P, I, I64, I64, I64, I, P]
         L.oracle_dequant.argtypes = [P, P, P, I64, I64, I64, P]
         L.oracle_linear.argtypes = [P, I64, I64, I64, P, P, I, I64, I, P, P, P]
@@ -85,7 +86,7 @@ class Oracle:
                   "oracle_dequant", "oracle_linear", "oracle_num_threads",
                   "oracle_quantize_weight_clipped", "oracle_quantize_act_ex",
                   "oracle_quantize_weight_ex", "oracle_smooth_fold_weight", "oracle_dequant_ex",
-                  "oracle_linear_ex"):
+                  "oracle_linear_ex", "oracle_decode_linear"):
             getattr(L, f).restype = ctypes.c_int
 
     @staticmethod
@@ -180,6 +181,20 @@ class Oracle:
                                               bits, N, group_size, y_dtype, _ptr(xq), _ptr(st),
                                               _ptr(y)), "linear_ex")
         return y, xq, st
+
+    def decode_linear(self, xbits: np.ndarray, x_dtype: int, wq: np.ndarray, s_w: np.ndarray,
+                      bits: int = 8, group_size: int = 0, y_dtype: int = 0) -> np.ndarray:
+        """The decode variant: fp16 / bf16 x [K] against dequantized weights,
+        no activation quantization.  Returns uint16 patterns [N]."""
+        xb = _half_bits(np.ascontiguousarray(xbits).reshape(-1))
+        K = xb.size
+        wq = np.ascontiguousarray(wq)
+        N = wq.shape[0]
+        sw = np.ascontiguousarray(s_w, dtype=np.float32)
+        y = np.empty((N,), np.uint16)
+        self._check(self.lib.oracle_decode_linear(_ptr(xb), x_dtype, K, _ptr(wq), _ptr(sw), bits, N,
+                                                  group_size, y_dtype, _ptr(y)), "decode_linear")
+        return y
 
     def quantize_act(self, x: np.ndarray, K: int | None = None):
         """x: fp16 [M, ldx]; quantizes the first K (default: all) columns of

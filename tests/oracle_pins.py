@@ -483,6 +483,70 @@ def pin_smoothing_improves_outlier_workload(orc):
     assert e1 < 0.6 * e0, (e0, e1)
 
 
+# ------------------------------------------------------ decode variant ---
+
+def pin_decode_one_hot_and_exact(orc):
+    """Decode variant, closed forms.  A one-hot x = c e_j picks one weight:
+    y[n] = fp16(c * q[n, j] * s_w[n, g(j)]).  With scales that are powers of
+    two and x of small dyadic values every partial sum is exact in fp64, so
+    y is the exactly rounded dot product numpy computes in float64."""
+    from synth_inputs import weights
+    rng = np.random.default_rng(41)
+    K, N = 512, 48
+    w = weights(N, K, seed=41)
+    for bits, gs in ((8, 0), (8, 64), (4, 0), (4, 128)):
+        wq, sw = orc.quantize_weight(w, bits, gs)
+        codes = wq.astype(np.int64) if bits == 8 else _unpack4(wq)
+        L = K if gs == 0 else gs
+        swf = np.asarray(sw, np.float64).reshape(N, -1)
+        for j in (0, 5, 200, K - 1):
+            x = np.zeros(K, np.float16)
+            x[j] = np.float16(1.5)
+            y = orc.decode_linear(x, 0, wq, sw, bits, gs).view(np.float16)
+            ref = (1.5 * codes[:, j] * swf[:, j // L]).astype(np.float16)
+            assert np.array_equal(y, ref), (bits, gs, j)
+    # power-of-two scales: w = q * 2^-e per row / group
+    q = rng.integers(-127, 128, size=(N, K))
+    q[:, 0] = 127
+    e = rng.integers(6, 10, size=(N, 1))
+    w2 = _f16(q * 2.0 ** -e)
+    wq, sw = orc.quantize_weight(w2, 8, 0)
+    assert np.array_equal(sw, (127 * 2.0 ** -e[:, 0] / 127).astype(np.float32))
+    x = _f16(rng.integers(-64, 65, K) / 16.0)
+    y = orc.decode_linear(x, 0, wq, sw, 8, 0).view(np.float16)
+    ref = (wq.astype(np.float64) * sw.astype(np.float64)[:, None]) @ x.astype(np.float64)
+    assert np.array_equal(y, ref.astype(np.float16))
+
+
+def pin_decode_nearest_rational(orc):
+    """Decode variant on random tiny inputs: every output is the fp16 value
+    nearest to the exact rational result (Python fractions), per channel and
+    per group, int8 and int4, fp16 and bf16 activations."""
+    from fractions import Fraction
+    from synth_inputs import activations, weights
+    K, N = 128, 6
+    x = activations(1, K, seed=43)[0]
+    xb16 = _torch_bf16_bits(x.astype(np.float32))
+    w = weights(N, K, seed=43)
+    for bits, gs in ((8, 0), (8, 64), (4, 0), (4, 64)):
+        wq, sw = orc.quantize_weight(w, bits, gs)
+        codes = wq.astype(np.int64) if bits == 8 else _unpack4(wq)
+        L = K if gs == 0 else gs
+        swf = np.asarray(sw, np.float32).reshape(N, -1)
+        for xd, xbits in ((0, x.view(np.uint16)), (1, xb16)):
+            xv = [Fraction(float(v)) for v in (x.astype(np.float64) if xd == 0 else
+                                              (xb16.astype(np.uint32) << 16).view(np.float32))]
+            y = orc.decode_linear(xbits, xd, wq, sw, bits, gs).view(np.float16)
+            for n in range(N):
+                exact = sum(Fraction(float(swf[n, g])) *
+                            sum(xv[k] * int(codes[n, k]) for k in range(g * L, (g + 1) * L))
+                            for g in range(K // L))
+                got = Fraction(float(y[n]))
+                up = Fraction(float(np.nextafter(y[n], np.float16(np.inf))))
+                dn = Fraction(float(np.nextafter(y[n], np.float16(-np.inf))))
+                assert abs(got - exact) <= abs(up - exact) and abs(got - exact) <= abs(dn - exact)
+
+
 # ---------------------------------------------------------- accumulation ---
 
 def _brute_acc(xq, wcodes, gs):

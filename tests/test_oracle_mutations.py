@@ -54,6 +54,10 @@ MUTATIONS = {
     "bf16_encode_ties_away": ("double m = nearbyint(ldexp(a, -q));           /* count of quanta, ties to even */\n    if (q == -133)",
                               "double m = round(ldexp(a, -q));\n    if (q == -133)"),
     "bf16_encode_bias": ("((q + 134) << 7)", "((q + 133) << 7)"),
+    "decode_group_scale_index": ("t += (double)s_w[n * G + g] * a;", "t += (double)s_w[n * G] * a;"),
+    "decode_quantizes_nothing_wrong_sign": ("a += (double)widen(x[k], x_dtype) * (double)weight_code(wq, bits, K, n, k);",
+                                           "a += (double)widen(x[k], x_dtype) * (double)abs(weight_code(wq, bits, K, n, k));"),
+    "decode_x_dtype_ignored": ("a += (double)widen(x[k], x_dtype)", "a += (double)widen(x[k], DT_F16)"),
     "output_dtype_ignored": ("narrow(dequant_value(s_tok[m], s_w + n * G, acc + (m * N + n) * G, G),\n                                  y_dtype);",
                              "narrow(dequant_value(s_tok[m], s_w + n * G, acc + (m * N + n) * G, G),\n                                  DT_F16);"),
     "dequant_via_float": ("return (double)s_tok * t;",
