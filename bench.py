@@ -257,6 +257,41 @@ def dtype_variants_bench(torch, cider, si, steps=50):
     return records
 
 
+def decode_bench(torch, cider, si):
+    """The pages' decode variant (dequantized weights, no activation
+    quantization) on the one-token operator shapes: time per call (HIP graph
+    of back-to-back calls over rotating copies) and the algorithmic bytes
+    (x, weight codes, scales, y) per second against 8 TB/s."""
+    records = []
+    for name, bits, gs, N, K in (("w8a16_pc", 8, 0, 10240, 2560), ("w4a16_pc", 4, 0, 10240, 2560),
+                                 ("w8a16_pg64", 8, 64, 2560, 10240), ("w8a16_pg128", 8, 128, 2560, 10240),
+                                 ("w4a16_pg64", 4, 64, 2560, 10240), ("w4a16_pg128", 4, 128, 2560, 10240)):
+        x = torch.from_numpy(si.activations(1, K)[0].view(np.int16)).cuda().view(torch.float16)
+        w = torch.from_numpy(si.weights(N, K).view(np.int16)).cuda().view(torch.float16)
+        G = 1 if gs == 0 else K // gs
+        B = copies_for(bits, gs, N, K, 1)
+        sets = []
+        for _ in range(B):
+            wq = torch.empty((N, K) if bits == 8 else (N, K // 2),
+                             dtype=torch.int8 if bits == 8 else torch.uint8, device="cuda")
+            sw = torch.empty((N,) if gs == 0 else (N, G), dtype=torch.float32, device="cuda")
+            cider.cider_quantize_weight(w, N, K, bits, gs, wq, sw)
+            sets.append((x.clone(), wq, sw, torch.empty((N,), dtype=torch.float16, device="cuda")))
+
+        def call(i):
+            xx, wq, sw, y = sets[i % B]
+            cider.cider_decode_linear(xx, K, wq, sw, N, bits, gs, 0, y)
+        t = graph_time(torch, call, B, max(1, 4000 // B))
+        nbytes = 2 * K + (N * K if bits == 8 else N * K // 2) + 4 * N * G + 2 * N
+        rec = {"workload": name, "N": N, "K": K, "us_per_call": round(t * 1e6, 3),
+               "gbps": round(nbytes / t / 1e9, 1), "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4)}
+        records.append(rec)
+        log("decode %s N=%d K=%d: %.2f us, %.0f GB/s" % (name, N, K, t * 1e6, nbytes / t / 1e9))
+        del sets, x, w
+        torch.cuda.empty_cache()
+    return records
+
+
 class DecoderStack:
     """The layer at model scale: the four W8A8 per-channel linears of each of
     `layers` decoder layers of an 8B-class model (QKV 6144x4096, O 4096x4096,
@@ -469,6 +504,10 @@ def main():
     # ------------------------------------------------------------- sweep ---
     if not args.no_sweep:
         result["sweep"] = sweep(torch, cider, si)
+
+    # ------------------------------------------------- the decode variant ---
+    if not args.no_sweep:
+        result["decode"] = decode_bench(torch, cider, si)
 
     # ------------------------------------ input / output types, smoothing ---
     if not args.no_sweep:

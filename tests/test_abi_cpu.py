@@ -171,6 +171,18 @@ def test_dtype_and_smoothing_argument_codes():
               check=False) == cider.CIDER_ERR_INVALID_ARG
 
 
+def test_decode_argument_codes():
+    dl = cider.cider_decode_linear
+    assert dl(P, 1024, P2, P3, 100, 8, 0, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert dl(P, 32768, P2, P3, 64, 4, 128, 1, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert dl(P, 32768, P2, P3, 64, 8, 0, 0, P, stream=0, check=False) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
+    assert dl(P, 1000, P2, P3, 64, 8, 0, 0, P, stream=0, check=False) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
+    assert dl(P, 1024, P2, P3, 64, 8, 32, 0, P, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    assert dl(P, 1024, P2, P3, 64, 8, 0, 3, P, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    assert dl(BAD, 1024, P2, P3, 64, 8, 0, 0, P, stream=0, check=False) == cider.CIDER_ERR_MISALIGNED
+    assert dl(P, 1024, P2, P3, 0, 8, 0, 0, None, stream=0, check=False) == cider.CIDER_OK
+
+
 def test_linear_argument_codes():
     f = cider.cider_w8a8_linear
     ws = cider.cider_linear_workspace_bytes(16, 256)

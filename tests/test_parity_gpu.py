@@ -288,6 +288,43 @@ def test_linear_ex_whole_path(M, N, K, ldx, x_dtype, y_dtype, smooth, bits, gs):
     gu.assert_out_close(gu.bits_to_host(y), ref, y_dtype, "linear_ex M=%d" % M)
 
 
+# ------------------------------------------------------- decode variant ---
+
+DECODE_SHAPES = [(512, 1024), (10240, 2560), (2560, 10240), (100, 640), (64, 16384), (3, 64)]
+
+
+@pytest.mark.parametrize("y_dtype", [0, 1])
+@pytest.mark.parametrize("bits,gs", MODES, ids=MODE_IDS)
+@pytest.mark.parametrize("N,K", DECODE_SHAPES + [(64, 32768)])
+def test_decode_linear(N, K, bits, gs, y_dtype):
+    """The decode variant (dequantized weights, fp16 activation as is) against
+    the oracle's fp64 evaluation.  The kernel sums in fp32, so the bound adds
+    2^-16 of the sum of |terms| to the usual output tolerance (the fp32
+    summation error of at most ~100 sequential additions is below 2^-17 of it)."""
+    if gs and K % gs:
+        pytest.skip("K not a multiple of the group size")
+    if bits == 8 and K > 16384:
+        pytest.skip("int8 decode envelope: K <= 16384")
+    import torch
+    orc = get_oracle()
+    x = si.activations(1, K, seed=N + K)[0]
+    w = si.weights(N, K, seed=N)
+    wq, sw = orc.quantize_weight(w, bits, gs)
+    y = gu.empty((N,), torch.int16)
+    cider.cider_decode_linear(gu.to_dev(x), K, gu.to_dev(wq), gu.to_dev(sw), N, bits, gs, y_dtype, y)
+    ref = orc.decode_linear(x, 0, wq, sw, bits, gs, y_dtype)
+    codes = wq.astype(np.float64) if bits == 8 else gu.unpack_int4(wq).astype(np.float64)
+    L = K if gs == 0 else gs
+    swf = np.repeat(np.asarray(sw, np.float64).reshape(N, -1), L, axis=1)
+    S = (np.abs(codes) * swf) @ np.abs(x.astype(np.float64))
+    got = gu.bits_to_f64(gu.bits_to_host(y), y_dtype)
+    r = gu.bits_to_f64(ref, y_dtype)
+    bound = 1e-3 + (2.0 ** -10 if y_dtype == 0 else 2.0 ** -7) * np.abs(r) + 2.0 ** -16 * S
+    err = np.abs(got - r)
+    assert np.all(np.isfinite(got)) and np.all(err <= bound), (
+        "%d of %d outside, worst ratio %.3g" % (int((err > bound).sum()), N, float((err / bound).max())))
+
+
 # ----------------------------------------------------------------- product ---
 
 PRODUCT_SHAPES = [(64, 512, 1024), (300, 320, 1024), (700, 576, 512), (513, 1024, 2560),

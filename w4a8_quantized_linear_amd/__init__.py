@@ -33,7 +33,7 @@ EXPORTS = (
     "cider_w8a8_gemm", "cider_w4a8_gemm", "cider_w8a8_gemm_i32", "cider_w4a8_gemm_i32",
     "cider_linear_workspace_bytes", "cider_w8a8_linear", "cider_w4a8_linear", "cider_set_path",
     "cider_quantize_weight_clipped", "cider_quantize_weight_ex", "cider_smooth_fold_weight",
-    "cider_quantize_act_ex", "cider_gemm_ex", "cider_linear_ex",
+    "cider_quantize_act_ex", "cider_gemm_ex", "cider_linear_ex", "cider_decode_linear",
 )
 
 CIDER_DTYPE_F16 = 0
@@ -73,6 +73,7 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         "cider_quantize_act_ex": ([P, I, I64, I64, I64, P, P, P, P], I),
         "cider_gemm_ex": ([P, P, P, P, I64, I64, I64, I, I, I, P, P], I),
         "cider_linear_ex": ([P, I, I64, I64, I64, P, P, P, I64, I, I, I, P, SZ, P, P], I),
+        "cider_decode_linear": ([P, I64, P, P, I64, I, I, I, P, P], I),
         "cider_w8a8_gemm": ([P, P, P, P, I64, I64, I64, I, P, P], I),
         "cider_w4a8_gemm": ([P, P, P, P, I64, I64, I64, I, P, P], I),
         "cider_w8a8_gemm_i32": ([P, P, I64, I64, I64, I, P, P], I),
@@ -170,6 +171,13 @@ def cider_linear_ex(x, x_dtype, M, K, ldx, smooth, wq, s_w, N, bits, group_size,
                                 N, bits, group_size, y_dtype, _ptr(workspace), workspace_bytes,
                                 _ptr(y), _stream(stream))
     return _ret(st, "cider_linear_ex", check)
+
+
+def cider_decode_linear(x_f16, K, wq, s_w, N, bits, group_size, y_dtype, y, stream=None,
+                        check=True):
+    st = load().cider_decode_linear(_ptr(x_f16), K, _ptr(wq), _ptr(s_w), N, bits, group_size,
+                                    y_dtype, _ptr(y), _stream(stream))
+    return _ret(st, "cider_decode_linear", check)
 
 
 def cider_quantize_act(x_f16, M, K, ldx, xq, s_tok, stream=None, check=True):

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libcider.so")
-SOURCES = ["api.hip", "quantize.hip", "clip.hip", "smooth.hip", "gemm.hip", "gemm_skinny.hip", "gemv.hip"]
+SOURCES = ["api.hip", "quantize.hip", "clip.hip", "smooth.hip", "decode.hip", "gemm.hip", "gemm_skinny.hip", "gemv.hip"]
 HEADERS = ["cider_kernels.h", "quant_common.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -18,6 +18,8 @@ namespace {
 constexpr int64_t kMaxK = 133144;       // K * 127^2 < 2^31
 constexpr int64_t kGemvMaxBytes = 32768;  // M * K int8 codes held in LDS
 constexpr int64_t kMaxOperandBytes = int64_t(1) << 31;
+constexpr int64_t kDecodeMaxK8 = 16384;   // decode kernel: chunks per lane held twice in registers
+constexpr int64_t kDecodeMaxK4 = 32768;
 
 std::atomic<int> g_path{0};
 
@@ -394,6 +396,31 @@ cider_status cider_linear_ex(const void *x, int x_dtype, int64_t M, int64_t K, i
 {
     return run_linear(x, x_dtype, M, K, ldx, smooth, wq, s_w, N, bits, group_size, y_dtype,
                       workspace, workspace_bytes, y, stream);
+}
+
+cider_status cider_decode_linear(const void *x_f16, int64_t K, const void *wq, const float *s_w,
+                                 int64_t N, int bits, int group_size, int y_dtype, void *y,
+                                 void *stream)
+{
+    if (N < 0 || K <= 0 || (bits != 8 && bits != 4) || !dtype_ok(y_dtype))
+        return CIDER_ERR_INVALID_ARG;
+    if (group_size != 0 && group_size != 64 && group_size != 128)
+        return CIDER_ERR_INVALID_ARG;
+    if (K % 64 != 0 || K > (bits == 8 ? kDecodeMaxK8 : kDecodeMaxK4) ||
+        (group_size && K % group_size != 0))
+        return CIDER_ERR_UNSUPPORTED_SHAPE;
+    if (N == 0)
+        return CIDER_OK;
+    if (!x_f16 || !wq || !s_w || !y)
+        return CIDER_ERR_INVALID_ARG;
+    if (!aligned16(x_f16) || !aligned16(wq) || (reinterpret_cast<uintptr_t>(s_w) & 3u) ||
+        (reinterpret_cast<uintptr_t>(y) & 1u))
+        return CIDER_ERR_MISALIGNED;
+    if (!device_usable())
+        return CIDER_ERR_NO_DEVICE;
+    return from_hip(cider::launch_decode(static_cast<const uint16_t *>(x_f16), K, wq, s_w, N, bits,
+                                         group_size, out_kind_of(y_dtype), y,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int cider_set_path(int path)

@@ -78,4 +78,10 @@ hipError_t launch_gemv_fused(const uint16_t *x, int64_t K, const void *wq, const
                              int64_t N, int bits, int group_size, void *y, int8_t *xq_out,
                              float *s_tok_out, int out_kind, hipStream_t stream);
 
+// The decode variant (no activation quantization): y [N] = fp16 / bf16 of
+// sum_g s_w[n, g] * sum_{k in g} x[k] * q[n, k], x fp16 [K] (16-byte aligned),
+// K % 64 == 0, K <= 16384 (int8) or 32768 (int4).
+hipError_t launch_decode(const uint16_t *x, int64_t K, const void *wq, const float *s_w, int64_t N,
+                         int bits, int group_size, int out_kind, void *y, hipStream_t stream);
+
 }  // namespace cider
