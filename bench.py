@@ -292,6 +292,40 @@ def decode_bench(torch, cider, si):
     return records
 
 
+def small_m_bench(torch, cider, si):
+    """Few tokens (M = 2 .. 64), the pages' small-tile regime: whole-layer
+    time per call on each operator shape, through the automatic path and,
+    where it applies (M <= 8, M * K <= 32768), forced onto the matrix-vector
+    kernel."""
+    records = []
+    for name, wl in si.WORKLOADS.items():
+        if name == "w8a8_pc_small":
+            continue
+        Nw, Kw = wl["N"], wl["K"]
+        xs = si.activations(64, Kw)
+        ws = si.weights(Nw, Kw)
+        for gs in wl["group_sizes"]:
+            for Mw in (2, 4, 8, 16, 32, 64):
+                Bw = copies_for(wl["bits"], gs, Nw, Kw, Mw)
+                Lw = Layer(torch, cider, wl["bits"], gs, Nw, Kw, Mw, xs[:Mw], ws, Bw)
+                calls = max(Bw, 8)
+                rec = {"workload": name, "group_size": gs, "M": Mw}
+                paths = [("auto", cider.PATH_AUTO)]
+                if Mw <= 8 and Mw * Kw <= 32768:
+                    paths.append(("matrix_vector", cider.PATH_GEMV))
+                for pname, path in paths:
+                    cider.cider_set_path(path)
+                    t = graph_time(torch, Lw.linear, calls, max(1, 400 // calls))
+                    rec[pname + "_us"] = round(t * 1e6, 2)
+                cider.cider_set_path(cider.PATH_AUTO)
+                records.append(rec)
+                log("small M %s gs=%d M=%d: %s" % (name, gs, Mw, ", ".join(
+                    "%s %.2f us" % (k[:-3], v) for k, v in rec.items() if k.endswith("_us"))))
+                del Lw
+                torch.cuda.empty_cache()
+    return records
+
+
 class DecoderStack:
     """The layer at model scale: the four W8A8 per-channel linears of each of
     `layers` decoder layers of an 8B-class model (QKV 6144x4096, O 4096x4096,
@@ -508,6 +542,10 @@ def main():
     # ------------------------------------------------- the decode variant ---
     if not args.no_sweep:
         result["decode"] = decode_bench(torch, cider, si)
+
+    # ------------------------------------------------------ few tokens ---
+    if not args.no_sweep:
+        result["small_m"] = small_m_bench(torch, cider, si)
 
     # ------------------------------------ input / output types, smoothing ---
     if not args.no_sweep:

@@ -159,7 +159,8 @@ cider_status cider_quantize_act(const void *x_f16, int64_t M, int64_t K, int64_t
    Pipeline", step matmul_fused_dequant; "TensorOps matmul2d"; "W8A8
    Quantization Granularity").  group_size 0: per-channel s_w [N];
    64 / 128: per-group s_w [N, K/gs].  y: fp16 [M, N].
-   M = 1 runs the matrix-vector kernel, larger M the matrix-core kernel. */
+   Up to 8 tokens (M * K <= 32768) run the matrix-vector kernel, more the
+   matrix-core kernel. */
 cider_status cider_w8a8_gemm(const int8_t *xq, const float *s_tok, const int8_t *wq,
                              const float *s_w, int64_t M, int64_t N, int64_t K,
                              int group_size, void *y_f16, void *stream);
@@ -229,7 +230,8 @@ cider_status cider_decode_linear(const void *x_f16, int64_t K, const void *wq, c
                                  void *stream);
 
 /* Test hook: force the product path for subsequent calls in this process.
-   0 = automatic (M = 1 with K <= 32768 -> matrix-vector, else matrix cores),
+   0 = automatic (M <= 8 with M * K <= 32768 -> matrix-vector, else matrix
+   cores),
    1 = always the matrix-vector kernel (calls with M > 8 or M * K > 32768 then
    return CIDER_ERR_UNSUPPORTED_SHAPE), 2 = always the matrix-core kernel.
    Returns the previous setting, or -1 for an invalid value. */

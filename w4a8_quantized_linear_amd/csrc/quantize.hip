@@ -85,7 +85,7 @@ __device__ __forceinline__ uint2 chunk_codes(uint4 v, const float *__restrict__ 
     }
 }
 
-template <int TS, int NCH, int BITS, int DT, bool SMOOTH, bool STREAM>
+template <int TS, int NCH, int BITS, int DT, bool SMOOTH>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__restrict__ x,
                                                             int64_t rows, int64_t len, int64_t ld,
                                                             const float *__restrict__ smooth,
@@ -94,69 +94,46 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__re
 {
     constexpr int TEAMS = 256 / TS;
     const int lane = threadIdx.x % TS;
-    int64_t row = (int64_t)blockIdx.x * TEAMS + threadIdx.x / TS;
+    const int64_t row = (int64_t)blockIdx.x * TEAMS + threadIdx.x / TS;
     if (row >= rows)
         return;  // a team never straddles a wavefront, so whole teams leave together
+    const uint16_t *xr = x + row * ld;
     const int nch = (int)(len >> 3);
-    // Every load of a row is issued before any is used: a lane past the row
-    // end re-reads the row's last chunk (an address that is always valid) and
-    // its result is masked out, so no branch separates the loads (a branch
-    // would make the compiler wait for each load at the join).
-    auto load_row = [&](uint4 (&d)[NCH], int64_t r) {
-        const uint16_t *xr = x + r * ld;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = min(i * TS + lane, nch - 1);
-            d[i] = *reinterpret_cast<const uint4 *>(xr + (int64_t)c * 8);
-        }
-    };
+    // Every load is issued before any is used: a lane past the row end
+    // re-reads the row's last chunk (an address that is always valid) and its
+    // result is masked out, so no branch separates the loads (a branch would
+    // make the compiler wait for each load at the join).
     uint4 v[NCH];
-    load_row(v, row);
-    // STREAM: teams walk the rows with a grid-wide stride, loading the next
-    // row (the last row again at the end: a cache hit, never used) while the
-    // current one is reduced, quantized and stored.
-    const int64_t stride = (int64_t)gridDim.x * TEAMS;
-    for (;;) {
-        const int64_t next = row + stride;  // team-uniform
-        uint4 nv[STREAM ? NCH : 1];
-        if constexpr (STREAM)
-            load_row(nv, min(next, rows - 1));
-        uint32_t amax = 0;
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = i * TS + lane;
-            const uint32_t m = chunk_amax<DT, SMOOTH>(v[i], smooth, min(c, nch - 1));
-            amax = (c < nch && m > amax) ? m : amax;
-        }
+    for (int i = 0; i < NCH; ++i) {
+        const int c = min(i * TS + lane, nch - 1);
+        v[i] = *reinterpret_cast<const uint4 *>(xr + (int64_t)c * 8);
+    }
+    uint32_t amax = 0;
 #pragma unroll
-        for (int o = TS / 2; o > 0; o >>= 1) {
-            const uint32_t other = (uint32_t)__shfl_xor((int)amax, o, TS);
-            amax = other > amax ? other : amax;
-        }
-        const float s = amax_value<DT, SMOOTH>(amax) / quant_divisor<BITS>();
-        const float rs = 1.0f / s;
-        if (lane == 0)
-            scale[row] = s;
+    for (int i = 0; i < NCH; ++i) {
+        const int c = i * TS + lane;
+        const uint32_t m = chunk_amax<DT, SMOOTH>(v[i], smooth, min(c, nch - 1));
+        amax = (c < nch && m > amax) ? m : amax;
+    }
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = i * TS + lane;
-            if (c < nch) {
-                const uint2 q = chunk_codes<BITS, DT, SMOOTH, (NCH <= 8)>(v[i], smooth, c, s, rs);
-                if constexpr (BITS == 8)
-                    *reinterpret_cast<uint2 *>(out + row * len + (int64_t)c * 8) = q;
-                else
-                    *reinterpret_cast<uint32_t *>(out + row * (len / 2) + (int64_t)c * 4) = q.x;
-            }
-        }
-        if constexpr (!STREAM) {
-            break;
-        } else {
-            if (next >= rows)
-                break;
-            row = next;
+    for (int o = TS / 2; o > 0; o >>= 1) {
+        const uint32_t other = (uint32_t)__shfl_xor((int)amax, o, TS);
+        amax = other > amax ? other : amax;
+    }
+    const float s = amax_value<DT, SMOOTH>(amax) / quant_divisor<BITS>();
+    const float rs = 1.0f / s;
+    if (lane == 0)
+        scale[row] = s;
 #pragma unroll
-            for (int i = 0; i < NCH; ++i)
-                v[i] = nv[i];
+    for (int i = 0; i < NCH; ++i) {
+        const int c = i * TS + lane;
+        if (c < nch) {
+            const uint2 q = chunk_codes<BITS, DT, SMOOTH, (NCH <= 8)>(v[i], smooth, c, s, rs);
+            if constexpr (BITS == 8)
+                *reinterpret_cast<uint2 *>(out + row * len + (int64_t)c * 8) = q;
+            else
+                *reinterpret_cast<uint32_t *>(out + row * (len / 2) + (int64_t)c * 4) = q.x;
         }
     }
 }
@@ -205,42 +182,15 @@ __global__ __launch_bounds__(256) void quantize_long_rows_kernel(const uint16_t 
     }
 }
 
-int compute_units()
-{
-    static int cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 256;
-    if (!cached[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
-constexpr int kStreamBlocksPerCu = 4;
-
-// Short rows (a team's row fits 8 chunks per lane) stream through a grid of
-// kStreamBlocksPerCu workgroups per compute unit when there are more rows
-// than that; other cases take one row per team.
 template <int TS, int NCH, int BITS, int DT, bool SMOOTH>
 hipError_t launch_team(const uint16_t *x, int64_t rows, int64_t len, int64_t ld, const float *smooth,
                        void *out, float *scale, hipStream_t stream)
 {
     constexpr int TEAMS = 256 / TS;
     const int64_t blocks = (rows + TEAMS - 1) / TEAMS;
-    const int64_t cap = (int64_t)compute_units() * kStreamBlocksPerCu;
-    if (NCH <= 8 && blocks > cap) {
-        hipLaunchKernelGGL((quantize_rows_kernel<TS, NCH, BITS, DT, SMOOTH, (NCH <= 8)>),
-                           dim3((unsigned)cap), dim3(256), 0, stream, x, rows, len, ld, smooth,
-                           static_cast<uint8_t *>(out), scale);
-    } else {
-        hipLaunchKernelGGL((quantize_rows_kernel<TS, NCH, BITS, DT, SMOOTH, false>),
-                           dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, len, ld, smooth,
-                           static_cast<uint8_t *>(out), scale);
-    }
+    hipLaunchKernelGGL((quantize_rows_kernel<TS, NCH, BITS, DT, SMOOTH>), dim3((unsigned)blocks),
+                       dim3(256), 0, stream, x, rows, len, ld, smooth, static_cast<uint8_t *>(out),
+                       scale);
     return hipGetLastError();
 }
 
