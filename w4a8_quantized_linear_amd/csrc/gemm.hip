@@ -11,17 +11,18 @@
 //     of one token); per group the roles swap (a lane's outputs are 16
 //     tokens of one channel, so each group needs one scale per lane and
 //     32-channel block).  A wavefront owns WN x WM outputs.
-//   * K advances 64 bytes per tile.  Tiles go from HBM to LDS with
+//   * K advances BK bytes per tile (64; 128 or 256 for few tokens).  Tiles go
+//     from HBM to LDS with
 //     buffer_load_dwordx4 ... lds (no registers involved) through a ring of
 //     STAGES LDS stages, so STAGES - 1 tiles of copies are in flight while
 //     the matrix cores work; a tile's copies are awaited with a counted
 //     vmcnt, not a full drain.  Per group, the tile's channel scales of its
 //     group travel the same way (buffer_load_dword ... lds).
-//   * Each 64-deep tile is two 32-deep matrix-core steps.  The fragments of
-//     the next step are read from LDS while the current step's MFMAs run
-//     (two register sets, reads interleaved between MFMAs).  The one
-//     barrier per tile sits between the two steps, where the queued MFMAs
-//     cover it; right after it the stage just consumed is refilled.
+//   * Each tile is BK / 32 matrix-core steps of 32.  The fragments of the
+//     next step are read from LDS while the current step's MFMAs run (two
+//     register sets, reads interleaved between MFMAs).  The one barrier per
+//     tile sits before the last step, where the queued MFMAs cover it; the
+//     stage consumed by the previous tile is refilled around it.
 //   * Per group, a group's first MFMA starts from zero and, once its last
 //     K tile is multiplied, its int32 sums are scaled into fp32 accumulators.
 //   * int8 tiles: rows of 64 bytes, 16-byte chunk c of row r at slot
@@ -378,17 +379,20 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // The dequant scales of this tile's channels and tokens, staged in LDS at
-    // the start (plain loads whose latency hides under the prologue copies);
-    // indices are clamped into range, values past the edge are never used.
-    if constexpr (OUT != OUT_I32) {
-        constexpr int TSW = PG ? 0 : TN;  // per group, channel scales come with the tiles
-        for (int t = threadIdx.x; t < TSW + TM; t += NW * 64) {
-            if (t < TSW)
-                s_sw[t] = args.s_w[min(n0 + t, N - 1)];
-            else
-                s_st[t - TSW] = args.s_tok[min(m0 + (t - TSW), M - 1)];
-        }
+    // The dequant scales of this tile's channels and tokens go into registers
+    // now (branch-free loads whose latency hides under the main loop) and
+    // into LDS only before the epilogue: storing them to LDS here would make
+    // every wave wait for them before it issues its first copy.  Indices are
+    // clamped into range; values past the edge are never used.
+    constexpr int TSW = PG ? 0 : TN;  // per group, channel scales come with the tiles
+    constexpr int NSC = OUT != OUT_I32 ? (TSW + TM + NW * 64 - 1) / (NW * 64) : 0;
+    float scv[NSC > 0 ? NSC : 1];
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) {
+        const int t = (int)threadIdx.x + i * NW * 64;
+        const float *src = t < TSW ? args.s_w + min(n0 + t, N - 1)
+                                   : args.s_tok + min(m0 + min(t - TSW, TM - 1), M - 1);
+        scv[i] = *src;
     }
 
     // Ring of STAGES stages.  Tile kt is computed from stage kt % STAGES;
@@ -399,7 +403,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     // of the ring.  (When K has fewer than STAGES - 1 tiles, the prologue
     // repeats tile KT-1 into stages nobody reads; the waits below then only
     // count conservatively.)
-    static_assert(KSTEPS == 2, "two 32-deep steps per tile");
+    static_assert(KSTEPS == 2 || !PG, "per group, two 32-deep steps per tile");
     static_assert(STAGES >= 3, "the refill targets the stage freed one tile earlier");
     constexpr int DA = D / 2;
 #pragma unroll
@@ -430,10 +434,18 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
         const bool refill = kt + STAGES - 1 < KT;  // wavefront-uniform
         // step 0: reads step 1's fragments, first half of the refill
         step(first, f0, f1, kt, 1, refill ? DA : 0, 0, rstage, rsrc);
+        // deeper tiles: the middle steps, each reading the next step's
+        // fragments from the same stage (the register sets alternate)
+#pragma unroll
+        for (int ks = 1; ks < KSTEPS - 1; ks += 2) {
+            step(Flag<false>{}, f1, f0, kt, ks + 1, 0, 0, rstage, rsrc);
+            step(Flag<false>{}, f0, f1, kt, ks + 2, 0, 0, rstage, rsrc);
+        }
         // Tile kt+1 must have landed; tiles kt+2 .. kt+STAGES-2 and the first
         // half of tile kt+STAGES-1 may still be in flight (in the last tiles:
         // tiles kt+2 .. KT-1).  Every wave must also be done reading tile
-        // kt's stage before anyone refills it.
+        // kt's stage (its last fragments were read in the step just run)
+        // before anyone refills it.
         wait_lgkm0();
         if (refill)
             wait_vmcnt<(STAGES - 3) * DT + DA>();
@@ -441,8 +453,8 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
             wait_tiles<DT, STAGES - 3>(KT - 2 - kt);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        // step 1: reads tile kt+1's step-0 fragments (at the last tile: a stage
-        // whose contents are never used), second half of the refill
+        // last step: reads tile kt+1's step-0 fragments (at the last tile: a
+        // stage whose contents are never used), second half of the refill
         step(Flag<false>{}, f1, f0, kt + 1, 0, refill ? DT - DA : 0, DA, rstage, rsrc);
         if constexpr (PG && decltype(last)::value) {
             if constexpr (SCALED) {
@@ -489,6 +501,17 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     // short K) when the epilogue reuses it or the workgroup's LDS is handed
     // to the next workgroup.
     wait_vmcnt<0>();
+    if constexpr (OUT != OUT_I32) {
+#pragma unroll
+        for (int i = 0; i < NSC; ++i) {
+            const int t = (int)threadIdx.x + i * NW * 64;
+            if (t < TSW)
+                s_sw[t] = scv[i];
+            else if (t < TSW + TM)
+                s_st[t - TSW] = scv[i];
+        }
+        __syncthreads();  // the scales are in LDS; every wave is done with the operand stages
+    }
 
     // Epilogue.  Block (i, j) gives the lane token m = wm*WM + 32j + lane%32
     // and, for q = 0..3, output channels nb .. nb+3, nb = wn*WN + 32i + 8q +
@@ -537,7 +560,6 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
         // write instruction touches fall in distinct bank groups), then leave
         // as 16-byte stores, consecutive lanes along a token row.
         constexpr int CPRO = WN * 2 / 16;
-        __syncthreads();  // every wave is done with the operand stages, and its copies have landed
         uint8_t *ob = smem + wave * (32 * ROWB);
         uint16_t *yout = static_cast<uint16_t *>(args.out);
 #pragma unroll
@@ -578,6 +600,8 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
 template <int TN, int TM, int WN, int WM, int BK, int BITS, int GS, int OUT, int STAGES>
 hipError_t launch_cfg(const ProductArgs &a, hipStream_t stream)
 {
+    if (a.K % BK != 0)  // the kernel walks whole K tiles
+        return hipErrorInvalidValue;
     const int tiles_n = (int)((a.N + TN - 1) / TN);
     const int tiles_m = (int)((a.M + TM - 1) / TM);
     dim3 grid(tiles_n * tiles_m), block((TN / WN) * (TM / WM) * 64);
@@ -611,7 +635,8 @@ int64_t rounds(int64_t M, int64_t N, int TM, int TN)
 }
 
 // Tile shape by M (measured on MI355X over the N=10240 / N=2560 operator
-// shapes).  Small M: 64-channel x 128-token tiles with a deep copy ring
+// shapes).  M <= 128: 64 channels x 32 / 64 / 128 tokens with deep K tiles;
+// M <= 256: 64-channel x 128-token tiles with a deep copy ring
 // (latency-bound: more copies in flight).  Larger M: a big tile, chosen by
 // how many whole rounds of workgroups over the compute units it needs times
 // its measured time per tile:
@@ -622,6 +647,18 @@ int64_t rounds(int64_t M, int64_t N, int TM, int TN)
 template <int BITS, int OUT>
 hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
 {
+    // Few tokens: the weights stream through once, so each K tile is deep
+    // (128 bytes of a weight row, 256 for packed int4) to read whole cache
+    // lines per row and halve the tiles, and with them the per-tile barrier
+    // and wait latency that bounds a workgroup's rate here.
+    constexpr int BKS = BITS == 8 ? 128 : 256, STS = BITS == 8 ? 4 : 3;
+    if (a.M <= 128 && a.K % BKS == 0) {  // whole deep tiles only
+        if (a.M <= 32)
+            return launch_cfg<64, 32, 32, 32, BKS, BITS, 0, OUT, STS>(a, stream);
+        if (a.M <= 64)
+            return launch_cfg<64, 64, 32, 64, BKS, BITS, 0, OUT, STS>(a, stream);
+        return launch_cfg<64, 128, 32, 64, BKS, BITS, 0, OUT, STS>(a, stream);
+    }
     if (a.M <= 256)
         return launch_cfg<64, 128, 32, 64, 64, BITS, 0, OUT, 8>(a, stream);
     const int64_t r320 = rounds(a.M, a.N, 256, 320), r256 = rounds(a.M, a.N, 256, 256);

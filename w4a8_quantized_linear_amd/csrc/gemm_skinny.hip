@@ -99,18 +99,22 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(ProductArgs args, int 
     const int64_t wld = BITS == 8 ? K : K / 2;
     const int G = PG ? (int)(K / GS) : 1;
 
-    // zero the int32 tile; stage the tile's scales (their latency hides
-    // under the main loop; the barrier before the reduction orders them)
+    // Zero the int32 tile.  The tile's scales go into registers now
+    // (branch-free loads whose latency hides under the main loop) and into
+    // LDS just before the reduction's barrier: stored to LDS here, every
+    // wavefront would wait for them before issuing its first weight load.
     if constexpr (!PG)
         for (int o = threadIdx.x; o < TM * TS; o += kThreads)
             part[o] = 0;
-    if constexpr (OUT != OUT_I32) {
-        for (int o = threadIdx.x; o < TM + TN; o += kThreads) {
-            if (o < TM)
-                s_st[o] = args.s_tok[min(m0 + o, M - 1)];
-            else if constexpr (!PG)
-                s_sw[o - TM] = args.s_w[min(n0 + (o - TM), N - 1)];
-        }
+    constexpr int NSV = PG ? TM : TM + TN;  // per group, channel scales come per unit
+    constexpr int NSC = OUT != OUT_I32 ? (NSV + kThreads - 1) / kThreads : 0;
+    float scv[NSC > 0 ? NSC : 1];
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) {
+        const int o = (int)threadIdx.x + i * kThreads;
+        const float *src = o < TM ? args.s_tok + min(m0 + o, M - 1)
+                                  : args.s_w + min(n0 + min(o - TM, TN - 1), N - 1);
+        scv[i] = *src;
     }
     __syncthreads();
 
@@ -253,6 +257,17 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(ProductArgs args, int 
     }
     if constexpr (PG && OUT == OUT_I32)
         return;
+
+    if constexpr (OUT != OUT_I32) {
+#pragma unroll
+        for (int i = 0; i < NSC; ++i) {
+            const int o = (int)threadIdx.x + i * kThreads;
+            if (o < TM)
+                s_st[o] = scv[i];
+            else if (o < NSV)
+                s_sw[o - TM] = scv[i];
+        }
+    }
 
     // Partial tiles to LDS.  Block (i, j) gives the lane: per channel, token
     // 16j + lane%16 and channels 16i + 4*(lane/16) + e; per group, channel
