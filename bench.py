@@ -85,6 +85,10 @@ class Layer:
                 st=torch.empty((M,), dtype=torch.float32, device=dev),
                 y=torch.empty((M, N), dtype=torch.float16, device=dev)))
         del x, w
+        # one workspace for every copy (calls are ordered on one stream), large
+        # enough for the split-K product where the shape uses it
+        self.ws_bytes = cider.cider_linear_workspace_bytes_ex(M, N, K, bits, gs)
+        self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=dev)
 
     def quantize(self, i):
         s = self.sets[i % len(self.sets)]
@@ -96,13 +100,16 @@ class Layer:
         f(s["xq"], s["st"], s["wq"], s["sw"], self.M, self.N, self.K, self.gs, s["y"])
 
     def linear(self, i):
+        """The whole layer through the linear entry point (M = 1: quantization
+        fused into the one-token kernel, no workspace; up to 128 tokens: the
+        split-K product where the shape uses it)."""
         s = self.sets[i % len(self.sets)]
-        if self.M == 1:  # quantization fused into the one-token kernel, no workspace
-            f = self.cider.cider_w8a8_linear if self.bits == 8 else self.cider.cider_w4a8_linear
+        f = self.cider.cider_w8a8_linear if self.bits == 8 else self.cider.cider_w4a8_linear
+        if self.M == 1:
             f(s["x"], 1, self.K, self.K, s["wq"], s["sw"], self.N, self.gs, None, 0, s["y"])
         else:
-            self.quantize(i)
-            self.gemm(i)
+            f(s["x"], self.M, self.K, self.K, s["wq"], s["sw"], self.N, self.gs, self.ws,
+              self.ws_bytes, s["y"])
 
 
 def alg_bytes(bits, gs, N, K, M):

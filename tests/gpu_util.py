@@ -98,9 +98,12 @@ def gemm_i32_gpu(xq, wq, M, N, K, bits, gs):
     return acc
 
 
-def linear_gpu(xd, M, K, ldx, wq, sw, N, bits, gs):
+def linear_gpu(xd, M, K, ldx, wq, sw, N, bits, gs, split=True):
+    """The linear entry point; split=True hands it the workspace that lets
+    it split K (as the benchmark does), split=False the minimal one."""
     import torch
-    ws_bytes = cider.cider_linear_workspace_bytes(M, K)
+    ws_bytes = (cider.cider_linear_workspace_bytes_ex(M, N, K, bits, gs) if split
+                else cider.cider_linear_workspace_bytes(M, K))
     ws = empty((max(ws_bytes, 16),), torch.uint8)
     y = empty((M, N), torch.float16)
     f = cider.cider_w8a8_linear if bits == 8 else cider.cider_w4a8_linear

@@ -31,7 +31,7 @@ PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
 EXPORTS = (
     "cider_is_available", "cider_status_str", "cider_quantize_weight", "cider_quantize_act",
     "cider_w8a8_gemm", "cider_w4a8_gemm", "cider_w8a8_gemm_i32", "cider_w4a8_gemm_i32",
-    "cider_linear_workspace_bytes", "cider_w8a8_linear", "cider_w4a8_linear", "cider_set_path",
+    "cider_linear_workspace_bytes", "cider_linear_workspace_bytes_ex", "cider_w8a8_linear", "cider_w4a8_linear", "cider_set_path",
     "cider_quantize_weight_clipped", "cider_quantize_weight_ex", "cider_smooth_fold_weight",
     "cider_quantize_act_ex", "cider_gemm_ex", "cider_linear_ex", "cider_decode_linear",
 )
@@ -79,6 +79,7 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         "cider_w8a8_gemm_i32": ([P, P, I64, I64, I64, I, P, P], I),
         "cider_w4a8_gemm_i32": ([P, P, I64, I64, I64, I, P, P], I),
         "cider_linear_workspace_bytes": ([I64, I64], SZ),
+        "cider_linear_workspace_bytes_ex": ([I64, I64, I64, I, I], SZ),
         "cider_w8a8_linear": ([P, I64, I64, I64, P, P, I64, I, P, SZ, P, P], I),
         "cider_w4a8_linear": ([P, I64, I64, I64, P, P, I64, I, P, SZ, P, P], I),
         "cider_set_path": ([I], I),
@@ -211,6 +212,10 @@ def cider_w4a8_gemm_i32(xq, wq4, M, N, K, group_size, acc, stream=None, check=Tr
 
 def cider_linear_workspace_bytes(M, K) -> int:
     return int(load().cider_linear_workspace_bytes(M, K))
+
+
+def cider_linear_workspace_bytes_ex(M, N, K, bits, group_size) -> int:
+    return int(load().cider_linear_workspace_bytes_ex(M, N, K, bits, group_size))
 
 
 def cider_w8a8_linear(x_f16, M, K, ldx, wq, s_w, N, group_size, workspace, workspace_bytes,

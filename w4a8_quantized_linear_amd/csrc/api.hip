@@ -27,6 +27,17 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Bytes of the split product's partial sums (4-byte words per tile and
+// split), and those plus the tile counters.
+size_t split_part_bytes(const cider::SplitPlan &p)
+{
+    return round256((size_t)(p.tiles * p.splits * p.tile_elems) * 4u);
+}
+size_t split_bytes(const cider::SplitPlan &p)
+{
+    return split_part_bytes(p) + round256((size_t)p.tiles * sizeof(uint32_t));
+}
+
 // 1: usable gfx950 device current; 0: not.  Cached per device id.
 int device_usable()
 {
@@ -185,8 +196,23 @@ cider_status run_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_
                                                  out_kind_of(y_dtype), s));
     int8_t *xq = static_cast<int8_t *>(ws);
     float *s_tok = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + round256((size_t)(M * K)));
+    // Split K when the plan asks for it and the workspace has room for the
+    // partial sums and tile counters (the quantize launch clears the counters).
+    cider::SplitPlan plan{1, 0, 0};
+    void *part = nullptr;
+    uint32_t *cnt = nullptr;
+    if (path == PATH_GEMM) {
+        plan = cider::plan_split(M, N, K, bits, group_size);
+        if (plan.splits > 1 && ws_bytes >= cider_linear_workspace_bytes(M, K) + split_bytes(plan)) {
+            part = static_cast<uint8_t *>(ws) + cider_linear_workspace_bytes(M, K);
+            cnt = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(part) + split_part_bytes(plan));
+        } else {
+            plan.splits = 1;
+        }
+    }
     hipError_t e = cider::launch_quantize_rows(static_cast<const uint16_t *>(x), x_dtype, M, K, ldx,
-                                               smooth, 8, xq, s_tok, s);
+                                               smooth, 8, xq, s_tok, s, cnt,
+                                               cnt ? (int)plan.tiles : 0);
     if (e != hipSuccess)
         return CIDER_ERR_HIP;
     cider::ProductArgs a{};
@@ -201,6 +227,8 @@ cider_status run_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_
     a.group_size = group_size;
     a.out_kind = out_kind_of(y_dtype);
     a.out = y;
+    if (plan.splits > 1)
+        return from_hip(cider::launch_gemm_split(a, plan, part, cnt, s));
     return from_hip(path == PATH_GEMV ? cider::launch_gemv(a, s) : cider::launch_gemm(a, s));
 }
 
@@ -373,6 +401,17 @@ size_t cider_linear_workspace_bytes(int64_t M, int64_t K)
     if (M <= 0 || K <= 0)
         return 0;
     return round256((size_t)(M * K)) + round256((size_t)M * sizeof(float));
+}
+
+size_t cider_linear_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int bits, int group_size)
+{
+    const size_t base = cider_linear_workspace_bytes(M, K);
+    int path = PATH_GEMM;
+    if (check_shape(M, N, K, bits, group_size) != CIDER_OK || M <= 0 || N <= 0 ||
+        pick_path(M, K, &path) != CIDER_OK || path != PATH_GEMM)
+        return base;
+    const cider::SplitPlan p = cider::plan_split(M, N, K, bits, group_size);
+    return p.splits < 2 ? base : base + split_bytes(p);
 }
 
 cider_status cider_w8a8_linear(const void *x_f16, int64_t M, int64_t K, int64_t ldx,

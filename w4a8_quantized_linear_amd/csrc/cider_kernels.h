@@ -14,10 +14,12 @@ namespace cider {
 // [rows].  len % 8 == 0.  smooth (fp32 [len], 16-byte aligned, bits 8 only)
 // or null: each element divided by its column's factor before the absmax.
 // Per-token activations are rows = M, len = K; per-channel weights rows = N;
-// per-group weights are the [N * K/gs, gs] view of W.
+// per-group weights are the [N * K/gs, gs] view of W.  `zero` (nzero
+// words, or null) is cleared by the same launch: the split product's tile
+// counters, reset before every product that uses them.
 hipError_t launch_quantize_rows(const uint16_t *x, int dtype, int64_t rows, int64_t len, int64_t ld,
                                 const float *smooth, int bits, void *out, float *scale,
-                                hipStream_t stream);
+                                hipStream_t stream, uint32_t *zero = nullptr, int nzero = 0);
 
 // The same with each row's range the percentile of its |w| (percentile
 // clipping): ranks r0 <= r1 of the two order statistics and the
@@ -63,9 +65,31 @@ struct ProductArgs {
     void *out;             // fp16 [M, N] or int32 [M, N] / [M, N, K/gs]
 };
 
+// Split-K state handed to the product kernel (all zero: no split).
+struct SplitArgs {
+    void *part;      // partial sums, [tiles][splits][TM * TN] 4-byte words
+    uint32_t *cnt;   // [tiles] arrival counters, zero at launch
+    int splits;
+};
+
 // Matrix-core product (any M >= 1, every mode); per group with M <= 256
 // goes to the few-token kernel.
 hipError_t launch_gemm(const ProductArgs &a, hipStream_t stream);
+
+// Split-K product for few tokens (fp16 / bf16 output only).  Each output
+// tile is computed by `splits` workgroups over disjoint K ranges (whole
+// groups per group); each writes its partial sums (int32 per channel, the
+// group-scaled fp32 sums per group) to `part`, and the last one to finish
+// (counted in cnt[tile], which must be zero at launch) adds them up in split
+// order and stores the dequantized tile.
+struct SplitPlan {
+    int splits;          // 1: no split
+    int64_t tiles;       // output tiles = counters
+    int64_t tile_elems;  // partial-sum words per tile and split
+};
+SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int bits, int group_size);
+hipError_t launch_gemm_split(const ProductArgs &a, const SplitPlan &p, void *part, uint32_t *cnt,
+                             hipStream_t stream);
 hipError_t launch_gemm_skinny(const ProductArgs &a, hipStream_t stream);
 
 // Matrix-vector product for M <= 8 and M * K <= 32768.

@@ -190,9 +190,12 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_n, int tiles_m, i
 // that a lane's outputs all belong to one channel per 32-channel block and
 // need one group scale each; the int32 sum of each group is scaled into an
 // fp32 accumulator as soon as the group's last K tile is multiplied.
-template <int TN, int TM, int WN, int WM, int BK, int BITS, int GS, int OUT, int STAGES>
+// SPLIT: workgroup blockIdx.x computes split z = blockIdx.x / tiles of tile
+// blockIdx.x % tiles (the splits of a tile share its XCD), over its share
+// of the K tiles, then takes part in the split reduction.
+template <int TN, int TM, int WN, int WM, int BK, int BITS, int GS, int OUT, int STAGES, bool SPLIT = false>
 __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
-    ProductArgs args, int tiles_n, int tiles_m, int group_m)
+    ProductArgs args, int tiles_n, int tiles_m, int group_m, SplitArgs sp)
 {
     constexpr int NWN = TN / WN, NWM = TM / WM, NW = NWN * NWM;
     constexpr int FN = WN / 32, FM = WM / 32;
@@ -231,14 +234,28 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     __shared__ __attribute__((aligned(16))) float s_st[OUT != OUT_I32 ? TM : 4];         // s_tok tile
 
     const int64_t M = args.M, N = args.N, K = args.K;
+    int pid = blockIdx.x, z = 0;
+    if constexpr (SPLIT) {
+        z = pid / (tiles_n * tiles_m);
+        pid -= z * (tiles_n * tiles_m);
+    }
     int tn, tm;
-    tile_coords(blockIdx.x, tiles_n, tiles_m, group_m, tn, tm);
+    tile_coords(pid, tiles_n, tiles_m, group_m, tn, tm);
     const int64_t n0 = (int64_t)tn * TN, m0 = (int64_t)tm * TM;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wn = wave % NWN, wm = wave / NWN;
     const uint32_t wld = (uint32_t)(BITS == 8 ? K : K / 2);
-    const int KT = (int)(K / BK);
+    // This workgroup's K tiles kt0 .. kt0 + KT - 1 (a split takes whole
+    // groups; the host guarantees every split at least one).
+    int kt0 = 0, KT = (int)(K / BK);
+    if constexpr (SPLIT) {
+        constexpr int U = PG ? GS / BK : 1;
+        const int KU = KT / U;
+        const int u0 = (int)((int64_t)z * KU / sp.splits), u1 = (int)((int64_t)(z + 1) * KU / sp.splits);
+        kt0 = u0 * U;
+        KT = (u1 - u0) * U;
+    }
 
     const i32x4 rX = make_rsrc(args.xq, (uint32_t)(M * K));
     const i32x4 rW = make_rsrc(args.wq, (uint32_t)(N * (int64_t)wld));
@@ -285,9 +302,9 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     const uint32_t smem_lds = lds_address(smem);
     auto copy_one = [&](int j, int stage, int src) {
         if (j < D) {
-            dma16(crs[j], smem_lds + stage * STAGE + cdst[j], coff[j] + (uint32_t)src * cstep[j]);
+            dma16(crs[j], smem_lds + stage * STAGE + cdst[j], coff[j] + (uint32_t)(kt0 + src) * cstep[j]);
         } else if constexpr (SCOPY) {
-            const uint32_t g = (uint32_t)(src * BK / GS);
+            const uint32_t g = (uint32_t)((kt0 + src) * BK / GS);
             dma4(rS, smem_lds + stage * STAGE + sdst[j - D], soff[j - D] + g * 4u);
         }
     };
@@ -467,7 +484,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
                             facc[i][j][e] += (float)acc[i][j][e] * sw[i];
             } else {
                 // int32 hook: acc[m, n, g] for this lane's channel and tokens
-                const int64_t g = (int64_t)kt * BK / GS;
+                const int64_t g = (int64_t)(kt0 + kt) * BK / GS;
 #pragma unroll
                 for (int i = 0; i < FN; ++i) {
                     const int64_t n = n0 + wn * WN + i * 32 + frow;
@@ -501,6 +518,104 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     // short K) when the epilogue reuses it or the workgroup's LDS is handed
     // to the next workgroup.
     wait_vmcnt<0>();
+    if constexpr (SPLIT) {
+        // Split reduction.  Partial sums live tile by tile, split by split,
+        // each lane's 16-byte quarters of its (i, j) block 64 lanes apart.
+        // They are stored and loaded as relaxed device-scope atomics, which
+        // this GPU performs at the device-coherent level, past the XCD-private
+        // L2 caches; each split waits for its stores to complete before the
+        // barrier after which thread 0 counts the split in, and the last of a
+        // tile's splits to count in loads the others' partials only after
+        // that.  (A release / acquire fence pair per workgroup would write
+        // back and invalidate the whole L2 of its XCD instead -- measured at
+        // 3-4x the time of the unsplit product.)  The partials are added in
+        // split order, so the sum does not depend on which split was last.
+        static_assert(OUT != OUT_I32, "split products dequantize");
+        constexpr int TILE = TM * TN;
+        typedef unsigned long long u64;
+        uint32_t *mine = static_cast<uint32_t *>(sp.part) + (int64_t)pid * sp.splits * TILE +
+                         wave * (64 * FN * FM * 16) + lane * 4;
+        auto slot = [&](int zz, int i, int j, int q) {
+            return reinterpret_cast<u64 *>(mine + (int64_t)zz * TILE + ((i * FM + j) * 4 + q) * 256);
+        };
+        auto quarter = [&](int i, int j, int q) -> i32x4 {
+            if constexpr (SCALED)
+                return i32x4{__float_as_int(facc[i][j][4 * q]), __float_as_int(facc[i][j][4 * q + 1]),
+                             __float_as_int(facc[i][j][4 * q + 2]), __float_as_int(facc[i][j][4 * q + 3])};
+            else
+                return i32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        };
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const i32x4 v = quarter(i, j, q);
+                    u64 *d = slot(z, i, j, q);
+                    __hip_atomic_store(d, (u64)(uint32_t)v[0] | ((u64)(uint32_t)v[1] << 32), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(d + 1, (u64)(uint32_t)v[2] | ((u64)(uint32_t)v[3] << 32), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+        wait_vmcnt<0>();  // this lane's partial stores have completed
+        __syncthreads();
+        uint32_t *flag = reinterpret_cast<uint32_t *>(smem);  // the ring is idle now
+        if (threadIdx.x == 0)
+            *flag = __hip_atomic_fetch_add(sp.cnt + pid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (*flag != (uint32_t)(sp.splits - 1))
+            return;
+        // Every split's partial (this one's included) is read back, split
+        // after split, the next split's loads in flight while the previous
+        // one is added (branch-free: past the last split the index is
+        // clamped and the extra loads are not used).
+        typedef i32x4 Part[FN][FM][4];
+        auto fetch = [&](int zz, Part &dst) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const u64 *src = slot(zz, i, j, q);
+                        const u64 lo = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        const u64 hi = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        dst[i][j][q] = i32x4{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi,
+                                             (int)(uint32_t)(hi >> 32)};
+                    }
+        };
+        auto add = [&](bool first_split, const Part &v) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if constexpr (SCALED) {
+                                const float f = __int_as_float(v[i][j][q][e]);
+                                facc[i][j][4 * q + e] = first_split ? f : facc[i][j][4 * q + e] + f;
+                            } else {
+                                const int t = v[i][j][q][e];
+                                acc[i][j][4 * q + e] = first_split ? t : acc[i][j][4 * q + e] + t;
+                            }
+                        }
+        };
+        const int S = sp.splits;
+        Part pa, pb;
+        fetch(0, pa);
+        for (int zz = 0; zz < S; zz += 2) {
+            fetch(min(zz + 1, S - 1), pb);
+            add(zz == 0, pa);
+            fetch(min(zz + 2, S - 1), pa);
+            if (zz + 1 < S)
+                add(false, pb);
+        }
+        // (every wave reads the flag before the barrier below, after which
+        // the epilogue may reuse the ring)
+    }
     if constexpr (OUT != OUT_I32) {
 #pragma unroll
         for (int i = 0; i < NSC; ++i) {
@@ -606,7 +721,23 @@ hipError_t launch_cfg(const ProductArgs &a, hipStream_t stream)
     const int tiles_m = (int)((a.M + TM - 1) / TM);
     dim3 grid(tiles_n * tiles_m), block((TN / WN) * (TM / WM) * 64);
     hipLaunchKernelGGL((gemm_kernel<TN, TM, WN, WM, BK, BITS, GS, OUT, STAGES>), grid, block, 0,
-                       stream, a, tiles_n, tiles_m, 8);
+                       stream, a, tiles_n, tiles_m, 8, SplitArgs{});
+    return hipGetLastError();
+}
+
+template <int TN, int TM, int WN, int WM, int BK, int BITS, int GS, int OUT, int STAGES>
+hipError_t launch_split_cfg(const ProductArgs &a, const SplitPlan &p, void *part, uint32_t *cnt,
+                            hipStream_t stream)
+{
+    const int tiles_n = (int)((a.N + TN - 1) / TN);
+    const int tiles_m = (int)((a.M + TM - 1) / TM);
+    constexpr int U = GS ? GS / BK : 1;  // K tiles per split unit
+    if (a.K % BK != 0 || p.splits < 2 || a.K / BK / U < p.splits || p.tiles != (int64_t)tiles_n * tiles_m ||
+        p.tile_elems != (int64_t)TN * TM)
+        return hipErrorInvalidValue;  // the plan does not fit this configuration
+    dim3 grid(tiles_n * tiles_m * p.splits), block((TN / WN) * (TM / WM) * 64);
+    hipLaunchKernelGGL((gemm_kernel<TN, TM, WN, WM, BK, BITS, GS, OUT, STAGES, true>), grid, block, 0,
+                       stream, a, tiles_n, tiles_m, 8, SplitArgs{part, cnt, p.splits});
     return hipGetLastError();
 }
 
@@ -696,7 +827,94 @@ hipError_t launch_group_bits(const ProductArgs &a, hipStream_t stream)
     return a.bits == 8 ? launch_group<8, GS, OUT>(a, stream) : launch_group<4, GS, OUT>(a, stream);
 }
 
+// Split-K tiles for few tokens: 64 channels x 32 / 64 / 128 tokens; per
+// channel with the deep K tiles of the unsplit few-token product, per group
+// with 64-deep tiles (whole groups per split).
+constexpr int kSplitTN = 64;
+constexpr int split_tm(int64_t M) { return M <= 32 ? 32 : M <= 64 ? 64 : 128; }
+constexpr int split_bk(int bits, int group_size) { return group_size ? 64 : bits == 8 ? 128 : 256; }
+
+template <int BITS, int GS, int OUT>
+hipError_t launch_split_bits(const ProductArgs &a, const SplitPlan &p, void *part, uint32_t *cnt,
+                             hipStream_t stream)
+{
+    if constexpr (GS == 0) {
+        constexpr int BKS = BITS == 8 ? 128 : 256, STS = BITS == 8 ? 4 : 3;
+        if (a.M <= 32)
+            return launch_split_cfg<kSplitTN, 32, 32, 32, BKS, BITS, 0, OUT, STS>(a, p, part, cnt, stream);
+        if (a.M <= 64)
+            return launch_split_cfg<kSplitTN, 64, 32, 64, BKS, BITS, 0, OUT, STS>(a, p, part, cnt, stream);
+        return launch_split_cfg<kSplitTN, 128, 32, 64, BKS, BITS, 0, OUT, STS>(a, p, part, cnt, stream);
+    } else {
+        if (a.M <= 32)
+            return launch_split_cfg<kSplitTN, 32, 64, 32, 64, BITS, GS, OUT, 6>(a, p, part, cnt, stream);
+        if (a.M <= 64)
+            return launch_split_cfg<kSplitTN, 64, 64, 32, 64, BITS, GS, OUT, 6>(a, p, part, cnt, stream);
+        return launch_split_cfg<kSplitTN, 128, 64, 32, 64, BITS, GS, OUT, 6>(a, p, part, cnt, stream);
+    }
+}
+
+template <int OUT>
+hipError_t launch_split_kind(const ProductArgs &a, const SplitPlan &p, void *part, uint32_t *cnt,
+                             hipStream_t stream)
+{
+    const bool b8 = a.bits == 8;
+    switch (a.group_size) {
+    case 0:
+        return b8 ? launch_split_bits<8, 0, OUT>(a, p, part, cnt, stream)
+                  : launch_split_bits<4, 0, OUT>(a, p, part, cnt, stream);
+    case 64:
+        return b8 ? launch_split_bits<8, 64, OUT>(a, p, part, cnt, stream)
+                  : launch_split_bits<4, 64, OUT>(a, p, part, cnt, stream);
+    default:
+        return b8 ? launch_split_bits<8, 128, OUT>(a, p, part, cnt, stream)
+                  : launch_split_bits<4, 128, OUT>(a, p, part, cnt, stream);
+    }
+}
+
 }  // namespace
+
+// When to split, from measurements of the whole layer on MI355X (N = 10240,
+// K = 2560 per channel; N = 2560, K = 10240 per group; 16 to 256 tokens):
+//   * per group (up to 256 tokens): the unsplit few-token kernel takes
+//     35-70 us; split into about one workgroup per compute unit, the
+//     matrix-core tiles take 26-42 us;
+//   * int4 per channel (up to 64 tokens): about two workgroups per compute
+//     unit, 12-14% faster;
+//   * int8 per channel: never faster -- the deep-K tiles already stream the
+//     weights at the rate the split reaches, and the partial sums' round trip
+//     through memory costs more than the extra workgroups gain.
+SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int bits, int group_size)
+{
+    SplitPlan p{1, 0, 0};
+    const int bk = split_bk(bits, group_size);
+    const int64_t max_m = group_size ? 256 : bits == 4 ? 64 : 0;
+    if (M < 1 || M > max_m || N < 1 || K < bk || K % bk != 0)
+        return p;
+    const int TM = split_tm(M);
+    const int64_t tiles = ((N + kSplitTN - 1) / kSplitTN) * ((M + TM - 1) / TM);
+    const int64_t units = K / bk / (group_size ? group_size / bk : 1);
+    const int64_t target = (group_size ? 1 : 2) * (int64_t)compute_units();
+    int64_t S = (target + tiles / 2) / tiles;  // nearest
+    S = S < 8 ? S : 8;
+    S = S < units ? S : units;
+    if (S < 2)
+        return p;
+    p.splits = (int)S;
+    p.tiles = tiles;
+    p.tile_elems = (int64_t)kSplitTN * TM;
+    return p;
+}
+
+hipError_t launch_gemm_split(const ProductArgs &a, const SplitPlan &p, void *part, uint32_t *cnt,
+                             hipStream_t stream)
+{
+    switch (a.out_kind) {
+    case OUT_F16: return launch_split_kind<OUT_F16>(a, p, part, cnt, stream);
+    case OUT_BF16: return launch_split_kind<OUT_BF16>(a, p, part, cnt, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 template <int OUT>
 hipError_t launch_kind(const ProductArgs &a, hipStream_t stream)

@@ -90,9 +90,13 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__re
                                                             int64_t rows, int64_t len, int64_t ld,
                                                             const float *__restrict__ smooth,
                                                             uint8_t *__restrict__ out,
-                                                            float *__restrict__ scale)
+                                                            float *__restrict__ scale,
+                                                            uint32_t *__restrict__ zero, int nzero)
 {
     constexpr int TEAMS = 256 / TS;
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < nzero; i += 256)
+            zero[i] = 0u;
     const int lane = threadIdx.x % TS;
     const int64_t row = (int64_t)blockIdx.x * TEAMS + threadIdx.x / TS;
     if (row >= rows)
@@ -145,9 +149,13 @@ __global__ __launch_bounds__(256) void quantize_long_rows_kernel(const uint16_t 
                                                                  int64_t len, int64_t ld,
                                                                  const float *__restrict__ smooth,
                                                                  uint8_t *__restrict__ out,
-                                                                 float *__restrict__ scale)
+                                                                 float *__restrict__ scale,
+                                                                 uint32_t *__restrict__ zero, int nzero)
 {
     __shared__ uint32_t red[4];
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < nzero; i += 256)
+            zero[i] = 0u;
     const int64_t row = blockIdx.x;
     const uint16_t *xr = x + row * ld;
     const int64_t nch = len >> 3;
@@ -184,31 +192,31 @@ __global__ __launch_bounds__(256) void quantize_long_rows_kernel(const uint16_t 
 
 template <int TS, int NCH, int BITS, int DT, bool SMOOTH>
 hipError_t launch_team(const uint16_t *x, int64_t rows, int64_t len, int64_t ld, const float *smooth,
-                       void *out, float *scale, hipStream_t stream)
+                       void *out, float *scale, hipStream_t stream, uint32_t *zero, int nzero)
 {
     constexpr int TEAMS = 256 / TS;
     const int64_t blocks = (rows + TEAMS - 1) / TEAMS;
     hipLaunchKernelGGL((quantize_rows_kernel<TS, NCH, BITS, DT, SMOOTH>), dim3((unsigned)blocks),
                        dim3(256), 0, stream, x, rows, len, ld, smooth, static_cast<uint8_t *>(out),
-                       scale);
+                       scale, zero, nzero);
     return hipGetLastError();
 }
 
 template <int BITS, int DT, bool SMOOTH>
 hipError_t launch_bits(const uint16_t *x, int64_t rows, int64_t len, int64_t ld, const float *smooth,
-                       void *out, float *scale, hipStream_t stream)
+                       void *out, float *scale, hipStream_t stream, uint32_t *zero, int nzero)
 {
     const int64_t nch = len / 8;
     if (nch <= 8)
-        return launch_team<8, 1, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream);
+        return launch_team<8, 1, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream, zero, nzero);
     if (nch <= 16)
-        return launch_team<16, 1, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream);
+        return launch_team<16, 1, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream, zero, nzero);
     if (nch <= 32)
-        return launch_team<32, 1, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream);
+        return launch_team<32, 1, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream, zero, nzero);
     const int64_t per_lane = (nch + 63) / 64;
 #define CIDER_TEAM64(n)                                                                          \
     if (per_lane <= n)                                                                           \
-        return launch_team<64, n, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream);
+        return launch_team<64, n, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream, zero, nzero);
     CIDER_TEAM64(1)
     CIDER_TEAM64(2)
     CIDER_TEAM64(3)
@@ -223,7 +231,7 @@ hipError_t launch_bits(const uint16_t *x, int64_t rows, int64_t len, int64_t ld,
     CIDER_TEAM64(24)
 #undef CIDER_TEAM64
     hipLaunchKernelGGL((quantize_long_rows_kernel<BITS, DT, SMOOTH>), dim3((unsigned)rows), dim3(256),
-                       0, stream, x, len, ld, smooth, static_cast<uint8_t *>(out), scale);
+                       0, stream, x, len, ld, smooth, static_cast<uint8_t *>(out), scale, zero, nzero);
     return hipGetLastError();
 }
 
@@ -231,21 +239,21 @@ hipError_t launch_bits(const uint16_t *x, int64_t rows, int64_t len, int64_t ld,
 
 hipError_t launch_quantize_rows(const uint16_t *x, int dtype, int64_t rows, int64_t len, int64_t ld,
                                 const float *smooth, int bits, void *out, float *scale,
-                                hipStream_t stream)
+                                hipStream_t stream, uint32_t *zero, int nzero)
 {
     if (rows == 0)
         return hipSuccess;
     if (smooth) {  // activations only: int8 codes
         if (bits != 8)
             return hipErrorInvalidValue;
-        return dtype == DT_BF16 ? launch_bits<8, DT_BF16, true>(x, rows, len, ld, smooth, out, scale, stream)
-                                : launch_bits<8, DT_F16, true>(x, rows, len, ld, smooth, out, scale, stream);
+        return dtype == DT_BF16 ? launch_bits<8, DT_BF16, true>(x, rows, len, ld, smooth, out, scale, stream, zero, nzero)
+                                : launch_bits<8, DT_F16, true>(x, rows, len, ld, smooth, out, scale, stream, zero, nzero);
     }
     if (dtype == DT_BF16)
-        return bits == 8 ? launch_bits<8, DT_BF16, false>(x, rows, len, ld, nullptr, out, scale, stream)
-                         : launch_bits<4, DT_BF16, false>(x, rows, len, ld, nullptr, out, scale, stream);
-    return bits == 8 ? launch_bits<8, DT_F16, false>(x, rows, len, ld, nullptr, out, scale, stream)
-                     : launch_bits<4, DT_F16, false>(x, rows, len, ld, nullptr, out, scale, stream);
+        return bits == 8 ? launch_bits<8, DT_BF16, false>(x, rows, len, ld, nullptr, out, scale, stream, zero, nzero)
+                         : launch_bits<4, DT_BF16, false>(x, rows, len, ld, nullptr, out, scale, stream, zero, nzero);
+    return bits == 8 ? launch_bits<8, DT_F16, false>(x, rows, len, ld, nullptr, out, scale, stream, zero, nzero)
+                     : launch_bits<4, DT_F16, false>(x, rows, len, ld, nullptr, out, scale, stream, zero, nzero);
 }
 
 }  // namespace cider
