@@ -155,16 +155,32 @@ __device__ __forceinline__ void wait_lgkm0()
     __builtin_amdgcn_s_waitcnt(0xC07F);
 }
 
-// Widen 8 packed nibbles (low nibble = even k) to int8 codes q = u - 8.
+// Widen 8 packed nibbles (low nibble = even k) to int8 codes q = u - 8, k
+// order kept: the even-k nibbles (low) and odd-k nibbles (high) are masked
+// into bytes, interleaved with two byte permutes, and each byte u becomes
+// u - 8 as (u + 0x78) ^ 0x80 (no carry leaves a byte for u <= 15).  Nine VALU
+// operations per 8 codes: the int4 product's main loop is otherwise bound by
+// this widening, not by the matrix cores.
 __device__ __forceinline__ void unpack8(uint32_t v, uint32_t &d0, uint32_t &d1)
 {
     const uint32_t lo = v & 0x0F0F0F0Fu;
     const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
-    const uint32_t a = (lo & 0xFFu) | ((hi & 0xFFu) << 8) | ((lo & 0xFF00u) << 8) | ((hi & 0xFF00u) << 16);
-    const uint32_t b = ((lo >> 16) & 0xFFu) | ((hi >> 8) & 0xFF00u) | ((lo & 0xFF000000u) >> 8) |
-                       (hi & 0xFF000000u);
+    const uint32_t a = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // k0 k1 k2 k3
+    const uint32_t b = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // k4 k5 k6 k7
     d0 = (a + 0x78787878u) ^ 0x80808080u;
     d1 = (b + 0x78787878u) ^ 0x80808080u;
+}
+
+// The same nibbles as unsigned bytes u = q + 8 (five operations per 8
+// codes).  Per channel the product takes these and subtracts 8 * sum_k x[m, k]
+// per token once the K loop is done: sum q x = sum u x - 8 sum x, exactly in
+// int32 (|sum u x| <= 15 * 127 * K).
+__device__ __forceinline__ void unpack8u(uint32_t v, uint32_t &d0, uint32_t &d1)
+{
+    const uint32_t lo = v & 0x0F0F0F0Fu;
+    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
+    d0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    d1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
 }
 
 __device__ __forceinline__ void tile_coords(int pid, int tiles_n, int tiles_m, int group_m,
@@ -332,14 +348,27 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
             f.b[j] = *reinterpret_cast<const i32x4 *>(st + off8<BK>(wm * WM + j * 32 + frow, ks * 2 + fhalf));
         }
     };
+    // int4 per channel: unsigned codes, corrected by the token sums below.
+    constexpr bool USUM = BITS == 4 && !PG;
     auto widen = [&](Frags &f, int i) {
         if constexpr (BITS == 4) {
             uint32_t d0, d1, d2, d3;
-            unpack8(f.ap[i].x, d0, d1);
-            unpack8(f.ap[i].y, d2, d3);
+            if constexpr (USUM) {
+                unpack8u(f.ap[i].x, d0, d1);
+                unpack8u(f.ap[i].y, d2, d3);
+            } else {
+                unpack8(f.ap[i].x, d0, d1);
+                unpack8(f.ap[i].y, d2, d3);
+            }
             f.a[i] = i32x4{(int)d0, (int)d1, (int)d2, (int)d3};
         }
     };
+    // Sums of the token codes this lane multiplies: token block j's row
+    // (lane % 32), the 16-byte chunks of half lane / 32 of every step.
+    int xs[USUM ? FM : 1];
+#pragma unroll
+    for (int j = 0; j < (USUM ? FM : 1); ++j)
+        xs[j] = 0;
 
     i32x16 acc[FN][FM];
     // Per group (fp16 output): facc accumulates each group's int32 sums
@@ -373,6 +402,13 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
 #pragma unroll
         for (int k = 0; k < LOADS; ++k)
             load_one(nxt, k, lkt, lks);
+        if constexpr (USUM) {
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    xs[j] = __builtin_amdgcn_sdot4(cur.b[j][e], 0x01010101, xs[j], false);
+        }
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
             widen(cur, i);
@@ -511,6 +547,19 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
         for (int kt = 0; kt < KT; kt += 2) {
             tile(kt, Flag<true>{}, Flag<false>{});
             tile(kt + 1, Flag<false>{}, Flag<true>{});
+        }
+    }
+
+    if constexpr (USUM) {
+        // both halves of each token's K: sum q x = sum u x - 8 sum x
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int t = 8 * (xs[j] + __shfl_xor(xs[j], 32, 64));
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[i][j][e] -= t;
         }
     }
 
@@ -768,13 +817,15 @@ int64_t rounds(int64_t M, int64_t N, int TM, int TN)
 // Tile shape by M (measured on MI355X over the N=10240 / N=2560 operator
 // shapes).  M <= 128: 64 channels x 32 / 64 / 128 tokens with deep K tiles;
 // M <= 256: 64-channel x 128-token tiles with a deep copy ring
-// (latency-bound: more copies in flight).  Larger M: a big tile, chosen by
+// (latency-bound: more copies in flight).  Up to 1024 tokens: 160-channel
+// tiles (int8 above 512 tokens: 8 waves of 160 x 64 over 256 tokens, 10%
+// faster than 128 tokens at M = 768..1024).  Larger M: a big tile, chosen by
 // how many whole rounds of workgroups over the compute units it needs times
-// its measured time per tile:
-//   int8: 320 x 256 (8 waves of 160 x 64), or 256 x 256 (8 waves of 128 x 64,
-//         about 0.8x the time per tile on HBM-cold operands);
-//   int4: 320 x 256, or 256 x 256 with 4 waves of 128 x 128 (each widened
-//         weight fragment feeds 4 token blocks; 0.61x the time per tile).
+// its measured time per tile: 320 x 256 (8 waves of 160 x 64), or 256 x 256
+// (8 waves of 128 x 64, about 0.8x the time per tile on HBM-cold operands).
+// int4 follows the same rule since its widening costs five VALU operations per
+// 8 codes (it used to favour a 4-wave 128 x 128 layout that widens each
+// weight fragment once for 4 token blocks).
 template <int BITS, int OUT>
 hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
 {
@@ -792,20 +843,14 @@ hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
     }
     if (a.M <= 256)
         return launch_cfg<64, 128, 32, 64, 64, BITS, 0, OUT, 8>(a, stream);
+    if (BITS == 8 && a.M > 512 && a.M <= 1024)
+        return launch_cfg<160, 256, 160, 64, 64, BITS, 0, OUT, 4>(a, stream);
+    if (a.M <= 1024)
+        return launch_cfg<160, 128, 160, 32, 64, BITS, 0, OUT, 4>(a, stream);
     const int64_t r320 = rounds(a.M, a.N, 256, 320), r256 = rounds(a.M, a.N, 256, 256);
-    if constexpr (BITS == 8) {
-        if (a.M <= 768)
-            return launch_cfg<160, 128, 160, 32, 64, BITS, 0, OUT, 4>(a, stream);
-        if (100 * r320 <= 80 * r256)
-            return launch_cfg<320, 256, 160, 64, 64, BITS, 0, OUT, 4>(a, stream);
-        return launch_cfg<256, 256, 128, 64, 64, BITS, 0, OUT, 4>(a, stream);
-    } else {
-        if (a.M <= 768)
-            return launch_cfg<64, 128, 32, 64, 64, BITS, 0, OUT, 3>(a, stream);
-        if (100 * r320 <= 61 * r256)
-            return launch_cfg<320, 256, 160, 64, 64, BITS, 0, OUT, 4>(a, stream);
-        return launch_cfg<256, 256, 128, 128, 64, BITS, 0, OUT, 3>(a, stream);
-    }
+    if (100 * r320 <= 80 * r256)
+        return launch_cfg<320, 256, 160, 64, 64, BITS, 0, OUT, 4>(a, stream);
+    return launch_cfg<256, 256, 128, 64, 64, BITS, 0, OUT, 4>(a, stream);
 }
 
 // Per group (operands swapped; a wave owns 32 tokens of WN channels).
