@@ -118,3 +118,48 @@ def test_split_not_used_past_its_range_or_for_one_token():
     for M, bits, gs in ((257, 8, 64), (65, 4, 0), (16, 8, 0), (1, 8, 64)):
         assert cider.cider_linear_workspace_bytes_ex(M, 2560, 2560, bits, gs) == \
             cider.cider_linear_workspace_bytes(M, 2560)
+
+
+@pytest.mark.parametrize("bits,gs,M,N,K", [(8, 64, 64, 640, 2048), (4, 0, 32, 1280, 2560),
+                                           (8, 0, 1, 2560, 2560), (4, 128, 200, 320, 1024),
+                                           (8, 0, 300, 640, 1024)])
+def test_linear_in_hip_graph(bits, gs, M, N, K):
+    """The linear call captured into a HIP graph (its tile counters are
+    cleared by the quantize kernel, not by a memset node) and replayed several
+    times with the program's own eager work and synchronizations in between:
+    every replay equals the eager result bit for bit."""
+    import torch
+    orc = get_oracle()
+    x = si.activations(M, K, seed=7)
+    w = si.weights(N, K, seed=8)
+    wq, sw = orc.quantize_weight(w, bits, gs)
+    xd, wqd, swd = gu.bits_to_dev(x.view(np.uint16)), gu.to_dev(wq), gu.to_dev(sw)
+    size = cider.cider_linear_workspace_bytes_ex(M, N, K, bits, gs)
+    ws = _garbage_workspace(size)
+    y = gu.empty((M, N), torch.int16)
+    f = cider.cider_w8a8_linear if bits == 8 else cider.cider_w4a8_linear
+
+    def call():
+        f(xd, M, K, K, wqd, swd, N, gs, None if M == 1 else ws, 0 if M == 1 else size, y)
+
+    call()
+    gu.sync()
+    eager = gu.bits_to_host(y).copy()
+    ref, _, _ = orc.linear_ex(x.view(np.uint16), 0, wq, sw, bits, gs, K=K, y_dtype=0)
+    gu.assert_out_close(eager, ref, 0, "eager M=%d" % M)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        call()  # warm on the capture stream
+        with torch.cuda.graph(g, stream=stream):
+            call()
+    torch.cuda.current_stream().wait_stream(stream)
+    gu.sync()
+    for r in range(4):
+        y.zero_()
+        ws.fill_(0x5A)  # the program's own eager work between replays
+        gu.sync()
+        g.replay()
+        gu.sync()
+        assert np.array_equal(gu.bits_to_host(y), eager), "replay %d" % r
