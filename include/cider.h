@@ -211,9 +211,11 @@ size_t cider_linear_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int bits
 
 /* The whole layer on fp16 activations, mirroring perchannel_linear(x, w, s)
    and w4a8_linear(x, packed, s) of Cider README "Low-Level API":
-   quantize_act into `workspace`, then the product.  For M = 1 the quantization
-   is fused into the matrix-vector kernel and the workspace is not touched.
-   x: fp16 [M, K] row stride ldx; y: fp16 [M, N]. */
+   quantize_act into `workspace`, then the product.  On the matrix-vector path
+   (M <= 8 with M * K <= 32768 under the automatic path setting) the
+   quantization is fused into the matrix-vector kernel and the workspace is
+   not touched (it may be null).  x: fp16 [M, K] row stride ldx; y: fp16
+   [M, N]. */
 cider_status cider_w8a8_linear(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
                                const int8_t *wq, const float *s_w, int64_t N, int group_size,
                                void *workspace, size_t workspace_bytes, void *y_f16,
@@ -224,10 +226,10 @@ cider_status cider_w4a8_linear(const void *x_f16, int64_t M, int64_t K, int64_t 
                                void *stream);
 
 /* The whole layer for any input / output type, with optional smoothing:
-   cider_quantize_act_ex into `workspace`, then cider_gemm_ex.  An fp16 token
-   (M = 1) without smoothing is quantized inside the matrix-vector kernel and
-   needs no workspace; every other call needs cider_linear_workspace_bytes(M,
-   K) bytes of it, or cider_linear_workspace_bytes_ex(...) bytes to split K.
+   cider_quantize_act_ex into `workspace`, then cider_gemm_ex.  fp16 tokens
+   without smoothing on the matrix-vector path (M <= 8, M * K <= 32768) are
+   quantized inside the matrix-vector kernel and need no workspace; every
+   other call needs cider_linear_workspace_bytes(M, K) bytes of it, or cider_linear_workspace_bytes_ex(...) bytes to split K.
    Calls that share a workspace must be ordered (one stream). */
 cider_status cider_linear_ex(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                              const float *smooth, const void *wq, const float *s_w, int64_t N,

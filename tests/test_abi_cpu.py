@@ -222,8 +222,12 @@ def test_linear_argument_codes():
     assert f(P, 16, 256, 256, P2, P3, 128, 0, P4, ws - 1, P, stream=0, check=False) == cider.CIDER_ERR_WORKSPACE
     assert f(P, 16, 256, 256, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_WORKSPACE
     assert f(P, 16, 256, 200, P2, P3, 128, 0, P4, ws, P, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
-    # one token: quantization fused into the matrix-vector kernel, no workspace needed
+    # up to 8 fp16 tokens on the matrix-vector path: quantization fused into
+    # the matrix-vector kernel, no workspace needed
     assert f(P, 1, 256, 256, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert f(P, 8, 256, 264, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    # past the matrix-vector range (M * K > 32768) the workspace is required
+    assert f(P, 8, 8192, 8192, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_WORKSPACE
 
 
 def test_forced_gemv_range():

@@ -179,8 +179,9 @@ cider_status run_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_
     st = pick_path(M, K, &path);
     if (st != CIDER_OK)
         return st;
-    // one fp16 token without smoothing: quantized inside the matrix-vector kernel
-    const bool fused = path == PATH_GEMV && M == 1 && x_dtype == CIDER_DTYPE_F16 && !smooth;
+    // fp16 tokens without smoothing on the matrix-vector path: quantized inside
+    // the matrix-vector kernel
+    const bool fused = path == PATH_GEMV && x_dtype == CIDER_DTYPE_F16 && !smooth;
     if (!fused) {
         if (!ws || ws_bytes < cider_linear_workspace_bytes(M, K))
             return CIDER_ERR_WORKSPACE;
@@ -191,8 +192,8 @@ cider_status run_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_
         return CIDER_ERR_NO_DEVICE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (fused)
-        return from_hip(cider::launch_gemv_fused(static_cast<const uint16_t *>(x), K, wq, s_w, N,
-                                                 bits, group_size, y, nullptr, nullptr,
+        return from_hip(cider::launch_gemv_fused(static_cast<const uint16_t *>(x), M, K, ldx, wq, s_w,
+                                                 N, bits, group_size, y, nullptr, nullptr,
                                                  out_kind_of(y_dtype), s));
     int8_t *xq = static_cast<int8_t *>(ws);
     float *s_tok = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + round256((size_t)(M * K)));

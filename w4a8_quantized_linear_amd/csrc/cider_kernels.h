@@ -95,12 +95,14 @@ hipError_t launch_gemm_skinny(const ProductArgs &a, hipStream_t stream);
 // Matrix-vector product for M <= 8 and M * K <= 32768.
 hipError_t launch_gemv(const ProductArgs &a, hipStream_t stream);
 
-// One-token layer: quantizes the fp16 row x [K] inside the matrix-vector
-// kernel and writes y [N] (fp16 or bf16 by out_kind).  xq_out / s_tok_out may be null; when given,
-// the quantized row and its scale are written there as well.
-hipError_t launch_gemv_fused(const uint16_t *x, int64_t K, const void *wq, const float *s_w,
-                             int64_t N, int bits, int group_size, void *y, int8_t *xq_out,
-                             float *s_tok_out, int out_kind, hipStream_t stream);
+// Few-token layer on the matrix-vector path: quantizes the fp16 rows x [M, K]
+// (row stride ldx elements, M <= 8) inside the matrix-vector kernel and
+// writes y [M, N] (fp16 or bf16 by out_kind).  xq_out [M, K] / s_tok_out [M]
+// may be null; when given, the quantized rows and their scales are written
+// there as well.
+hipError_t launch_gemv_fused(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const void *wq,
+                             const float *s_w, int64_t N, int bits, int group_size, void *y,
+                             int8_t *xq_out, float *s_tok_out, int out_kind, hipStream_t stream);
 
 // The decode variant (no activation quantization): y [N] = fp16 / bf16 of
 // sum_g s_w[n, g] * sum_{k in g} x[k] * q[n, k], x fp16 [K] (16-byte aligned),

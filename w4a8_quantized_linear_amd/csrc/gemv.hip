@@ -54,6 +54,7 @@ struct GemvParams {
     const uint8_t *wq;      // int8 [N, K] or packed [N, K/2]
     const float *s_w;       // [N] or [N, G]
     int64_t M, N, K;
+    int64_t ldx;            // fused: row stride of x in elements
     int R, NSEG, SEG;       // rows per workgroup, segments per row, chunks per segment
     void *out;
     int8_t *xq_out;         // fused: optional copy of the codes
@@ -134,9 +135,11 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 constexpr uint32_t kEvenBytes = 0x06040200u;
 constexpr uint32_t kOddBytes = 0x07050301u;
 
-// BITS 8 or 4; GS 0 / 64 / 128; OUT fp16 or int32; FUSED quantizes x first;
-// XR 16-byte token chunks per thread cover the whole token data.
-template <int BITS, int GS, int OUT, bool FUSED, int XR>
+// BITS 8 or 4; GS 0 / 64 / 128; OUT fp16 or int32; FUSED 0: int8 tokens
+// given, 1: one fp16 token quantized first, 2: up to kMaxM fp16 tokens
+// quantized first (row stride ldx); XR 16-byte token chunks per thread cover
+// the whole token data.
+template <int BITS, int GS, int OUT, int FUSED, int XR>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
 {
     constexpr int KPC = BITS == 8 ? 16 : 32;  // k values per 16-byte weight chunk
@@ -149,10 +152,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
     __shared__ uint32_t red[kWaves];
     __shared__ int xsum[kMaxM];
     __shared__ int xg[kGXSum ? kMaxGroupSums : 1];                // [m][g] group sums of x
+    __shared__ uint32_t tmax[kMaxM];                              // FUSED 2: token absmax bits
+    __shared__ float stok[kMaxM];                                 // FUSED 2: token scales
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t M = FUSED ? 1 : p.M, N = p.N, K = p.K;
+    const int64_t M = FUSED == 1 ? 1 : p.M, N = p.N, K = p.K;
     const int R = p.R, NSEG = p.NSEG, SEG = p.SEG;
     const int G = GS ? (int)(K / GS) : 1;
     const int64_t n0 = (int64_t)blockIdx.x * R;
@@ -172,13 +177,27 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
     //    them.  Fused: fp16 chunks of 8 values; otherwise int8 code chunks of
     //    16.  Buffer loads return zeros past the end (no branches, so no
     //    conservative waits at join points).
-    const uint32_t xbytes = FUSED ? (uint32_t)(K * 2) : (uint32_t)(M * K);
+    const uint32_t xbytes = FUSED == 1   ? (uint32_t)(K * 2)
+                            : FUSED == 2 ? (uint32_t)(((M - 1) * p.ldx + K) * 2)
+                                         : (uint32_t)(M * K);
     const auto rx = __builtin_amdgcn_make_buffer_rsrc(FUSED ? (void *)p.x : (void *)p.xq, (short)0,
                                                       (int)xbytes, kRsrcWord3);
     uint4 xr[XR];
+    // FUSED 2: chunk c (8 values) of the [M, K] tokens is chunk c - tm * KC8
+    // of token tm = c / KC8.
+    const int KC8 = (int)(K >> 3);
+    int tm[FUSED == 2 ? XR : 1];
 #pragma unroll
-    for (int j = 0; j < XR; ++j)
-        xr[j] = load16(rx, (uint32_t)(tid + j * kThreads) * 16u);
+    for (int j = 0; j < XR; ++j) {
+        const uint32_t c = (uint32_t)(tid + j * kThreads);
+        if constexpr (FUSED == 2) {
+            tm[j] = (int)(c / (uint32_t)KC8);
+            const bool live = c < (uint32_t)(M * KC8);
+            xr[j] = load16(rx, live ? (uint32_t)((tm[j] * p.ldx + (c - tm[j] * KC8) * 8) * 2) : kDead);
+        } else {
+            xr[j] = load16(rx, c * 16u);
+        }
+    }
 
     // 2. The weight loads of this wavefront's first kEarlyUnits units, and the
     //    scales: per group, each chunk's group scale; per channel, the scale
@@ -215,16 +234,89 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
         fin_sw = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(rsw, fin ? (uint32_t)(n0 + fin_r) * 4u : kDead, 0, 0));
 
-    if constexpr (kXSum && !FUSED) {
-        if (tid < kMaxM)
+    if constexpr ((kXSum && FUSED != 1) || FUSED == 2) {
+        if (tid < kMaxM) {
             xsum[tid] = 0;
+            tmax[tid] = 0;
+        }
         __syncthreads();
     }
 
     // 3. Token codes into LDS while the weights are in flight.  For int4 the
     //    codes of each block of 32 k are stored even k first, then odd k.
     float s_fused = 0.f;
-    if constexpr (FUSED) {
+    if constexpr (FUSED == 2) {
+        // Per-token absmax: a wavefront whose 64 chunks belong to one token
+        // reduces them first; otherwise each lane adds its chunk's maximum.
+        const int nch = (int)(M * KC8);
+#pragma unroll
+        for (int j = 0; j < XR; ++j) {
+            const int c = tid + j * kThreads;
+            const uint32_t mb = c < nch ? chunk_absmax_bits(xr[j]) : 0u;
+            const int t0 = __builtin_amdgcn_readfirstlane(tm[j]);
+            const int t63 = __builtin_amdgcn_readlane(tm[j], 63);
+            if (t0 == t63) {
+                const uint32_t w = wave_max_u32(mb);
+                if (lane == 0 && t0 < M)
+                    atomicMax(&tmax[t0], w);
+            } else if (c < nch) {
+                atomicMax(&tmax[tm[j]], mb);
+            }
+        }
+        __syncthreads();
+        const bool keep = blockIdx.x == 0 && p.xq_out;
+        int mprev = -1;
+        float s = 0.f, rs = 0.f;
+#pragma unroll
+        for (int j = 0; j < XR; ++j) {
+            const int c = tid + j * kThreads;
+            int csum = 0;
+            if (c < nch) {
+                const int m = tm[j], cc = c - m * KC8;  // chunk cc of token m
+                if (m != mprev) {
+                    s = half_bits_to_float(tmax[m]) / quant_divisor<8>();
+                    rs = 1.0f / s;
+                    mprev = m;
+                }
+                const uint2 q = quantize_chunk<8>(xr[j], s, rs);
+                uint8_t *xm = sx + m * K;
+                if constexpr (BITS == 8) {
+                    *reinterpret_cast<uint2 *>(xm + cc * 8) = q;
+                } else {
+                    uint8_t *blk = xm + (cc >> 2) * 32 + (cc & 3) * 4;
+                    *reinterpret_cast<uint32_t *>(blk) = __builtin_amdgcn_perm(q.y, q.x, kEvenBytes);
+                    *reinterpret_cast<uint32_t *>(blk + 16) = __builtin_amdgcn_perm(q.y, q.x, kOddBytes);
+                    csum = __builtin_amdgcn_sdot4((int)q.x, 0x01010101, 0, false);
+                    csum = __builtin_amdgcn_sdot4((int)q.y, 0x01010101, csum, false);
+                }
+                if (cc == 0) {
+                    stok[m] = s;
+                    if (blockIdx.x == 0 && p.s_tok_out)
+                        p.s_tok_out[m] = s;
+                }
+                if (keep)
+                    *reinterpret_cast<uint2 *>(p.xq_out + (int64_t)c * 8) = q;
+            }
+            if constexpr (kXSum) {
+                // the token's code sum (int4 correction), reduced like the absmax
+                const int t0 = __builtin_amdgcn_readfirstlane(tm[j]);
+                const int t63 = __builtin_amdgcn_readlane(tm[j], 63);
+                if (t0 == t63) {
+                    const int w = wave_sum_i32(csum);
+                    if (lane == 0 && t0 < M)
+                        atomicAdd(&xsum[t0], w);
+                } else if (c < nch) {
+                    atomicAdd(&xsum[tm[j]], csum);
+                }
+            }
+            if constexpr (kGXSum) {
+                // the GS / 8 chunks of a (token, group) sit on consecutive lanes
+                const int gsum = group_sum<GS / 8>(csum);
+                if ((tid & (GS / 8 - 1)) == 0 && c < nch)
+                    xg[(c * 8) / GS] = gsum;
+            }
+        }
+    } else if constexpr (FUSED == 1) {
         const int64_t nch = K >> 3;
         uint32_t amax = 0;
 #pragma unroll
@@ -318,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
         issue(u);
     __syncthreads();
     int xs_fused = 0;
-    if constexpr (kXSum && FUSED) {
+    if constexpr (kXSum && FUSED == 1) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)
             xs_fused += ipart[w];
@@ -397,11 +489,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
             for (int sg = 0; sg < NSEG; ++sg)
                 total += ipart[m * 64 + r * NSEG + sg];
             if constexpr (kXSum)
-                total -= 8 * (FUSED ? xs_fused : xsum[m]);
+                total -= 8 * (FUSED == 1 ? xs_fused : xsum[m]);
             if constexpr (OUT == OUT_I32) {
                 static_cast<int32_t *>(p.out)[m * N + n] = total;
             } else {
-                const float st = FUSED ? s_fused : p.s_tok[m];
+                const float st = FUSED == 1 ? s_fused : FUSED == 2 ? stok[m] : p.s_tok[m];
                 const float y = (float)total * st * fin_sw;
                 static_cast<uint16_t *>(p.out)[m * N + n] = out_bits<OUT>(y);
             }
@@ -409,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
             float tot = 0.f;
             for (int sg = 0; sg < NSEG; ++sg)
                 tot += part[m * 64 + r * NSEG + sg];
-            const float st = FUSED ? s_fused : p.s_tok[m];
+            const float st = FUSED == 1 ? s_fused : FUSED == 2 ? stok[m] : p.s_tok[m];
             static_cast<uint16_t *>(p.out)[m * N + n] = out_bits<OUT>(st * tot);
         }
     }
@@ -432,25 +524,27 @@ void plan(GemvParams &p, int bits, int group_size)
     p.R = (int)(kWaves * kMaxUnitsPerWave / nseg);
 }
 
-template <int BITS, int GS, int OUT, bool FUSED, int XR>
+template <int BITS, int GS, int OUT, int FUSED, int XR>
 hipError_t launch_xr(const GemvParams &p, hipStream_t stream)
 {
     const int64_t blocks = (p.N + p.R - 1) / p.R;
-    const size_t lds = (size_t)(FUSED ? 1 : p.M) * (size_t)p.K;
+    const size_t lds = (size_t)(FUSED == 1 ? 1 : p.M) * (size_t)p.K;
     hipLaunchKernelGGL((gemv_kernel<BITS, GS, OUT, FUSED, XR>), dim3((unsigned)blocks), dim3(kThreads),
                        lds, stream, p);
     return hipGetLastError();
 }
 
-template <int BITS, int GS, int OUT, bool FUSED>
+template <int BITS, int GS, int OUT, int FUSED>
 hipError_t launch_one(GemvParams p, hipStream_t stream)
 {
     plan(p, BITS, GS);
     if (p.R < 1 || p.SEG > 64 * kMaxChunksPerLane)
         return hipErrorInvalidValue;  // K too long for the per-lane register budget
-    if (BITS == 4 && GS != 0 && (FUSED ? 1 : p.M) * p.K / (GS ? GS : 1) > kMaxGroupSums)
+    if (BITS == 4 && GS != 0 && (FUSED == 1 ? 1 : p.M) * p.K / (GS ? GS : 1) > kMaxGroupSums)
         return hipErrorInvalidValue;
-    const int64_t xchunks = FUSED ? p.K / 8 : p.M * p.K / 16;
+    if (p.M < 1 || p.M > kMaxM || (FUSED == 1 && p.M != 1))
+        return hipErrorInvalidValue;
+    const int64_t xchunks = FUSED ? p.M * p.K / 8 : p.M * p.K / 16;
     const int64_t per_thread = (xchunks + kThreads - 1) / kThreads;
     if (per_thread <= 2)
         return launch_xr<BITS, GS, OUT, FUSED, 2>(p, stream);
@@ -461,7 +555,7 @@ hipError_t launch_one(GemvParams p, hipStream_t stream)
     return hipErrorInvalidValue;
 }
 
-template <int OUT, bool FUSED>
+template <int OUT, int FUSED>
 hipError_t dispatch(const GemvParams &p, int bits, int group_size, hipStream_t stream)
 {
     if (bits == 8) {
@@ -494,29 +588,35 @@ hipError_t launch_gemv(const ProductArgs &a, hipStream_t stream)
     p.K = a.K;
     p.out = a.out;
     if (a.out_kind == OUT_F16)
-        return dispatch<OUT_F16, false>(p, a.bits, a.group_size, stream);
+        return dispatch<OUT_F16, 0>(p, a.bits, a.group_size, stream);
     if (a.out_kind == OUT_BF16)
-        return dispatch<OUT_BF16, false>(p, a.bits, a.group_size, stream);
-    return dispatch<OUT_I32, false>(p, a.bits, a.group_size, stream);
+        return dispatch<OUT_BF16, 0>(p, a.bits, a.group_size, stream);
+    return dispatch<OUT_I32, 0>(p, a.bits, a.group_size, stream);
 }
 
-hipError_t launch_gemv_fused(const uint16_t *x, int64_t K, const void *wq, const float *s_w,
-                             int64_t N, int bits, int group_size, void *y, int8_t *xq_out,
-                             float *s_tok_out, int out_kind, hipStream_t stream)
+hipError_t launch_gemv_fused(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const void *wq,
+                             const float *s_w, int64_t N, int bits, int group_size, void *y,
+                             int8_t *xq_out, float *s_tok_out, int out_kind, hipStream_t stream)
 {
     GemvParams p{};
     p.x = x;
     p.wq = static_cast<const uint8_t *>(wq);
     p.s_w = s_w;
-    p.M = 1;
+    p.M = M;
     p.N = N;
     p.K = K;
+    p.ldx = ldx;
     p.out = y;
     p.xq_out = xq_out;
     p.s_tok_out = s_tok_out;
+    if (M == 1) {
+        if (out_kind == OUT_BF16)
+            return dispatch<OUT_BF16, 1>(p, bits, group_size, stream);
+        return dispatch<OUT_F16, 1>(p, bits, group_size, stream);
+    }
     if (out_kind == OUT_BF16)
-        return dispatch<OUT_BF16, true>(p, bits, group_size, stream);
-    return dispatch<OUT_F16, true>(p, bits, group_size, stream);
+        return dispatch<OUT_BF16, 2>(p, bits, group_size, stream);
+    return dispatch<OUT_F16, 2>(p, bits, group_size, stream);
 }
 
 }  // namespace cider
