@@ -302,7 +302,7 @@ def decode_bench(torch, cider, si):
 def small_m_bench(torch, cider, si):
     """Few tokens (M = 2 .. 64), the pages' small-tile regime: whole-layer
     time per call on each operator shape, through the automatic path and,
-    where it applies (M <= 8, M * K <= 32768), forced onto the matrix-vector
+    where it applies (M <= 8, M * K <= 65536), forced onto the matrix-vector
     kernel."""
     records = []
     for name, wl in si.WORKLOADS.items():
@@ -312,13 +312,13 @@ def small_m_bench(torch, cider, si):
         xs = si.activations(64, Kw)
         ws = si.weights(Nw, Kw)
         for gs in wl["group_sizes"]:
-            for Mw in (2, 4, 8, 16, 32, 64):
+            for Mw in (2, 4, 6, 8, 16, 32, 64):
                 Bw = copies_for(wl["bits"], gs, Nw, Kw, Mw)
                 Lw = Layer(torch, cider, wl["bits"], gs, Nw, Kw, Mw, xs[:Mw], ws, Bw)
                 calls = max(Bw, 8)
                 rec = {"workload": name, "group_size": gs, "M": Mw}
                 paths = [("auto", cider.PATH_AUTO)]
-                if Mw <= 8 and Mw * Kw <= 32768:
+                if Mw <= 8 and Mw * Kw <= 65536:
                     paths.append(("matrix_vector", cider.PATH_GEMV))
                 for pname, path in paths:
                     cider.cider_set_path(path)

@@ -159,8 +159,8 @@ cider_status cider_quantize_act(const void *x_f16, int64_t M, int64_t K, int64_t
    Pipeline", step matmul_fused_dequant; "TensorOps matmul2d"; "W8A8
    Quantization Granularity").  group_size 0: per-channel s_w [N];
    64 / 128: per-group s_w [N, K/gs].  y: fp16 [M, N].
-   Up to 8 tokens (M * K <= 32768) run the matrix-vector kernel, more the
-   matrix-core kernel. */
+   Few tokens (M * K <= 65536 and M <= 8, or M <= 4 for int4 weights) run the
+   matrix-vector kernel, more the matrix-core kernel. */
 cider_status cider_w8a8_gemm(const int8_t *xq, const float *s_tok, const int8_t *wq,
                              const float *s_w, int64_t M, int64_t N, int64_t K,
                              int group_size, void *y_f16, void *stream);
@@ -212,10 +212,10 @@ size_t cider_linear_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int bits
 /* The whole layer on fp16 activations, mirroring perchannel_linear(x, w, s)
    and w4a8_linear(x, packed, s) of Cider README "Low-Level API":
    quantize_act into `workspace`, then the product.  On the matrix-vector path
-   (M <= 8 with M * K <= 32768 under the automatic path setting) the
-   quantization is fused into the matrix-vector kernel and the workspace is
-   not touched (it may be null).  x: fp16 [M, K] row stride ldx; y: fp16
-   [M, N]. */
+   (M * K <= 65536 and M <= 8, or M <= 4 for int4 weights, under the automatic
+   path setting) the quantization is fused into the matrix-vector kernel and
+   the workspace is not touched (it may be null).  x: fp16 [M, K] row stride
+   ldx; y: fp16 [M, N]. */
 cider_status cider_w8a8_linear(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
                                const int8_t *wq, const float *s_w, int64_t N, int group_size,
                                void *workspace, size_t workspace_bytes, void *y_f16,
@@ -227,7 +227,7 @@ cider_status cider_w4a8_linear(const void *x_f16, int64_t M, int64_t K, int64_t 
 
 /* The whole layer for any input / output type, with optional smoothing:
    cider_quantize_act_ex into `workspace`, then cider_gemm_ex.  fp16 tokens
-   without smoothing on the matrix-vector path (M <= 8, M * K <= 32768) are
+   without smoothing on the matrix-vector path (see cider_w8a8_linear) are
    quantized inside the matrix-vector kernel and need no workspace; every
    other call needs cider_linear_workspace_bytes(M, K) bytes of it, or cider_linear_workspace_bytes_ex(...) bytes to split K.
    Calls that share a workspace must be ordered (one stream). */
@@ -251,9 +251,9 @@ cider_status cider_decode_linear(const void *x_f16, int64_t K, const void *wq, c
                                  void *stream);
 
 /* Test hook: force the product path for subsequent calls in this process.
-   0 = automatic (M <= 8 with M * K <= 32768 -> matrix-vector, else matrix
-   cores),
-   1 = always the matrix-vector kernel (calls with M > 8 or M * K > 32768 then
+   0 = automatic (M * K <= 65536 and M <= 8, or M <= 4 for int4 weights ->
+   matrix-vector, else matrix cores),
+   1 = always the matrix-vector kernel (calls with M > 8 or M * K > 65536 then
    return CIDER_ERR_UNSUPPORTED_SHAPE), 2 = always the matrix-core kernel.
    Returns the previous setting, or -1 for an invalid value. */
 int cider_set_path(int path);

@@ -226,8 +226,13 @@ def test_linear_argument_codes():
     # the matrix-vector kernel, no workspace needed
     assert f(P, 1, 256, 256, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
     assert f(P, 8, 256, 264, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
-    # past the matrix-vector range (M * K > 32768) the workspace is required
-    assert f(P, 8, 8192, 8192, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_WORKSPACE
+    # past the matrix-vector range (M * K > 65536, or M > 4 with int4 weights)
+    # the workspace is required
+    assert f(P, 8, 8256, 8256, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_WORKSPACE
+    assert f(P, 8, 8192, 8192, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    f4 = cider.cider_w4a8_linear
+    assert f4(P, 4, 256, 256, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert f4(P, 5, 256, 256, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_WORKSPACE
 
 
 def test_forced_gemv_range():
@@ -235,6 +240,8 @@ def test_forced_gemv_range():
     assert _gemm(M=8, K=4096) == cider.CIDER_ERR_NO_DEVICE
     assert _gemm(M=9) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
     assert _gemm(M=2, K=32768 - 64 + 64 * 256) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
+    assert _gemm(M=8, K=8192) == cider.CIDER_ERR_NO_DEVICE          # M * K = 65536
+    assert _gemm(M=8, K=8192 + 64) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
 
 
 def test_raises_with_check():

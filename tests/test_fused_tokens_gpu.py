@@ -1,10 +1,10 @@
 """GPU parity of the few-token linear call on the matrix-vector path: fp16
-tokens (M <= 8, M * K <= 32768, any row stride) quantized inside the
+tokens (M <= 8, M * K <= 65536, any row stride) quantized inside the
 matrix-vector kernel.  Checked against the oracle's whole layer (fp16 / bf16
 tolerance) and, bit for bit, against the two-kernel path on the same inputs
 (quantize kernel, then the matrix-vector product of the int8 tokens).
 Shapes include K = 64 (a wavefront's chunks then span several tokens, so the
-per-token maxima and code sums take the per-lane route) and M * K = 32768."""
+per-token maxima and code sums take the per-lane route) and M * K = 65536."""
 import numpy as np
 import pytest
 
@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
 MODES = [(8, 0), (8, 64), (8, 128), (4, 0), (4, 64), (4, 128)]
 MODE_IDS = ["w8a8_pc", "w8a8_pg64", "w8a8_pg128", "w4a8_pc", "w4a8_pg64", "w4a8_pg128"]
 SHAPES = [(2, 512, 2560, 2560), (3, 320, 1024, 1088), (5, 640, 64, 64), (8, 128, 4096, 4096),
-          (7, 2560, 4096, 4160), (4, 10240, 2560, 2560), (8, 64, 64, 72), (6, 192, 5120, 5120)]
+          (7, 2560, 4096, 4160), (4, 10240, 2560, 2560), (8, 64, 64, 72), (6, 192, 5120, 5120),
+          (4, 640, 10240, 10240), (6, 320, 10240, 10304), (8, 256, 8192, 8192)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -46,7 +47,8 @@ def test_fused_tokens(M, N, K, ldx, bits, gs, y_dtype):
     if gs and K % gs:
         pytest.skip("K not a multiple of the group size")
     import torch
-    assert M * K <= 32768
+    assert M * K <= 65536
+    cider.cider_set_path(cider.PATH_GEMV)  # the matrix-vector kernel at every shape here
     orc = get_oracle()
     x = si.activations(M, ldx, seed=M * 7 + K)
     x[M // 2, : K // 2] = 0  # a half-zero token

@@ -16,7 +16,7 @@
 namespace {
 
 constexpr int64_t kMaxK = 133144;       // K * 127^2 < 2^31
-constexpr int64_t kGemvMaxBytes = 32768;  // M * K int8 codes held in LDS
+constexpr int64_t kGemvMaxBytes = 65536;  // M * K int8 codes held in LDS (kernel limit)
 constexpr int64_t kMaxOperandBytes = int64_t(1) << 31;
 constexpr int64_t kDecodeMaxK8 = 16384;   // decode kernel: chunks per lane held twice in registers
 constexpr int64_t kDecodeMaxK4 = 32768;
@@ -96,11 +96,17 @@ cider_status check_shape(int64_t M, int64_t N, int64_t K, int bits, int group_si
 enum Path { PATH_AUTO = 0, PATH_GEMV = 1, PATH_GEMM = 2 };
 
 // Which kernel serves M tokens of K features; CIDER_ERR_UNSUPPORTED_SHAPE
-// when the matrix-vector kernel is forced outside its range.
-cider_status pick_path(int64_t M, int64_t K, int *path)
+// when the matrix-vector kernel is forced outside its range.  Automatic:
+// the matrix-vector kernel (one pass over the weights, each token's dot
+// products on the vector ALUs) up to 8 int8-weight tokens or 4 int4-weight
+// tokens (whose nibble handling costs more per token), where it measured
+// faster than the matrix-core products on the operator shapes (N=10240
+// K=2560 and N=2560 K=10240, every mode).
+cider_status pick_path(int64_t M, int64_t K, int bits, int *path)
 {
     const int forced = g_path.load(std::memory_order_relaxed);
     const bool gemv_ok = M <= 8 && M * K <= kGemvMaxBytes;
+    const bool gemv_auto = gemv_ok && M <= (bits == 4 ? 4 : 8);
     if (forced == PATH_GEMV) {
         if (!gemv_ok)
             return CIDER_ERR_UNSUPPORTED_SHAPE;
@@ -108,9 +114,7 @@ cider_status pick_path(int64_t M, int64_t K, int *path)
     } else if (forced == PATH_GEMM) {
         *path = PATH_GEMM;
     } else {
-        // One pass over the weights beats the small-tile matrix-core product
-        // up to 8 tokens (measured on the operator shapes, every mode).
-        *path = gemv_ok ? PATH_GEMV : PATH_GEMM;
+        *path = gemv_auto ? PATH_GEMV : PATH_GEMM;
     }
     return CIDER_OK;
 }
@@ -130,7 +134,7 @@ cider_status run_product(const int8_t *xq, const float *s_tok, const void *wq, c
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(out) || (scaled && !aligned16(s_w)))
         return CIDER_ERR_MISALIGNED;
     int path = PATH_GEMM;
-    st = pick_path(M, K, &path);
+    st = pick_path(M, K, bits, &path);
     if (st != CIDER_OK)
         return st;
     if (!device_usable())
@@ -176,7 +180,7 @@ cider_status run_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_
         (smooth && !aligned16(smooth)))
         return CIDER_ERR_MISALIGNED;
     int path = PATH_GEMM;
-    st = pick_path(M, K, &path);
+    st = pick_path(M, K, bits, &path);
     if (st != CIDER_OK)
         return st;
     // fp16 tokens without smoothing on the matrix-vector path: quantized inside
@@ -409,7 +413,7 @@ size_t cider_linear_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int bits
     const size_t base = cider_linear_workspace_bytes(M, K);
     int path = PATH_GEMM;
     if (check_shape(M, N, K, bits, group_size) != CIDER_OK || M <= 0 || N <= 0 ||
-        pick_path(M, K, &path) != CIDER_OK || path != PATH_GEMM)
+        pick_path(M, K, bits, &path) != CIDER_OK || path != PATH_GEMM)
         return base;
     const cider::SplitPlan p = cider::plan_split(M, N, K, bits, group_size);
     return p.splits < 2 ? base : base + split_bytes(p);
