@@ -85,34 +85,14 @@ __device__ __forceinline__ uint2 chunk_codes(uint4 v, const float *__restrict__ 
     }
 }
 
+// The quantization of one row held by a team of TS lanes in v[0 .. NCH-1]
+// (chunk i * TS + lane; lanes past the row end hold a copy of its last chunk,
+// masked out here): absmax by shuffles, the scale, the codes, the stores.
 template <int TS, int NCH, int BITS, int DT, bool SMOOTH>
-__global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__restrict__ x,
-                                                            int64_t rows, int64_t len, int64_t ld,
-                                                            const float *__restrict__ smooth,
-                                                            uint8_t *__restrict__ out,
-                                                            float *__restrict__ scale,
-                                                            uint32_t *__restrict__ zero, int nzero)
+__device__ __forceinline__ void quantize_team_row(const uint4 (&v)[NCH], int64_t row, int lane, int nch,
+                                                  int64_t len, const float *__restrict__ smooth,
+                                                  uint8_t *__restrict__ out, float *__restrict__ scale)
 {
-    constexpr int TEAMS = 256 / TS;
-    if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i < nzero; i += 256)
-            zero[i] = 0u;
-    const int lane = threadIdx.x % TS;
-    const int64_t row = (int64_t)blockIdx.x * TEAMS + threadIdx.x / TS;
-    if (row >= rows)
-        return;  // a team never straddles a wavefront, so whole teams leave together
-    const uint16_t *xr = x + row * ld;
-    const int nch = (int)(len >> 3);
-    // Every load is issued before any is used: a lane past the row end
-    // re-reads the row's last chunk (an address that is always valid) and its
-    // result is masked out, so no branch separates the loads (a branch would
-    // make the compiler wait for each load at the join).
-    uint4 v[NCH];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = min(i * TS + lane, nch - 1);
-        v[i] = *reinterpret_cast<const uint4 *>(xr + (int64_t)c * 8);
-    }
     uint32_t amax = 0;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -140,6 +120,43 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__re
                 *reinterpret_cast<uint32_t *>(out + row * (len / 2) + (int64_t)c * 4) = q.x;
         }
     }
+}
+
+// A row's chunks into registers.  Every load is issued before any is used: a
+// lane past the row end re-reads the row's last chunk (an address that is
+// always valid), so no branch separates the loads (a branch would make the
+// compiler wait for each load at the join).
+template <int TS, int NCH>
+__device__ __forceinline__ void load_team_row(const uint16_t *__restrict__ xr, int lane, int nch,
+                                              uint4 (&v)[NCH])
+{
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int c = min(i * TS + lane, nch - 1);
+        v[i] = *reinterpret_cast<const uint4 *>(xr + (int64_t)c * 8);
+    }
+}
+
+template <int TS, int NCH, int BITS, int DT, bool SMOOTH>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__restrict__ x,
+                                                            int64_t rows, int64_t len, int64_t ld,
+                                                            const float *__restrict__ smooth,
+                                                            uint8_t *__restrict__ out,
+                                                            float *__restrict__ scale,
+                                                            uint32_t *__restrict__ zero, int nzero)
+{
+    constexpr int TEAMS = 256 / TS;
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < nzero; i += 256)
+            zero[i] = 0u;
+    const int lane = threadIdx.x % TS;
+    const int64_t row = (int64_t)blockIdx.x * TEAMS + threadIdx.x / TS;
+    if (row >= rows)
+        return;  // a team never straddles a wavefront, so whole teams leave together
+    const int nch = (int)(len >> 3);
+    uint4 v[NCH];
+    load_team_row<TS, NCH>(x + row * ld, lane, nch, v);
+    quantize_team_row<TS, NCH, BITS, DT, SMOOTH>(v, row, lane, nch, len, smooth, out, scale);
 }
 
 // One workgroup per row, any length: absmax pass, then a quantize pass that
