@@ -27,6 +27,14 @@
 namespace cider {
 namespace {
 
+// The weights stream through once: non-temporal loads.
+__device__ __forceinline__ uint4 load_stream(const uint8_t *p)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return uint4{v.x, v.y, v.z, v.w};
+}
+
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBlocksPerCu = 3;  // workgroups per compute unit (rows beyond: grid-stride)
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint16_t *__rest
 #pragma unroll
         for (int j = 0; j < SC; ++j) {
             const int c = min(c0 + lane + 64 * j, KC - 1);  // past the segment: masked below
-            w[j] = *reinterpret_cast<const uint4 *>(row + (int64_t)c * 16);
+            w[j] = load_stream(row + (int64_t)c * 16);
             sc[j] = GS ? s_w[rr * G + c / LPG] : (j == 0 ? s_w[rr] : 0.f);
         }
     };
