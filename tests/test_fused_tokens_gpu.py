@@ -19,7 +19,8 @@ MODES = [(8, 0), (8, 64), (8, 128), (4, 0), (4, 64), (4, 128)]
 MODE_IDS = ["w8a8_pc", "w8a8_pg64", "w8a8_pg128", "w4a8_pc", "w4a8_pg64", "w4a8_pg128"]
 SHAPES = [(2, 512, 2560, 2560), (3, 320, 1024, 1088), (5, 640, 64, 64), (8, 128, 4096, 4096),
           (7, 2560, 4096, 4160), (4, 10240, 2560, 2560), (8, 64, 64, 72), (6, 192, 5120, 5120),
-          (4, 640, 10240, 10240), (6, 320, 10240, 10304), (8, 256, 8192, 8192)]
+          (4, 640, 10240, 10240), (6, 320, 10240, 10304), (8, 256, 8192, 8192),
+          (1, 192, 40960, 40960), (1, 512, 32768, 32768)]
 
 
 @pytest.fixture(scope="module", autouse=True)

@@ -9,7 +9,8 @@
 // HBM busy:
 //   * a workgroup owns R consecutive weight rows (contiguous in memory), split
 //     into NSEG K-segments of at most 3 16-byte chunks per lane; the R * NSEG
-//     (row, segment) units are dealt round-robin to its 8 wavefronts, 5 each;
+//     (row, segment) units are dealt round-robin to its 4 (one token) or 8
+//     wavefronts, 5 each;
 //   * each wavefront loads the token first, then issues the loads of its first
 //     two units (adjacent lanes, adjacent 16 bytes); the fused activation
 //     quantization (or the copy of the int8 tokens into LDS) runs while they
@@ -32,8 +33,11 @@
 namespace cider {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
+// Threads per workgroup: 256 for one fused token (4-5% faster per call at
+// the per-group and int4 shapes than 512), 512 otherwise (the token data of
+// up to M * K = 65536 codes spread over more threads' registers).
+constexpr int threads_for(int fused) { return fused == 1 ? 256 : 512; }
+constexpr int kMaxWaves = 8;
 constexpr int kMaxM = 8;
 constexpr int kMaxUnitsPerWave = 5;
 constexpr int kMaxChunksPerLane = 3;  // per unit: SEG <= 192
@@ -148,8 +152,10 @@ constexpr uint32_t kOddBytes = 0x07050301u;
 // quantized first (row stride ldx); XR 16-byte token chunks per thread cover
 // the whole token data.
 template <int BITS, int GS, int OUT, int FUSED, int XR>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
+__global__ __launch_bounds__(threads_for(FUSED)) void gemv_kernel(GemvParams p)
 {
+    constexpr int kThreads = threads_for(FUSED);
+    constexpr int kWaves = kThreads / 64;
     constexpr int KPC = BITS == 8 ? 16 : 32;  // k values per 16-byte weight chunk
     constexpr int LPG = GS ? GS / KPC : 1;    // lanes holding one group (chunks per group)
     constexpr bool kXSum = BITS == 4 && GS == 0;   // the -8 sum(x) correction, per token
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
     extern __shared__ __attribute__((aligned(16))) uint8_t sx[];  // [M][K] int8 codes
     __shared__ float part[kMaxM * 64];                            // [m][unit] partials
     __shared__ int ipart[kMaxM * 64];
-    __shared__ uint32_t red[kWaves];
+    __shared__ uint32_t red[kMaxWaves];
     __shared__ int xsum[kMaxM];
     __shared__ int xg[kGXSum ? kMaxGroupSums : 1];                // [m][g] group sums of x
     __shared__ uint32_t tmax[kMaxM];                              // FUSED 2: token absmax bits
@@ -517,10 +523,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
 
 // Split of the weight rows: NSEG = ceil(chunks / 192) segments of SEG chunks
 // (at most 3 per lane, whole groups; the last may be shorter), and as many
-// rows per workgroup as fit 40 units (5 per wavefront).  One workgroup of 8
-// wavefronts per compute unit at the decoder shapes: the token quantization
-// that every workgroup repeats is then spread over 512 threads.
-void plan(GemvParams &p, int bits, int group_size)
+// rows per workgroup as fit 5 units per wavefront (40 with 8 wavefronts, 20
+// with 4).
+void plan(GemvParams &p, int bits, int group_size, int waves)
 {
     const int KPC = bits == 8 ? 16 : 32;
     const int64_t KC = p.K / KPC;
@@ -529,7 +534,7 @@ void plan(GemvParams &p, int bits, int group_size)
     const int64_t seg = ((KC + nseg - 1) / nseg + lpg - 1) / lpg * lpg;
     p.NSEG = (int)nseg;
     p.SEG = (int)seg;
-    p.R = (int)(kWaves * kMaxUnitsPerWave / nseg);
+    p.R = (int)(waves * kMaxUnitsPerWave / nseg);
 }
 
 template <int BITS, int GS, int OUT, int FUSED, int XR>
@@ -537,7 +542,7 @@ hipError_t launch_xr(const GemvParams &p, hipStream_t stream)
 {
     const int64_t blocks = (p.N + p.R - 1) / p.R;
     const size_t lds = (size_t)(FUSED == 1 ? 1 : p.M) * (size_t)p.K;
-    hipLaunchKernelGGL((gemv_kernel<BITS, GS, OUT, FUSED, XR>), dim3((unsigned)blocks), dim3(kThreads),
+    hipLaunchKernelGGL((gemv_kernel<BITS, GS, OUT, FUSED, XR>), dim3((unsigned)blocks), dim3(threads_for(FUSED)),
                        lds, stream, p);
     return hipGetLastError();
 }
@@ -545,7 +550,8 @@ hipError_t launch_xr(const GemvParams &p, hipStream_t stream)
 template <int BITS, int GS, int OUT, int FUSED>
 hipError_t launch_one(GemvParams p, hipStream_t stream)
 {
-    plan(p, BITS, GS);
+    constexpr int kThreads = threads_for(FUSED);
+    plan(p, BITS, GS, kThreads / 64);
     if (p.R < 1 || p.SEG > 64 * kMaxChunksPerLane)
         return hipErrorInvalidValue;  // K too long for the per-lane register budget
     if (BITS == 4 && GS != 0 && (FUSED == 1 ? 1 : p.M) * p.K / (GS ? GS : 1) > kMaxGroupSums)
@@ -617,7 +623,9 @@ hipError_t launch_gemv_fused(const uint16_t *x, int64_t M, int64_t K, int64_t ld
     p.out = y;
     p.xq_out = xq_out;
     p.s_tok_out = s_tok_out;
-    if (M == 1) {
+    // one token of up to 256 * 16 chunks of 8 values: the one-token kernel;
+    // a longer one goes to the several-token kernel (512 threads hold it)
+    if (M == 1 && K / 8 <= threads_for(1) * 16) {
         if (out_kind == OUT_BF16)
             return dispatch<OUT_BF16, 1>(p, bits, group_size, stream);
         return dispatch<OUT_F16, 1>(p, bits, group_size, stream);
