@@ -6,10 +6,12 @@
 //
 // A "team" of TS lanes owns one row: it loads the row once in 16-byte
 // chunks (8 fp16 per lane per chunk, adjacent lanes adjacent in memory),
-// keeps it in registers, reduces the absmax with cross-lane shuffles, then
-// writes the codes (8 bytes or 4 packed bytes per chunk, again contiguous
-// across lanes) and the scale.  Short rows (weight groups of 64 / 128) use
-// teams of 8 / 16 lanes so a wavefront still covers 512 bytes per load.
+// keeps it in registers, reduces the absmax with cross-lane shuffles (a
+// whole-workgroup team also through LDS), then writes the codes (8 bytes or
+// 4 packed bytes per chunk, again contiguous across lanes) and the scale.
+// Short rows (weight groups of 64 / 128) use teams of 8 / 16 lanes so a
+// wavefront still covers 512 bytes per load; long rows use teams of 64 or,
+// when few or very long, of 256 lanes.
 // Rows longer than the register budget take a two-pass kernel that re-reads
 // the row from cache.
 //
@@ -100,10 +102,27 @@ __device__ __forceinline__ void quantize_team_row(const uint4 (&v)[NCH], int64_t
         const uint32_t m = chunk_amax<DT, SMOOTH>(v[i], smooth, min(c, nch - 1));
         amax = (c < nch && m > amax) ? m : amax;
     }
+    if constexpr (TS <= 64) {
 #pragma unroll
-    for (int o = TS / 2; o > 0; o >>= 1) {
-        const uint32_t other = (uint32_t)__shfl_xor((int)amax, o, TS);
-        amax = other > amax ? other : amax;
+        for (int o = TS / 2; o > 0; o >>= 1) {
+            const uint32_t other = (uint32_t)__shfl_xor((int)amax, o, TS);
+            amax = other > amax ? other : amax;
+        }
+    } else {
+        // a whole workgroup per row: wavefront maxima meet in LDS
+        __shared__ uint32_t red[TS / 64];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const uint32_t other = (uint32_t)__shfl_xor((int)amax, o, 64);
+            amax = other > amax ? other : amax;
+        }
+        if ((lane & 63) == 0)
+            red[lane >> 6] = amax;
+        __syncthreads();
+        amax = red[0];
+#pragma unroll
+        for (int w = 1; w < TS / 64; ++w)
+            amax = red[w] > amax ? red[w] : amax;
     }
     const float s = amax_value<DT, SMOOTH>(amax) / quant_divisor<BITS>();
     const float rs = 1.0f / s;
@@ -233,6 +252,25 @@ hipError_t launch_bits(const uint16_t *x, int64_t rows, int64_t len, int64_t ld,
         return launch_team<16, 1, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream, zero, nzero);
     if (nch <= 32)
         return launch_team<32, 1, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream, zero, nzero);
+    // Rows of more than 256 chunks, when there are few of them (up to 512)
+    // or they are long (1024 chunks and more): a whole workgroup per row, so
+    // each lane holds at most 8 chunks and the row's loads and codes spread
+    // over 4 wavefronts (K = 10240: M = 16 8.2 -> 3.9 us, M = 4096 35.8 ->
+    // 27.3 us; at K = 2560 and thousands of rows a wavefront per row stays
+    // faster).
+    if (nch > 256 && nch <= 256 * 8 && (rows <= 512 || nch >= 1024)) {
+        const int64_t pl = (nch + 255) / 256;
+#define CIDER_TEAM256(n)                                                                         \
+    if (pl <= n)                                                                                 \
+        return launch_team<256, n, BITS, DT, SMOOTH>(x, rows, len, ld, smooth, out, scale, stream, zero, nzero);
+        CIDER_TEAM256(2)
+        CIDER_TEAM256(3)
+        CIDER_TEAM256(4)
+        CIDER_TEAM256(5)
+        CIDER_TEAM256(6)
+        CIDER_TEAM256(8)
+#undef CIDER_TEAM256
+    }
     const int64_t per_lane = (nch + 63) / 64;
 #define CIDER_TEAM64(n)                                                                          \
     if (per_lane <= n)                                                                           \
