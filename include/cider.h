@@ -242,8 +242,7 @@ cider_status cider_linear_ex(const void *x, int x_dtype, int64_t M, int64_t K, i
      y[n] = sum_g s_w[n, g] * sum_{k in g} x[k] * q[n, k]
    (per channel: one group of K), accumulated in fp32 and rounded once to
    y_dtype.  x fp16 [K]; wq / s_w as for the products (bits 8 or 4, group_size
-   0 / 64 / 128); y [N].  K % 64 == 0 and K <= 16384 (bits 8) or 32768
-   (bits 4); any N >= 0.  Unlike the W8A8 one-token path, the result is not
+   0 / 64 / 128); y [N].  K % 64 == 0 and K <= 32768; any N >= 0.  Unlike the W8A8 one-token path, the result is not
    that of the quantized-activation formula: it is the dequantized-weight
    product, the other reading of the pages' decode step. */
 cider_status cider_decode_linear(const void *x_f16, int64_t K, const void *wq, const float *s_w,

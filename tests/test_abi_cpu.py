@@ -207,7 +207,8 @@ def test_decode_argument_codes():
     dl = cider.cider_decode_linear
     assert dl(P, 1024, P2, P3, 100, 8, 0, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
     assert dl(P, 32768, P2, P3, 64, 4, 128, 1, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
-    assert dl(P, 32768, P2, P3, 64, 8, 0, 0, P, stream=0, check=False) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
+    assert dl(P, 32768, P2, P3, 64, 8, 0, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert dl(P, 32832, P2, P3, 64, 8, 0, 0, P, stream=0, check=False) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
     assert dl(P, 1000, P2, P3, 64, 8, 0, 0, P, stream=0, check=False) == cider.CIDER_ERR_UNSUPPORTED_SHAPE
     assert dl(P, 1024, P2, P3, 64, 8, 32, 0, P, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
     assert dl(P, 1024, P2, P3, 64, 8, 0, 3, P, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG

@@ -304,8 +304,6 @@ def test_decode_linear(N, K, bits, gs, y_dtype):
     summation error of at most ~100 sequential additions is below 2^-17 of it)."""
     if gs and K % gs:
         pytest.skip("K not a multiple of the group size")
-    if bits == 8 and K > 16384:
-        pytest.skip("int8 decode envelope: K <= 16384")
     import torch
     orc = get_oracle()
     x = si.activations(1, K, seed=N + K)[0]

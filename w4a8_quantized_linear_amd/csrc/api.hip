@@ -18,8 +18,7 @@ namespace {
 constexpr int64_t kMaxK = 133144;       // K * 127^2 < 2^31
 constexpr int64_t kGemvMaxBytes = 65536;  // M * K int8 codes held in LDS (kernel limit)
 constexpr int64_t kMaxOperandBytes = int64_t(1) << 31;
-constexpr int64_t kDecodeMaxK8 = 16384;   // decode kernel: chunks per lane held twice in registers
-constexpr int64_t kDecodeMaxK4 = 32768;
+constexpr int64_t kDecodeMaxK = 32768;  // decode kernel: 16 activation chunks per thread, x [K] in LDS
 
 std::atomic<int> g_path{0};
 
@@ -452,7 +451,7 @@ cider_status cider_decode_linear(const void *x_f16, int64_t K, const void *wq, c
         return CIDER_ERR_INVALID_ARG;
     if (group_size != 0 && group_size != 64 && group_size != 128)
         return CIDER_ERR_INVALID_ARG;
-    if (K % 64 != 0 || K > (bits == 8 ? kDecodeMaxK8 : kDecodeMaxK4) ||
+    if (K % 64 != 0 || K > kDecodeMaxK ||
         (group_size && K % group_size != 0))
         return CIDER_ERR_UNSUPPORTED_SHAPE;
     if (N == 0)
