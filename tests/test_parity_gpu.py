@@ -181,7 +181,8 @@ def _smoothing(K, seed):
 @pytest.mark.parametrize("smooth", [False, True])
 @pytest.mark.parametrize("dtype", [0, 1])
 @pytest.mark.parametrize("M,K,ldx", [(64, 1024, 1024), (37, 2560, 2624), (5, 10240, 10240),
-                                     (3, 20480, 20480), (130, 256, 264), (1, 64, 64)])
+                                     (3, 20480, 20480), (130, 256, 264), (1, 64, 64),
+                                     (600, 6144, 6144)])
 def test_quantize_act_ex_bitexact(M, K, ldx, dtype, smooth):
     """fp16 / bf16 activations, with and without a smoothing vector:
     codes and scales bit-exact (including a zero token and exact ties)."""

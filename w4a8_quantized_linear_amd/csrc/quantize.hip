@@ -87,21 +87,11 @@ __device__ __forceinline__ uint2 chunk_codes(uint4 v, const float *__restrict__ 
     }
 }
 
-// The quantization of one row held by a team of TS lanes in v[0 .. NCH-1]
-// (chunk i * TS + lane; lanes past the row end hold a copy of its last chunk,
-// masked out here): absmax by shuffles, the scale, the codes, the stores.
-template <int TS, int NCH, int BITS, int DT, bool SMOOTH>
-__device__ __forceinline__ void quantize_team_row(const uint4 (&v)[NCH], int64_t row, int lane, int nch,
-                                                  int64_t len, const float *__restrict__ smooth,
-                                                  uint8_t *__restrict__ out, float *__restrict__ scale)
+// The largest magnitude bits over a team of TS lanes (a whole-workgroup team
+// also through LDS); every lane of the team gets the result.
+template <int TS>
+__device__ __forceinline__ uint32_t team_max(uint32_t amax, int lane)
 {
-    uint32_t amax = 0;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = i * TS + lane;
-        const uint32_t m = chunk_amax<DT, SMOOTH>(v[i], smooth, min(c, nch - 1));
-        amax = (c < nch && m > amax) ? m : amax;
-    }
     if constexpr (TS <= 64) {
 #pragma unroll
         for (int o = TS / 2; o > 0; o >>= 1) {
@@ -109,7 +99,6 @@ __device__ __forceinline__ void quantize_team_row(const uint4 (&v)[NCH], int64_t
             amax = other > amax ? other : amax;
         }
     } else {
-        // a whole workgroup per row: wavefront maxima meet in LDS
         __shared__ uint32_t red[TS / 64];
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
@@ -124,6 +113,43 @@ __device__ __forceinline__ void quantize_team_row(const uint4 (&v)[NCH], int64_t
         for (int w = 1; w < TS / 64; ++w)
             amax = red[w] > amax ? red[w] : amax;
     }
+    return amax;
+}
+
+// The quantization of one row held by a team of TS lanes in v[0 .. NCH-1]
+// (chunk i * TS + lane; lanes past the row end hold a copy of its last chunk,
+// masked out here): absmax by shuffles, the scale, the codes, the stores.
+// With smoothing and at most 8 chunks per lane, each value's quotient by its
+// smoothing factor is computed once and kept for both the absmax and the
+// codes (the same divisions, half as many); longer rows recompute it.
+template <int TS, int NCH, int BITS, int DT, bool SMOOTH>
+__device__ __forceinline__ void quantize_team_row(const uint4 (&v)[NCH], int64_t row, int lane, int nch,
+                                                  int64_t len, const float *__restrict__ smooth,
+                                                  uint8_t *__restrict__ out, float *__restrict__ scale)
+{
+    constexpr bool KEEP = SMOOTH && NCH <= 8;
+    float fs[KEEP ? NCH : 1][8];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int c = i * TS + lane;
+        uint32_t m;
+        if constexpr (KEEP) {
+            float l[8];
+            load_smooth(smooth, min(c, nch - 1), l);
+            smooth_chunk<DT>(v[i], l, fs[i]);
+            m = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t b = __builtin_bit_cast(uint32_t, fs[i][e]) & 0x7FFFFFFFu;
+                m = b > m ? b : m;
+            }
+        } else {
+            m = chunk_amax<DT, SMOOTH>(v[i], smooth, min(c, nch - 1));
+        }
+        amax = (c < nch && m > amax) ? m : amax;
+    }
+    amax = team_max<TS>(amax, lane);
     const float s = amax_value<DT, SMOOTH>(amax) / quant_divisor<BITS>();
     const float rs = 1.0f / s;
     if (lane == 0)
@@ -132,7 +158,11 @@ __device__ __forceinline__ void quantize_team_row(const uint4 (&v)[NCH], int64_t
     for (int i = 0; i < NCH; ++i) {
         const int c = i * TS + lane;
         if (c < nch) {
-            const uint2 q = chunk_codes<BITS, DT, SMOOTH, (NCH <= 8)>(v[i], smooth, c, s, rs);
+            uint2 q;
+            if constexpr (KEEP)
+                q = quantize_values<BITS>(fs[i], s, rs);
+            else
+                q = chunk_codes<BITS, DT, SMOOTH, (NCH <= 8)>(v[i], smooth, c, s, rs);
             if constexpr (BITS == 8)
                 *reinterpret_cast<uint2 *>(out + row * len + (int64_t)c * 8) = q;
             else
