@@ -182,10 +182,11 @@ __device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off
 
 // Each workgroup runs once.  The memory counter retires loads in order, so
 // the loads go out in the order they are needed: the activation chunks (XR
-// per thread), then every unit's weight chunks (and per group their scales),
-// then the row scale of the output this thread finishes; the activation is
-// written to LDS as soon as its own loads are back, and each unit's dot
-// products start as soon as that unit's weights are.  Unit sums meet in LDS
+// per thread), the first kEarly units' weight chunks (and per group their
+// scales) and the row scale of the output this thread finishes; the
+// activation is written to LDS as soon as its own loads are back, then the
+// remaining units' loads go out, and each unit's dot products start as soon
+// as that unit's weights are in.  Unit sums meet in LDS
 // and a row's segments are added in segment order (results do not depend on
 // timing).  Rows and chunks past the end read zeros through the buffer
 // descriptors' range checks and are never stored.
