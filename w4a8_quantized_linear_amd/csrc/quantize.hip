@@ -204,7 +204,8 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__re
     const int lane = threadIdx.x % TS;
     const int64_t row = (int64_t)blockIdx.x * TEAMS + threadIdx.x / TS;
     if (row >= rows)
-        return;  // a team never straddles a wavefront, so whole teams leave together
+        return;  // a team is part of one wavefront or the whole workgroup: whole teams
+                 // leave together (a 256-lane team's LDS barrier is reached by all or none)
     const int nch = (int)(len >> 3);
     uint4 v[NCH];
     load_team_row<TS, NCH>(x + row * ld, lane, nch, v);
