@@ -43,7 +43,7 @@ def _announce(request):
 
 ACT_SHAPES = [(64, 1024, 1024), (37, 2560, 2624), (5, 10240, 10240), (3, 12288, 12288),
               (2, 20480, 20480), (1, 64, 64), (1000, 128, 136), (9, 4096, 4096),
-              (7, 6144, 6152), (4, 16384, 16384), (600, 10240, 10240)]
+              (7, 6144, 6152), (11, 8192, 8200), (4, 16384, 16384), (600, 10240, 10240)]
 
 
 @pytest.mark.parametrize("M,K,ldx", ACT_SHAPES)
