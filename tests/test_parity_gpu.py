@@ -122,7 +122,7 @@ WEIGHT_CASES = [(512, 1024, 8, 0), (512, 1024, 8, 64), (512, 1024, 8, 128), (512
                 (10240, 2560, 8, 0), (2560, 10240, 8, 64), (2560, 10240, 8, 128),
                 (10240, 2560, 4, 0), (64, 20480, 8, 0), (64, 20480, 4, 0),
                 (512, 1024, 4, 64), (512, 1024, 4, 128), (2560, 10240, 4, 64),
-                (2560, 10240, 4, 128)]
+                (2560, 10240, 4, 128), (512, 4096, 8, 0), (256, 8192, 4, 0)]
 
 
 @pytest.mark.parametrize("N,K,bits,gs", WEIGHT_CASES)
