@@ -34,7 +34,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnits = 5;   // (row, segment) units per wavefront
-constexpr int kChunks = 3;  // 16-byte chunks per lane and unit
+constexpr int kChunks = 3;  // 16-byte chunks per lane and unit, at most
 constexpr int kEarly = 2;   // units whose loads go out before x is written to LDS
 static_assert(kWaves * kUnits <= kThreads, "one finishing thread per row");
 
@@ -190,7 +190,7 @@ __device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off
 // and a row's segments are added in segment order (results do not depend on
 // timing).  Rows and chunks past the end read zeros through the buffer
 // descriptors' range checks and are never stored.
-template <int BITS, int GS, int OUT, int XR>
+template <int BITS, int GS, int OUT, int XR, int SC>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // x [K]
@@ -218,13 +218,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
                                                       (int)(rows * wld), kRsrcWord3);
     const auto rs = __builtin_amdgcn_make_buffer_rsrc((void *)(p.s_w + n0 * G), (short)0,
                                                       rows * G * 4, kRsrcWord3);
-    uint4 wv[kUnits][kChunks];
-    float swv[GS ? kUnits : 1][GS ? kChunks : 1];
+    uint4 wv[kUnits][SC];
+    float swv[GS ? kUnits : 1][GS ? SC : 1];
     auto issue = [&](int u) __attribute__((always_inline)) {
         const int unit = wave + u * kWaves;
         const int r = unit / NSEG, sg = unit % NSEG;
 #pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
+        for (int i = 0; i < SC; ++i) {
             const int c = lane + 64 * i, kc = sg * SEG + c;
             const bool live = unit < units && c < SEG && kc < KC;
             wv[u][i] = load16_stream(rw, live ? (uint32_t)r * wld + (uint32_t)kc * 16u : kDead);
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p)
         const int sg = unit % NSEG;
         float total = 0.f;
 #pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
+        for (int i = 0; i < SC; ++i) {
             if (64 * i >= SEG)  // wavefront-uniform: no lane holds a chunk here
                 break;
             const int c = lane + 64 * i, kc = sg * SEG + c;
@@ -293,8 +293,14 @@ template <int BITS, int GS, int OUT, int XR>
 hipError_t launch_xr(const DecodeParams &p, hipStream_t stream)
 {
     const int64_t blocks = (p.N + p.R - 1) / p.R;
-    hipLaunchKernelGGL((decode_kernel<BITS, GS, OUT, XR>), dim3((unsigned)blocks), dim3(kThreads),
-                       (size_t)p.K * 2, stream, p);
+    // chunk slots per lane: 2 when a segment fits in 128 chunks (no load
+    // instructions for a slot no lane uses), else 3
+    if (p.SEG <= 128)
+        hipLaunchKernelGGL((decode_kernel<BITS, GS, OUT, XR, 2>), dim3((unsigned)blocks), dim3(kThreads),
+                           (size_t)p.K * 2, stream, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<BITS, GS, OUT, XR, kChunks>), dim3((unsigned)blocks), dim3(kThreads),
+                           (size_t)p.K * 2, stream, p);
     return hipGetLastError();
 }
 
