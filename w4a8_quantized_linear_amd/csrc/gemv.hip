@@ -8,7 +8,10 @@
 // The work is one pass over the weight matrix, so the kernel is built to keep
 // HBM busy:
 //   * a workgroup owns R consecutive weight rows (contiguous in memory), split
-//     into NSEG K-segments of at most 3 16-byte chunks per lane; the R * NSEG
+//     into NSEG K-segments of at most 3 16-byte chunks per lane (a kernel
+//     instance with 2 chunk slots when a segment fits in 128 chunks, so no
+//     load goes out for a slot no lane uses: int4 one-token calls at K = 2560
+//     5.86 -> 5.14 us); the R * NSEG
 //     (row, segment) units are dealt round-robin to its 4 (one token) or 8
 //     wavefronts, 5 each;
 //   * each wavefront loads the token first, then issues the loads of its first
@@ -40,7 +43,7 @@ constexpr int threads_for(int fused) { return fused == 1 ? 256 : 512; }
 constexpr int kMaxWaves = 8;
 constexpr int kMaxM = 8;
 constexpr int kMaxUnitsPerWave = 5;
-constexpr int kMaxChunksPerLane = 3;  // per unit: SEG <= 192
+constexpr int kMaxChunksPerLane = 3;  // per unit: SEG <= 192 (an instance with 2 serves SEG <= 128)
 constexpr int kEarlyUnits = 2;        // units whose loads go out before the token is quantized
 constexpr int kMaxGroupSums = 1024;   // int4 per group: (token, group) sums of the token codes
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor: raw 32-bit dwords, range-checked
@@ -151,7 +154,7 @@ constexpr uint32_t kOddBytes = 0x07050301u;
 // given, 1: one fp16 token quantized first, 2: up to kMaxM fp16 tokens
 // quantized first (row stride ldx); XR 16-byte token chunks per thread cover
 // the whole token data.
-template <int BITS, int GS, int OUT, int FUSED, int XR>
+template <int BITS, int GS, int OUT, int FUSED, int XR, int SC>
 __global__ __launch_bounds__(threads_for(FUSED)) void gemv_kernel(GemvParams p)
 {
     constexpr int kThreads = threads_for(FUSED);
@@ -221,14 +224,14 @@ __global__ __launch_bounds__(threads_for(FUSED)) void gemv_kernel(GemvParams p)
     //    alone keep enough bytes in flight.
     const auto rw = __builtin_amdgcn_make_buffer_rsrc((void *)p.wq, (short)0, (int)(N * wld), kRsrcWord3);
     const auto rsw = __builtin_amdgcn_make_buffer_rsrc((void *)p.s_w, (short)0, (int)(N * G * 4), kRsrcWord3);
-    uint4 wv[kMaxUnitsPerWave][kMaxChunksPerLane];
-    float swv[kMaxUnitsPerWave][kMaxChunksPerLane];
+    uint4 wv[kMaxUnitsPerWave][SC];
+    float swv[kMaxUnitsPerWave][SC];
     auto issue = [&](int u) __attribute__((always_inline)) {
         int r, sg;
         const bool valid = unit_of(u, r, sg);
         const uint32_t n = (uint32_t)min(n0 + r, N - 1);  // rows past N: any valid row, never stored
 #pragma unroll
-        for (int i = 0; i < kMaxChunksPerLane; ++i) {
+        for (int i = 0; i < SC; ++i) {
             const int c = lane + 64 * i;
             const uint32_t kc = (uint32_t)(sg * SEG + c);
             const bool live = valid && c < SEG && kc < (uint32_t)KC;
@@ -445,7 +448,7 @@ __global__ __launch_bounds__(threads_for(FUSED)) void gemv_kernel(GemvParams p)
             int isum = 0;
             float fsum = 0.f;
 #pragma unroll
-            for (int i = 0; i < kMaxChunksPerLane; ++i) {
+            for (int i = 0; i < SC; ++i) {
                 const int c = lane + 64 * i;
                 const bool live = c < SEG && (int64_t)sg * SEG + c < KC;
                 const int64_t kc = (int64_t)sg * SEG + (live ? c : 0);  // chunk index within the row
@@ -542,8 +545,14 @@ hipError_t launch_xr(const GemvParams &p, hipStream_t stream)
 {
     const int64_t blocks = (p.N + p.R - 1) / p.R;
     const size_t lds = (size_t)(FUSED == 1 ? 1 : p.M) * (size_t)p.K;
-    hipLaunchKernelGGL((gemv_kernel<BITS, GS, OUT, FUSED, XR>), dim3((unsigned)blocks), dim3(threads_for(FUSED)),
-                       lds, stream, p);
+    // chunk slots per lane: 2 when a segment fits in 128 chunks (no load
+    // instructions for a slot no lane uses), else 3
+    if (p.SEG <= 128)
+        hipLaunchKernelGGL((gemv_kernel<BITS, GS, OUT, FUSED, XR, 2>), dim3((unsigned)blocks),
+                           dim3(threads_for(FUSED)), lds, stream, p);
+    else
+        hipLaunchKernelGGL((gemv_kernel<BITS, GS, OUT, FUSED, XR, kMaxChunksPerLane>), dim3((unsigned)blocks),
+                           dim3(threads_for(FUSED)), lds, stream, p);
     return hipGetLastError();
 }
 
