@@ -219,6 +219,90 @@ def test_quantize_weight_bf16_bitexact(N, K, bits, gs, p):
     assert np.array_equal(gu.to_host(wq), rq)
 
 
+# Row magnitudes whose fp32 scale is not a normal number: absmax / 127 below
+# 2^-126 (and for 2^-133, the smallest bf16, a scale whose reciprocal
+# overflows).  1e-30 stays normal, as a control.
+TINY_AMAX = [1e-36, 3e-37, 1e-38, 2.0 ** -133, 1e-30]
+
+
+def _tiny_rows(amaxes, K, seed):
+    """float32 rows of N(0,1) values rescaled to the given absmax, each with
+    zeros, +-absmax, +-absmax/2 and +-absmax/4 at fixed positions."""
+    rng = np.random.default_rng([seed, 5])
+    rows = []
+    for a in amaxes:
+        r = rng.standard_normal(K).astype(np.float64)
+        r = r / np.abs(r).max() * a
+        r[:8] = [0.0, a, -a, a / 2, -a / 2, a / 4, 0.0, -a]
+        rows.append(r.astype(np.float32))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("K", [64, 256, 1024, 2560, 10240, 20480])
+def test_quantize_act_tiny_scales_bitexact(K):
+    """bf16 tokens whose scale is subnormal in fp32 (and one whose reciprocal
+    overflows), mixed with ordinary tokens: codes and scales bit-exact.  K
+    spans every team size of the quantize kernel and its long-row kernel."""
+    import torch
+    orc = get_oracle()
+    x = np.concatenate([_tiny_rows(TINY_AMAX, K, K), si.activations(3, K, seed=K).astype(np.float32)])
+    xb = gu.bf16_bits(x)
+    M = xb.shape[0]
+    xq = gu.empty((M, K), torch.int8)
+    st = gu.empty((M,), torch.float32)
+    cider.cider_quantize_act_ex(gu.bits_to_dev(xb), 1, M, K, K, None, xq, st)
+    rq, rs = orc.quantize_act_ex(xb, 1, K=K)
+    assert np.any((rs > 0) & (rs < 2.0 ** -126)), "the rows must give subnormal scales"
+    assert np.array_equal(gu.to_host(st), rs)
+    assert np.array_equal(gu.to_host(xq), rq)
+
+
+@pytest.mark.parametrize("K", [256, 1024, 10240, 20480])
+def test_quantize_act_huge_smoothing_bitexact(K):
+    """fp16 tokens divided by smoothing factors of 1e38 .. 3e38: the smoothed
+    values, and so the scales, fall below the normal fp32 range (tokens 2-3
+    scaled by 1/64 give scales whose reciprocal overflows); codes and scales
+    bit-exact against the oracle."""
+    import torch
+    orc = get_oracle()
+    x = si.activations(6, K, seed=K)
+    x[1, :8] = np.array([0, 1, -1, 0.5, -0.5, 0.25, 0, 3], np.float16)
+    x[2:4] = (x[2:4].astype(np.float32) / 64).astype(np.float16)
+    xb = x.view(np.uint16)
+    sm = (np.random.default_rng([K, 9]).uniform(1.0, 3.0, K) * 1e38).astype(np.float32)
+    M = x.shape[0]
+    xq = gu.empty((M, K), torch.int8)
+    st = gu.empty((M,), torch.float32)
+    cider.cider_quantize_act_ex(gu.bits_to_dev(xb), 0, M, K, K, gu.to_dev(sm), xq, st)
+    rq, rs = orc.quantize_act_ex(xb, 0, K=K, smooth=sm)
+    assert np.all(rs < 2.0 ** -126), "the smoothed rows must give subnormal scales"
+    assert np.array_equal(gu.to_host(st), rs)
+    assert np.array_equal(gu.to_host(xq), rq)
+
+
+@pytest.mark.parametrize("p", [100.0, 99.9])
+@pytest.mark.parametrize("bits,gs", MODES, ids=MODE_IDS)
+def test_quantize_weight_bf16_tiny_scales_bitexact(bits, gs, p):
+    """bf16 weight rows (and groups) whose scale, absmax / 127 or / 7, is
+    subnormal in fp32: codes and scales bit-exact."""
+    import torch
+    orc = get_oracle()
+    N, K = 64, 1024
+    w = si.weights(N, K, seed=3).astype(np.float32)
+    w[:len(TINY_AMAX)] = _tiny_rows(TINY_AMAX, K, 11)
+    w[8:8 + len(TINY_AMAX)] = _tiny_rows(TINY_AMAX, K, 12) * 7.0 / 127.0
+    if gs:
+        w[20, :gs] = _tiny_rows([1e-37], gs, 13)[0]          # one tiny group in a normal row
+    wb = gu.bf16_bits(w)
+    wq = gu.empty((N, K) if bits == 8 else (N, K // 2), torch.int8 if bits == 8 else torch.uint8)
+    sw = gu.empty((N,) if gs == 0 else (N, K // gs), torch.float32)
+    cider.cider_quantize_weight_ex(gu.bits_to_dev(wb), 1, N, K, bits, gs, p, wq, sw)
+    rq, rs = orc.quantize_weight_ex(wb, 1, bits, gs, p)
+    assert np.any((rs > 0) & (rs < 2.0 ** -126))
+    assert np.array_equal(gu.to_host(sw), rs)
+    assert np.array_equal(gu.to_host(wq), rq)
+
+
 @pytest.mark.parametrize("dtype", [0, 1])
 @pytest.mark.parametrize("N,K", [(512, 1024), (2560, 10240), (64, 8)])
 def test_smooth_fold_bitexact(N, K, dtype):

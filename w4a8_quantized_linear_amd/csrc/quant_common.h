@@ -87,22 +87,36 @@ __device__ __forceinline__ uint2 pack_codes(const int (&q)[8])
     return o;
 }
 
+// True when the scale is not a normal fp32 number (below 2^-126: bf16 rows
+// with absmax below about 1.5e-36, rows divided by huge smoothing factors).
+// Below 2^-128 the reciprocal rs = 1 / s overflows to +inf, so x * rs is
+// +-inf, or NaN for x = 0, and cannot stand in for the quotient x / s; the
+// bound on the product's error below is stated for normal scales only, so
+// every row under 2^-126 takes the correctly rounded division for every
+// value.  All-zero rows (s == 0) take it too; their codes are 0 either way.
+__device__ __forceinline__ bool tiny_scale(float s)
+{
+    return !(s >= 0x1p-126f);
+}
+
 // Codes of the 8 fp16 values of a chunk, packed: int8 -> 8 bytes (uint2),
 // int4 -> 8 nibbles u = q + 8 with value e at bits 4e (uint32 in .x).
 // rs must be 1.0f / s (correctly rounded).
 //
-// The code is rint of the correctly rounded quotient fl(x / s).  The product
-// t = fl(x * rs) differs from fl(x / s) by at most 3 * 2^-24 relative, i.e.
-// below 2^-15.4 in absolute terms for |x / s| <= 127.5, so rint(t) equals
-// rint(fl(x / s)) unless t lies within that distance of a half-integer.  A
-// chunk with a value within 2^-14 of a half-integer (about 1 value in 8000)
-// is recomputed with correctly rounded divisions.
+// The code is rint of the correctly rounded quotient fl(x / s).  For a normal
+// scale s the product t = fl(x * rs) differs from fl(x / s) by at most
+// 3 * 2^-24 relative, i.e. below 2^-15.4 in absolute terms for
+// |x / s| <= 127.5, so rint(t) equals rint(fl(x / s)) unless t lies within
+// that distance of a half-integer.  A chunk with a value within 2^-14 of a
+// half-integer (about 1 value in 8000), or any chunk of a row whose scale is
+// not a normal fp32 (tiny_scale), is recomputed with correctly rounded
+// divisions.
 template <int BITS, int DT = DT_F16>
 __device__ __forceinline__ uint2 quantize_chunk(uint4 v, float s, float rs)
 {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     float f[8], t[8];
-    bool near_half = false;
+    bool near_half = tiny_scale(s);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         f[2 * j] = widen_bits<DT>(w[j]);
@@ -155,14 +169,14 @@ __device__ __forceinline__ void smooth_chunk(uint4 v, const float (&sm)[8], floa
 }
 
 // Codes of 8 fp32 values, packed: rint of the correctly rounded quotients by
-// s, through the product with rs = 1 / s and the same near-half fallback as
-// quantize_chunk.  (fp32 values, so the bound on |f / s| is 127.5 again: the
-// scale comes from their own absmax.)
+// s, through the product with rs = 1 / s and the same near-half and tiny-scale
+// fallbacks as quantize_chunk.  (fp32 values, so the bound on |f / s| is 127.5
+// again: the scale comes from their own absmax.)
 template <int BITS>
 __device__ __forceinline__ uint2 quantize_values(const float (&f)[8], float s, float rs)
 {
     float t[8];
-    bool near_half = false;
+    bool near_half = tiny_scale(s);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         t[e] = f[e] * rs;
