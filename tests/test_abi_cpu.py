@@ -231,6 +231,15 @@ def test_linear_argument_codes():
     # the workspace is required
     assert f(P, 8, 8256, 8256, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_WORKSPACE
     assert f(P, 8, 8192, 8192, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    # a row stride that puts the last token 2 GiB or more past the first (the
+    # fused kernel's 32-bit buffer offsets would wrap) leaves the fused path:
+    # the tokens are quantized into the workspace instead
+    big = 2 ** 29 + 2 ** 28                               # ((M - 1) * ldx + K) * 2 >= 2^31 at M = 3
+    assert ((3 - 1) * big + 256) * 2 >= 2 ** 31 and ((2 - 1) * big + 256) * 2 < 2 ** 31
+    assert f(P, 2, 256, big, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert f(P, 3, 256, big, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_WORKSPACE
+    ws3 = cider.cider_linear_workspace_bytes(3, 256)
+    assert f(P, 3, 256, big, P2, P3, 128, 0, P4, ws3, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
     f4 = cider.cider_w4a8_linear
     assert f4(P, 4, 256, 256, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
     assert f4(P, 5, 256, 256, P2, P3, 128, 0, None, 0, P, stream=0, check=False) == cider.CIDER_ERR_WORKSPACE

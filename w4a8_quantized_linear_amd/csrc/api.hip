@@ -183,8 +183,11 @@ cider_status run_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_
     if (st != CIDER_OK)
         return st;
     // fp16 tokens without smoothing on the matrix-vector path: quantized inside
-    // the matrix-vector kernel
-    const bool fused = path == PATH_GEMV && x_dtype == CIDER_DTYPE_F16 && !smooth;
+    // the matrix-vector kernel, whose buffer descriptor spans the tokens with
+    // 32-bit byte offsets; a row stride that puts the last token 2 GiB or more
+    // past the first goes through the quantize kernel (64-bit row addresses)
+    const bool fused = path == PATH_GEMV && x_dtype == CIDER_DTYPE_F16 && !smooth &&
+                       ((M - 1) * ldx + K) * 2 < (int64_t(1) << 31);
     if (!fused) {
         if (!ws || ws_bytes < cider_linear_workspace_bytes(M, K))
             return CIDER_ERR_WORKSPACE;
