@@ -80,7 +80,9 @@ typedef enum {
     CIDER_ERR_MISALIGNED = 3,        /* a pointer not 16-byte aligned, or ldx % 8 != 0 */
     CIDER_ERR_NO_DEVICE = 4,         /* no usable gfx950 device (or CIDER_FORCE_UNAVAILABLE=1) */
     CIDER_ERR_HIP = 5,               /* the HIP runtime reported an error at launch */
-    CIDER_ERR_WORKSPACE = 6          /* workspace missing or smaller than cider_linear_workspace_bytes */
+    CIDER_ERR_WORKSPACE = 6,         /* workspace missing or smaller than cider_linear_workspace_bytes */
+    CIDER_ERR_SCRATCH_LIMIT = 7      /* cider_linear_ex_noalloc: the call needs more than
+                                        CIDER_NOALLOC_SCRATCH_BYTES of workspace */
 } cider_status;
 
 /* Element type of 16-bit activations, weights and outputs (Cider README
@@ -235,6 +237,33 @@ cider_status cider_linear_ex(const void *x, int x_dtype, int64_t M, int64_t K, i
                              const float *smooth, const void *wq, const float *s_w, int64_t N,
                              int bits, int group_size, int y_dtype, void *workspace,
                              size_t workspace_bytes, void *y, void *stream);
+
+/* Size of the static device array that serves as cider_linear_ex_noalloc's
+   workspace on each GPU (64 MiB). */
+#define CIDER_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+   capture, tight serving loops, harnesses that forbid hipMalloc): the same
+   layer as cider_linear_ex, with the workspace taken from a file-scope device
+   array of CIDER_NOALLOC_SCRATCH_BYTES per GPU that the library holds until
+   the process ends.  No allocation of any kind happens in the call; the
+   first call on a device looks up that device's array address once.  The
+   call splits K exactly when cider_linear_ex given
+   cider_linear_workspace_bytes_ex(...) bytes would, as long as those bytes fit
+   in the array, so its results equal that call's bit for bit; shapes whose
+   split workspace does not fit run unsplit (equal to cider_linear_ex given
+   cider_linear_workspace_bytes(M, K) bytes).  Calls whose
+   cider_linear_workspace_bytes(M, K) exceeds the array (M * K above about
+   64 Mi) return CIDER_ERR_SCRATCH_LIMIT before any launch; fused one-token
+   calls use no workspace.  Every call on one GPU shares that GPU's array and
+   leaves its contents behind (the quantize launch clears the split counters
+   each call), so calls must be ordered on one stream: calls that overlap on
+   one GPU (concurrent streams, several host threads) race on the array and
+   give undefined results.  Arguments and other statuses as cider_linear_ex. */
+cider_status cider_linear_ex_noalloc(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                     const float *smooth, const void *wq, const float *s_w,
+                                     int64_t N, int bits, int group_size, int y_dtype, void *y,
+                                     void *stream);
 
 /* The pages' decode kernel (Cider README, "Metal Kernel Pipeline", Decode
    (M = 1): a direct matrix-vector product with on-the-fly weight

@@ -49,7 +49,7 @@ def test_unavailable_without_device():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert cider.cider_status_str(s) not in ("", "unknown status")
     assert cider.cider_status_str(99) == "unknown status"
 
@@ -257,3 +257,27 @@ def test_forced_gemv_range():
 def test_raises_with_check():
     with pytest.raises(cider.CiderError):
         cider.cider_w8a8_gemm(P, P2, P3, P4, 4, 64, 96, 0, P, stream=0)
+
+
+def test_linear_noalloc_argument_codes():
+    """The no-allocation linear call: the same argument checks as
+    cider_linear_ex, no workspace argument, and a clear status for calls
+    whose workspace would not fit the static array."""
+    f = cider.cider_linear_ex_noalloc
+    lim = cider.CIDER_NOALLOC_SCRATCH_BYTES
+    assert f(P, 0, 16, 256, 256, None, P2, P3, 128, 8, 0, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert f(P, 0, 16, 256, 200, None, P2, P3, 128, 8, 0, 0, P, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    assert f(BAD, 0, 16, 256, 256, None, P2, P3, 128, 8, 0, 0, P, stream=0, check=False) == cider.CIDER_ERR_MISALIGNED
+    assert f(P, 2, 16, 256, 256, None, P2, P3, 128, 8, 0, 0, P, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    assert f(P, 0, 16, 256, 256, None, P2, P3, 128, 8, 32, 0, P, stream=0, check=False) == cider.CIDER_ERR_INVALID_ARG
+    # the largest token count whose activations and scales fit, and one more
+    K = 10240
+    M = 1
+    while cider.cider_linear_workspace_bytes(M + 1, K) <= lim:
+        M += 1
+    assert cider.cider_linear_workspace_bytes(M, K) <= lim < cider.cider_linear_workspace_bytes(M + 1, K)
+    assert f(P, 0, M, K, K, None, P2, P3, 2560, 8, 64, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert f(P, 0, M + 1, K, K, None, P2, P3, 2560, 8, 64, 0, P, stream=0, check=False) == cider.CIDER_ERR_SCRATCH_LIMIT
+    # a fused one-token call needs no workspace at any size
+    assert f(P, 0, 1, 65536, 65536, None, P2, P3, 128, 8, 0, 0, P, stream=0, check=False) == cider.CIDER_ERR_NO_DEVICE
+    assert cider.cider_status_str(cider.CIDER_ERR_SCRATCH_LIMIT) != "unknown status"

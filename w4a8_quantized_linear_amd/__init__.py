@@ -25,6 +25,8 @@ CIDER_ERR_MISALIGNED = 3
 CIDER_ERR_NO_DEVICE = 4
 CIDER_ERR_HIP = 5
 CIDER_ERR_WORKSPACE = 6
+CIDER_ERR_SCRATCH_LIMIT = 7
+CIDER_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
 
@@ -34,6 +36,7 @@ EXPORTS = (
     "cider_linear_workspace_bytes", "cider_linear_workspace_bytes_ex", "cider_w8a8_linear", "cider_w4a8_linear", "cider_set_path",
     "cider_quantize_weight_clipped", "cider_quantize_weight_ex", "cider_smooth_fold_weight",
     "cider_quantize_act_ex", "cider_gemm_ex", "cider_linear_ex", "cider_decode_linear",
+    "cider_linear_ex_noalloc",
 )
 
 CIDER_DTYPE_F16 = 0
@@ -73,6 +76,7 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         "cider_quantize_act_ex": ([P, I, I64, I64, I64, P, P, P, P], I),
         "cider_gemm_ex": ([P, P, P, P, I64, I64, I64, I, I, I, P, P], I),
         "cider_linear_ex": ([P, I, I64, I64, I64, P, P, P, I64, I, I, I, P, SZ, P, P], I),
+        "cider_linear_ex_noalloc": ([P, I, I64, I64, I64, P, P, P, I64, I, I, I, P, P], I),
         "cider_decode_linear": ([P, I64, P, P, I64, I, I, I, P, P], I),
         "cider_w8a8_gemm": ([P, P, P, P, I64, I64, I64, I, P, P], I),
         "cider_w4a8_gemm": ([P, P, P, P, I64, I64, I64, I, P, P], I),
@@ -172,6 +176,14 @@ def cider_linear_ex(x, x_dtype, M, K, ldx, smooth, wq, s_w, N, bits, group_size,
                                 N, bits, group_size, y_dtype, _ptr(workspace), workspace_bytes,
                                 _ptr(y), _stream(stream))
     return _ret(st, "cider_linear_ex", check)
+
+
+def cider_linear_ex_noalloc(x, x_dtype, M, K, ldx, smooth, wq, s_w, N, bits, group_size, y_dtype,
+                            y, stream=None, check=True):
+    st = load().cider_linear_ex_noalloc(_ptr(x), x_dtype, M, K, ldx, _ptr(smooth), _ptr(wq),
+                                        _ptr(s_w), N, bits, group_size, y_dtype, _ptr(y),
+                                        _stream(stream))
+    return _ret(st, "cider_linear_ex_noalloc", check)
 
 
 def cider_decode_linear(x_f16, K, wq, s_w, N, bits, group_size, y_dtype, y, stream=None,

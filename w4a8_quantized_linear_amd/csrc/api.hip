@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "cider.h"
 #include "cider_kernels.h"
@@ -71,6 +72,41 @@ int device_usable()
 }
 
 cider_status from_hip(hipError_t e) { return e == hipSuccess ? CIDER_OK : CIDER_ERR_HIP; }
+
+// Workspace of cider_linear_ex_noalloc: a device array of fixed size, one per
+// GPU, kept for the life of the process.  Host code never passes the array's
+// name to a kernel or a copy (on the host it is only a stand-in for the
+// symbol); it uses the device address hipGetSymbolAddress returns for the
+// current device, looked up once per device.
+__device__ __align__(256) uint8_t scratch[CIDER_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The current device's scratch address, or nullptr when it cannot be had.
+void *scratch_address()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p)
+        return p;
+    void *addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    g_scratch_ptr[dev].store(addr, std::memory_order_release);
+    return addr;
+}
 
 // Shape / mode checks shared by the product calls.
 cider_status check_shape(int64_t M, int64_t N, int64_t K, int bits, int group_size)
@@ -161,10 +197,12 @@ cider::OutKind out_kind_of(int y_dtype)
     return y_dtype == CIDER_DTYPE_BF16 ? cider::OUT_BF16 : cider::OUT_F16;
 }
 
+// The whole layer.  static_ws: ignore ws / ws_bytes and use the current
+// device's scratch array instead (after every argument and device check).
 cider_status run_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                         const float *smooth, const void *wq, const float *s_w, int64_t N, int bits,
                         int group_size, int y_dtype, void *ws, size_t ws_bytes, void *y,
-                        void *stream)
+                        void *stream, bool static_ws = false)
 {
     cider_status st = check_shape(M, N, K, bits, group_size);
     if (st != CIDER_OK)
@@ -189,13 +227,24 @@ cider_status run_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_
     const bool fused = path == PATH_GEMV && x_dtype == CIDER_DTYPE_F16 && !smooth &&
                        ((M - 1) * ldx + K) * 2 < (int64_t(1) << 31);
     if (!fused) {
-        if (!ws || ws_bytes < cider_linear_workspace_bytes(M, K))
-            return CIDER_ERR_WORKSPACE;
-        if (!aligned16(ws))
-            return CIDER_ERR_MISALIGNED;
+        if (static_ws) {
+            if (cider_linear_workspace_bytes(M, K) > CIDER_NOALLOC_SCRATCH_BYTES)
+                return CIDER_ERR_SCRATCH_LIMIT;
+        } else {
+            if (!ws || ws_bytes < cider_linear_workspace_bytes(M, K))
+                return CIDER_ERR_WORKSPACE;
+            if (!aligned16(ws))
+                return CIDER_ERR_MISALIGNED;
+        }
     }
     if (!device_usable())
         return CIDER_ERR_NO_DEVICE;
+    if (static_ws && !fused) {
+        ws = scratch_address();
+        if (!ws)
+            return CIDER_ERR_HIP;
+        ws_bytes = CIDER_NOALLOC_SCRATCH_BYTES;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (fused)
         return from_hip(cider::launch_gemv_fused(static_cast<const uint16_t *>(x), M, K, ldx, wq, s_w,
@@ -291,6 +340,7 @@ const char *cider_status_str(int status)
     case CIDER_ERR_NO_DEVICE: return "no usable gfx950 device";
     case CIDER_ERR_HIP: return "HIP runtime error at launch";
     case CIDER_ERR_WORKSPACE: return "workspace missing or too small";
+    case CIDER_ERR_SCRATCH_LIMIT: return "call needs more than the static scratch array holds";
     default: return "unknown status";
     }
 }
@@ -444,6 +494,15 @@ cider_status cider_linear_ex(const void *x, int x_dtype, int64_t M, int64_t K, i
 {
     return run_linear(x, x_dtype, M, K, ldx, smooth, wq, s_w, N, bits, group_size, y_dtype,
                       workspace, workspace_bytes, y, stream);
+}
+
+cider_status cider_linear_ex_noalloc(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                     const float *smooth, const void *wq, const float *s_w,
+                                     int64_t N, int bits, int group_size, int y_dtype, void *y,
+                                     void *stream)
+{
+    return run_linear(x, x_dtype, M, K, ldx, smooth, wq, s_w, N, bits, group_size, y_dtype,
+                      nullptr, 0, y, stream, true);
 }
 
 cider_status cider_decode_linear(const void *x_f16, int64_t K, const void *wq, const float *s_w,
