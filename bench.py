@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 matrix throughput, TOP/s
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E bandwidth, GB/s
 ROTATE_BYTES = 1 << 30       # working-set copies cycled through per step
+WARMUP_MIN_S = 0.25          # least time of sustained load before the timed steps
 PAGES_M5PRO_PC_M4096_MS = 4.41  # the pages' per-channel latency at M=4096, [10240 x 2560], Apple M5 Pro
 
 
@@ -172,6 +173,18 @@ def traffic_record(kernel_source, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(M, N, K, x_np, w_np, budget_s):
     """The oracle (as it stands) on the first rows of the same workload:
     quantize_act + int8 product + dequant per row, timed on the host cores."""
@@ -187,9 +200,116 @@ def cpu_baseline(M, N, K, x_np, w_np, budget_s):
     orc.linear(x_np[:rows], wq, sw)
     dt = time.perf_counter() - t0
     return {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TOP/s",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
+            "host_logical_cpus": os.cpu_count(),
             "sample": "first %d of %d tokens of W8A8 per-channel N=%d K=%d: quantize_act + "
                       "int8 product + dequant, %.2f s wall" % (rows, M, N, K, dt)}
+
+
+# The operator configurations: (name, weight bits, group size, N, K).
+CONFIGS = [("w8a8_pc_small", 8, 0, 512, 1024), ("w8a8_pc", 8, 0, 10240, 2560),
+           ("w8a8_pg64", 8, 64, 2560, 10240), ("w8a8_pg128", 8, 128, 2560, 10240),
+           ("w4a8_pc", 4, 0, 10240, 2560)]
+
+
+def oracle_times(si, budget_s=3.0, M_full=4096):
+    """The oracle's host time per configuration, split into its steps:
+    quantize_act, then the integer product and the dequant.  The small
+    configuration (M=64) runs whole, also on one thread; the operator shapes
+    run the first rows that fit about budget_s and are also given per token
+    and scaled to M_full tokens (the oracle's rows are independent, so its
+    time is linear in M)."""
+    from oracle.oracle import get as get_oracle
+    orc = get_oracle()
+    threads = orc.num_threads()
+    out = []
+    for name, bits, gs, N, K in CONFIGS:
+        small = name == "w8a8_pc_small"
+        w = si.weights(N, K)
+        wq, sw = orc.quantize_weight(w, bits, gs)
+        x = si.activations(64 if small else 8, K)
+        t0 = time.perf_counter()
+        orc.dequant(orc.gemm_acc(orc.quantize_act(x)[0], wq, bits, gs), np.ones(len(x), np.float32), sw)
+        per_row = (time.perf_counter() - t0) / len(x)
+        rows = 64 if small else int(max(8, min(M_full, budget_s / max(per_row, 1e-9))))
+        x = si.activations(rows, K)
+
+        def run():
+            t0 = time.perf_counter()
+            xq, st = orc.quantize_act(x)
+            t1 = time.perf_counter()
+            acc = orc.gemm_acc(xq, wq, bits, gs)
+            orc.dequant(acc, st, sw)
+            t2 = time.perf_counter()
+            return t1 - t0, t2 - t1
+
+        tq, tg = run()
+        rec = {"config": name, "weight_bits": bits, "group_size": gs, "N": N, "K": K,
+               "tokens": rows, "threads": threads,
+               "quantize_act_s": round(tq, 5), "gemm_dequant_s": round(tg, 5),
+               "total_s": round(tq + tg, 5)}
+        if small:
+            orc.set_num_threads(1)
+            try:
+                tq1, tg1 = run()
+            finally:
+                orc.set_num_threads(threads)
+            rec.update({"single_thread_quantize_act_s": round(tq1, 5),
+                        "single_thread_gemm_dequant_s": round(tg1, 5),
+                        "single_thread_total_s": round(tq1 + tg1, 5)})
+        else:
+            f = M_full / rows
+            rec.update({"per_token_us": round((tq + tg) / rows * 1e6, 2),
+                        "scaled_to_M%d_s" % M_full: {"quantize_act": round(tq * f, 3),
+                                                     "gemm_dequant": round(tg * f, 3),
+                                                     "total": round((tq + tg) * f, 3)}})
+        log("oracle %s: %d tokens, quantize_act %.3f s, gemm+dequant %.3f s" % (name, rows, tq, tg))
+        out.append(rec)
+    return out
+
+
+# Cosine of the layer's output against the fp16 product, as measured on the
+# same inputs in numpy (64 tokens, seed 0) when the scheme was surveyed: what
+# a correct implementation of this quantization gives on these inputs.
+QUALITY_EXPECTED = {"w8a8_pc_small": 0.99914, "w8a8_pc": 0.99892, "w8a8_pg64": 0.99834,
+                    "w8a8_pg128": 0.99834, "w4a8_pc": 0.98753}
+
+
+def quality_report(torch, cider, si, M=64):
+    """Quality of the quantized layer per configuration: the first M tokens
+    through the linear call (weights quantized on the device) against the
+    fp16 product x @ w^T evaluated in float64 on the host: cosine and
+    relative Frobenius error.  A property of the quantization scheme on these
+    inputs (the outlier columns widen the token scales), reported, not a
+    pass / fail gate."""
+    out = []
+    for name, bits, gs, N, K in CONFIGS:
+        x = si.activations(M, K)
+        w = si.weights(N, K)
+        xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.float16)
+        wd = torch.from_numpy(w.view(np.int16)).cuda().view(torch.float16)
+        wq = torch.empty((N, K) if bits == 8 else (N, K // 2),
+                         dtype=torch.int8 if bits == 8 else torch.uint8, device="cuda")
+        sw = torch.empty((N,) if gs == 0 else (N, K // gs), dtype=torch.float32, device="cuda")
+        cider.cider_quantize_weight(wd, N, K, bits, gs, wq, sw)
+        ws_bytes = cider.cider_linear_workspace_bytes_ex(M, N, K, bits, gs)
+        ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device="cuda")
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        f = cider.cider_w8a8_linear if bits == 8 else cider.cider_w4a8_linear
+        f(xd, M, K, K, wq, sw, N, gs, ws, ws_bytes, y)
+        yh = y.view(torch.int16).cpu().numpy().view(np.float16).astype(np.float64)
+        ref = x.astype(np.float64) @ w.astype(np.float64).T
+        cos = float((yh * ref).sum() / np.sqrt((yh * yh).sum() * (ref * ref).sum()))
+        rel = float(np.linalg.norm(yh - ref) / np.linalg.norm(ref))
+        rec = {"config": name, "tokens": M, "N": N, "K": K, "weight_bits": bits,
+               "group_size": gs, "cosine": round(cos, 6), "rel_frobenius_error": round(rel, 6),
+               "cosine_expected": QUALITY_EXPECTED[name]}
+        log("quality %s: cosine %.5f (expected %.5f), relative error %.5f"
+            % (name, cos, QUALITY_EXPECTED[name], rel))
+        out.append(rec)
+        del xd, wd, wq, sw, ws, y
+    torch.cuda.empty_cache()
+    return out
 
 
 def weight_quant_bench(torch, cider, si, reps=20):
@@ -477,40 +597,55 @@ def main():
     B = copies_for(8, 0, N, K, M)
     L = Layer(torch, cider, 8, 0, N, K, M, x_np, w_np, B)
     ops = 2.0 * M * N * K
-    for i in range(args.warmup):
-        L.linear(i)
+    # warm-up: the requested steps, then more until the chip has run this
+    # load for at least WARMUP_MIN_S (the clocks settle under sustained
+    # matrix-core load; a few steps are not enough)
+    t0 = time.perf_counter()
+    i = 0
+    while i < args.warmup or time.perf_counter() - t0 < WARMUP_MIN_S:
+        L.quantize(i)
+        L.gemm(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    log("warm-up: %d steps in %.0f ms" % (i, (time.perf_counter() - t0) * 1e3))
     log("timing %d steps (%d rotating copies)" % (args.steps, B))
     stream = torch.cuda.current_stream()
-    # timed region 1: whole steps back to back -> value, ms_per_step
+    # The timed region: K whole steps back to back, host-timed between two
+    # synchronizations -> value, ms_per_step.  Inside it, a HIP event on the
+    # launch stream before each step's quantize launch and one between its
+    # quantize and product launches: the product kernel's duration of step i
+    # is the time from the second event of step i to the first of step i+1
+    # (or the closing event), so both kernel averages come from the very
+    # launches the step time covers and cannot exceed it.
+    ev_q = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_g = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        ev_q[i].record(stream)
         L.quantize(i)
+        ev_g[i].record(stream)
         L.gemm(i)
+    ev_end.record(stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_per_step = dt / args.steps * 1e3
     value = ops / (dt / args.steps) / 1e12
-    # timed region 2: the product kernel alone, the same launches back to back
-    # between two HIP events on its stream -> its average launch duration
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        L.gemm(i)
-    e1.record(stream)
-    e1.synchronize()
-    gemm_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    nxt = ev_q[1:] + [ev_end]
+    gemm_ms = [ev_g[i].elapsed_time(nxt[i]) for i in range(args.steps)]
+    quant_ms = [ev_q[i].elapsed_time(ev_g[i]) for i in range(args.steps)]
+    device_ms = ev_q[0].elapsed_time(ev_end)
+    gemm_s = sum(gemm_ms) / args.steps / 1e3
+    quant_s = sum(quant_ms) / args.steps / 1e3
+    assert gemm_s + quant_s <= dt / args.steps * 1.0001, (gemm_s, quant_s, dt / args.steps)
     achieved = ops / gemm_s / 1e12
-    # the quantize kernel alone, likewise
-    e0.record(stream)
-    for i in range(args.steps):
-        L.quantize(i)
-    e1.record(stream)
-    e1.synchronize()
-    quant_s = e0.elapsed_time(e1) / 1e3 / args.steps
-    log("step %.2f us, product kernel %.2f us (%.0f TOPS), quantize kernel %.2f us"
-        % (ms_per_step * 1e3, gemm_s * 1e6, achieved, quant_s * 1e6))
+    log("step %.2f us (device %.2f us), product kernel %.2f us (%.0f TOPS; median %.2f us), "
+        "quantize kernel %.2f us"
+        % (ms_per_step * 1e3, device_ms * 1e3 / args.steps, gemm_s * 1e6, achieved,
+           sorted(gemm_ms)[args.steps // 2] * 1e3, quant_s * 1e6))
     traffic = traffic_record(os.path.join(ROOT, "w4a8_quantized_linear_amd", "csrc", "gemm.hip"),
                              "w8a8_pc_N10240_K2560_M4096")
     result = {
@@ -536,7 +671,9 @@ def main():
                      "traffic": traffic,
                      "kernel": "gemm_kernel (int8 matrix-core product + dequant, per channel)",
                      "kernel_us": round(gemm_s * 1e6, 2),
-                     "quantize_kernel_us": round(quant_s * 1e6, 2)},
+                     "quantize_kernel_us": round(quant_s * 1e6, 2),
+                     "timing": "HIP events on the launch stream around each launch of the "
+                               "timed steps (the same launches as ms_per_step)"},
     }
     del L
     torch.cuda.empty_cache()
@@ -571,10 +708,14 @@ def main():
     if not args.no_stack:
         result["stack"] = stack_bench(torch, cider, si)
 
+    # --------------------------------------------------- quality report ---
+    result["quality"] = quality_report(torch, cider, si)
+
     # -------------------------------------------------------- CPU oracle ---
     if not args.no_cpu:
         log("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(M, N, K, x_np, w_np, args.cpu_seconds)
+        result["cpu_baseline"]["per_config"] = oracle_times(si)
     else:
         result["cpu_baseline"] = None
 

@@ -533,3 +533,15 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the thread count of later calls (n >= 1).  Scheduling only: every
+   loop above splits independent rows, so results do not depend on it. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -82,6 +82,8 @@ class Oracle:
         L.oracle_gemm_acc.argtypes = [P, P, I, I64, I64, I64, I, P]
         L.oracle_dequant.argtypes = [P, P, P, I64, I64, I64, P]
         L.oracle_linear.argtypes = [P, I64, I64, I64, P, P, I, I64, I, P, P, P]
+        L.oracle_set_num_threads.argtypes = [I]
+        L.oracle_set_num_threads.restype = None
         for f in ("oracle_quantize_act", "oracle_quantize_weight", "oracle_gemm_acc",
                   "oracle_dequant", "oracle_linear", "oracle_num_threads",
                   "oracle_quantize_weight_clipped", "oracle_quantize_act_ex",
@@ -96,6 +98,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return self.lib.oracle_num_threads()
+
+    def set_num_threads(self, n: int):
+        """Thread count of later calls (scheduling only; results unchanged)."""
+        self.lib.oracle_set_num_threads(int(n))
 
     def half_to_double(self, h: int) -> float:
         return self.lib.oracle_half_to_double(int(h))
