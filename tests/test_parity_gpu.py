@@ -453,6 +453,42 @@ def test_product_f16_tolerance(M, N, K, bits, gs, path):
     gu.assert_f16_close(gu.to_host(y), ref, "M=%d N=%d K=%d bits=%d gs=%d" % (M, N, K, bits, gs))
 
 
+@pytest.mark.parametrize("out", ["i32", "f16", "bf16"])
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M,N,K", [(2100, 10304, 1024), (1100, 640, 256), (1030, 576, 1344),
+                                   (1100, 320, 128), (4100, 704, 2560)])
+def test_many_token_tiles(M, N, K, bits, out):
+    """Per-channel products above 1024 tokens.  With K a multiple of 128 and
+    at least 256, one workgroup per compute unit walks several 320 x 256
+    output tiles (2100 x 10304: 297 tiles, so some workgroups take two, with
+    ragged tiles in both M and N; 4100 x 704: ragged N, 17 token tiles); K =
+    1344 (not a multiple of 128) and K = 128 (one K tile) take the other
+    kernel.  int32 sums bit-exact and outputs within tolerance on sampled rows
+    against the oracle, every output against the exact product."""
+    import torch
+    orc = get_oracle()
+    _, _, xq, st, wq, sw = _inputs(M, N, K, bits, 0, seed=M + N + K)
+    d = [gu.to_dev(a) for a in (xq, st, wq, sw)]
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 511, M // 2, M - 2, M - 1],
+                                     np.random.default_rng(M).integers(0, M, 8)]))
+    ref_acc = orc.gemm_acc(xq[rows], wq, bits, 0)
+    if out == "i32":
+        acc = gu.to_host(gu.gemm_i32_gpu(d[0], d[2], M, N, K, bits, 0))
+        assert np.array_equal(acc[rows], ref_acc)
+        full = xq.astype(np.int64) @ (wq if bits == 8 else gu.unpack_int4(wq)).astype(np.int64).T
+        assert np.array_equal(acc, full)
+        return
+    y_dtype = 0 if out == "f16" else 1
+    y = gu.empty((M, N), torch.int16)
+    cider.cider_gemm_ex(d[0], d[1], d[2], d[3], M, N, K, bits, 0, y_dtype, y)
+    got = gu.bits_to_host(y)
+    gu.assert_out_close(got[rows], orc.dequant_ex(ref_acc, st[rows], sw, y_dtype), y_dtype,
+                        "%s M=%d N=%d K=%d bits=%d" % (out, M, N, K, bits))
+    if out == "f16":
+        gu.assert_every_output(y.view(torch.float16), xq, st, wq if bits == 8 else gu.unpack_int4(wq), sw, 0,
+                               "M=%d N=%d K=%d bits=%d" % (M, N, K, bits))
+
+
 @pytest.mark.parametrize("bits,gs", MODES, ids=MODE_IDS)
 @pytest.mark.parametrize("M,N,K", [(1, 512, 1024), (3, 320, 2560), (8, 576, 4096), (2, 128, 10240)])
 def test_gemv_path_matches_gemm_path(M, N, K, bits, gs):

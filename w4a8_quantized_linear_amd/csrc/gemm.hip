@@ -786,6 +786,421 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     }
 }
 
+// Persistent per-channel product for many tokens (int8 or packed int4
+// weights).  Same arithmetic as gemm_kernel per channel; what differs is how
+// the operands reach the matrix cores:
+//   * K tiles are 128 bytes of every token row (a whole 128-byte line; packed
+//     int4 weight rows give 64 bytes).  Copying 64-byte halves of lines, each
+//     line is requested from L2 twice; measured on this chip, a compute unit
+//     then pulls about 17.6 bytes per clock from L2 against 25.6 with whole
+//     lines, and the 320 x 256 tile needs about 29 per clock to keep its
+//     matrix cores busy.
+//   * The LDS ring has two stages of one 128-deep K tile each (72 KB for
+//     int8).  Tile kt is computed from stage kt & 1 in four 32-deep steps;
+//     the one barrier per K tile sits before the fourth step, after which the
+//     stage of tile kt is refilled with tile kt + 2 while the fourth step's
+//     MFMAs run.
+//   * One workgroup per compute unit walks several output tiles.  The first
+//     K tile of its next output tile is copied during the current tile's last
+//     K tile and epilogue; the epilogue stages its fp16 rows in the other
+//     (idle) stage of the ring.
+//   * Outputs leave through range-checked buffer stores (out-of-range rows
+//     and channels are dropped by the hardware), so every wave issues the same
+//     number of memory instructions and the in-order vmcnt waits count
+//     exactly.
+// Needs K % 128 == 0 and K >= 256 (two K tiles).
+// Two outputs packed into one dword (first in the low half): fp16 through
+// the packed conversion (round to nearest even, as the scalar one), bf16 by
+// out_bits.
+template <int OUT>
+__device__ __forceinline__ uint32_t pack2(float a, float b)
+{
+    if constexpr (OUT == OUT_F16) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
+    } else {
+        return (uint32_t)out_bits<OUT>(a) | ((uint32_t)out_bits<OUT>(b) << 16);
+    }
+}
+
+// Channel blocks (of 32) per staging pass: the largest power of two up to
+// fn whose 32 rows (cb * 64 bytes + 16 of padding each) fit in wreg bytes.
+constexpr int cb_for(int fn, int wreg)
+{
+    int cb = 1;
+    while (cb * 2 <= fn && 32 * (cb * 2 * 64 + 16) <= wreg)
+        cb *= 2;
+    return cb;
+}
+
+template <int TN, int TM, int WN, int WM, int BITS, int OUT>
+__global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_wide_kernel(ProductArgs args, int tiles_n,
+                                                                               int tiles_m, int group_m)
+{
+    constexpr int BK = 128;
+    constexpr int NWN = TN / WN, NWM = TM / WM, NW = NWN * NWM;
+    constexpr int FN = WN / 32, FM = WM / 32;
+    constexpr int XROW = BK, WROW = BITS == 8 ? BK : BK / 2;
+    constexpr int XBYTES = TM * XROW, WBYTES = TN * WROW;
+    constexpr int STAGE = XBYTES + WBYTES;
+    constexpr int XB = XBYTES / 1024, WB = WBYTES / 1024, TB = XB + WB;
+    constexpr int D = (XB + NW - 1) / NW + (WB + NW - 1) / NW;  // copies per wave per K tile
+    static_assert(XBYTES % 1024 == 0 && WBYTES % 1024 == 0, "tiles of whole 1 KB blocks");
+    constexpr bool USUM = BITS == 4;  // unsigned int4 codes, corrected by the token sums
+    // epilogue: each wave stages CB channel blocks of 32 tokens at a time in
+    // its share of the idle stage (rows of 64 * CB bytes padded by 16)
+    constexpr int WREG = STAGE / NW;
+    constexpr int CB = cb_for(FN, WREG);
+    constexpr int NPASS = (FN + CB - 1) / CB;
+    static_assert((FN % CB & (FN % CB - 1)) == 0, "the last pass is a power of two wide too");
+    constexpr int ROWB = CB * 64 + 16;
+    // fp16 stores per wave per output tile: per token block and pass, 32 rows
+    // of cb * 64 bytes in 16-byte pieces; int32: one 16-byte store per
+    // (token block, channel block, quarter)
+    constexpr int STORES = OUT == OUT_I32 ? FM * FN * 4 : FM * FN * 2;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) float s_sw[OUT != OUT_I32 ? TN : 4];
+    __shared__ __attribute__((aligned(16))) float s_st[OUT != OUT_I32 ? TM : 4];
+
+    const int64_t M = args.M, N = args.N, K = args.K;
+    const int KT = (int)(K / BK);
+    const int tiles = tiles_n * tiles_m;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave % NWN, wm = wave / NWN;
+    const int frow = lane & 31, fhalf = lane >> 5;
+    const uint32_t wld = (uint32_t)(BITS == 8 ? K : K / 2);
+    const i32x4 rX = make_rsrc(args.xq, (uint32_t)(M * K));
+    const i32x4 rW = make_rsrc(args.wq, (uint32_t)(N * (int64_t)wld));
+
+    // Copies: each wave takes DX consecutive 1 KB blocks of the token tile and
+    // DW of the weight tile (clamped repeats of the last block when they do not
+    // split evenly, so every wave issues D = DX + DW copies per K tile).  A
+    // block holds 1024 / ROW consecutive rows; lane l takes row l / (ROW / 16)
+    // of it and LDS slot l % (ROW / 16), which receives global chunk
+    // slot ^ swizzle(row).  For these row lengths the swizzle depends on the
+    // block only through its parity (128-byte rows) or not at all (64-byte
+    // rows), so two per-lane offsets serve every block.
+    constexpr int DX = (XB + NW - 1) / NW, DW = (WB + NW - 1) / NW;
+    constexpr int CX = XROW / 16, CW = WROW / 16;
+    constexpr int RX = 1024 / XROW, RW = 1024 / WROW;  // rows per block
+    uint32_t xlane[2], wlane[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        const int rx = par * RX + lane / CX;
+        xlane[par] = (uint32_t)((lane / CX) * K) + (((lane % CX) ^ swz8<BK>(rx)) << 4);
+        const int rw = par * RW + lane / CW;
+        wlane[par] = (uint32_t)((lane / CW) * (int64_t)wld) +
+                     (((lane % CW) ^ (BITS == 8 ? swz8<BK>(rw) : swz4<BK>(rw))) << 4);
+    }
+    const uint32_t smem_lds = lds_address(smem);
+    const uint32_t xstep = (uint32_t)(RX * K), wstep = (uint32_t)(RW * (int64_t)wld);
+    // Copy j (0 <= j < D: DX token blocks, then DW weight blocks) of K tile kt
+    // of the output tile at (m0, n0) into `stage`.
+    auto copy_one = [&](int j, int stage, int64_t m0, int64_t n0, int kt) {
+        const uint32_t lds = smem_lds + stage * STAGE;
+        if (j < DX) {
+            const int b = min(wave * DX + j, XB - 1);  // wavefront-uniform
+            const uint32_t u = (uint32_t)(m0 * K) + (uint32_t)kt * XROW + (uint32_t)b * xstep;
+            dma16(rX, lds + b * 1024, xlane[b & 1] + u);
+        } else {
+            const int b = min(wave * DW + (j - DX), WB - 1);
+            const uint32_t u = (uint32_t)(n0 * (int64_t)wld) + (uint32_t)kt * WROW + (uint32_t)b * wstep;
+            dma16(rW, lds + XBYTES + b * 1024, wlane[b & 1] + u);
+        }
+    };
+    // all D copies of a K tile (the empty asm keeps the compiler from
+    // precomputing one register per copy: two per-lane offsets and uniform
+    // terms are enough)
+    auto copy_tile = [&](int stage, int64_t m0, int64_t n0, int kt) {
+        asm volatile("" : "+v"(xlane[0]), "+v"(xlane[1]), "+v"(wlane[0]), "+v"(wlane[1]));
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            copy_one(j, stage, m0, n0, kt);
+    };
+
+    struct Frags {
+        i32x4 a[FN];
+        uint2 ap[BITS == 4 ? FN : 1];
+        i32x4 b[FM];
+    };
+    constexpr int LOADS = FN + FM;
+    // Fragment addresses.  Rows of a fragment are 32 consecutive rows starting
+    // at a multiple of 32, so their swizzle depends on the lane only: one base
+    // address per operand, and fragment k lies 32 rows further (an immediate
+    // offset).  Step ks flips address bits (ks << 5) (int8 rows: chunk
+    // 2 ks + half) or (ks << 4) (packed int4 rows: chunk ks), inside the row.
+    const uint32_t abase = BITS == 8 ? (uint32_t)(XBYTES + (wn * WN + frow) * WROW + ((fhalf ^ swz8<BK>(frow)) << 4))
+                                     : (uint32_t)(XBYTES + (wn * WN + frow) * WROW + (swz4<BK>(frow) << 4) + fhalf * 8);
+    const uint32_t bbase = (uint32_t)((wm * WM + frow) * XROW + ((fhalf ^ swz8<BK>(frow)) << 4));
+    auto load_frags = [&](Frags &f, int stage, int ks) {
+        const uint32_t a = (abase + (uint32_t)(stage * STAGE)) ^ (uint32_t)(ks << (BITS == 8 ? 5 : 4));
+        const uint32_t b = (bbase + (uint32_t)(stage * STAGE)) ^ (uint32_t)(ks << 5);
+#pragma unroll
+        for (int k = 0; k < FN; ++k) {
+            if constexpr (BITS == 8)
+                f.a[k] = *reinterpret_cast<const i32x4 *>(smem + a + k * 32 * WROW);
+            else
+                f.ap[k] = *reinterpret_cast<const uint2 *>(smem + a + k * 32 * WROW);
+        }
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+            f.b[j] = *reinterpret_cast<const i32x4 *>(smem + b + j * 32 * XROW);
+    };
+    auto widen = [&](Frags &f, int i) {
+        if constexpr (BITS == 4) {
+            uint32_t d0, d1, d2, d3;
+            unpack8u(f.ap[i].x, d0, d1);
+            unpack8u(f.ap[i].y, d2, d3);
+            f.a[i] = i32x4{(int)d0, (int)d1, (int)d2, (int)d3};
+        }
+    };
+
+    i32x16 acc[FN][FM];
+    int xs[USUM ? FM : 1];
+    // One 32-deep step: the D copies of the K tile at (cm0, cn0, ckt) into
+    // `cstage` first when `copies` (a short burst; the other wave of the SIMD
+    // keeps its matrix core busy meanwhile), then the MFMAs on `cur` with the
+    // fragment reads of the next step (into `nxt`, from stage `lstage`, step
+    // `lks`) spread between them.  (Raising the wave priority around the MFMAs
+    // helped an LDS-resident copy of this loop but made the product 2-3%
+    // slower; issuing the copies one per MFMA instead of in a burst was no
+    // faster.)
+    auto step = [&](Frags &cur, Frags &nxt, bool reads, int lstage, int lks, bool copies, int cstage,
+                    int64_t cm0, int64_t cn0, int ckt) {
+        if (copies)
+            copy_tile(cstage, cm0, cn0, ckt);
+        __builtin_amdgcn_sched_barrier(0);
+        if (reads)
+            load_frags(nxt, lstage, lks);
+        if constexpr (USUM) {
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    xs[j] = __builtin_amdgcn_sdot4(cur.b[j][e], 0x01010101, xs[j], false);
+        }
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            widen(cur, i);
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0);
+        }
+        constexpr int PER = (FN * FM) / LOADS > 0 ? (FN * FM) / LOADS : 1;
+#pragma unroll
+        for (int k = 0; k < LOADS; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // then MFMAs
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // The dequant scales of an output tile go into registers early (loaded
+    // before the previous tile's epilogue, so their latency hides) and into
+    // LDS before its own epilogue.  Indices are clamped into range; values
+    // past the edge are never used.
+    constexpr int NSC = OUT != OUT_I32 ? (TN + TM + NW * 64 - 1) / (NW * 64) : 0;
+    static_assert(NSC + STORES + D < 64, "vmcnt range");
+    float scv[NSC > 0 ? NSC : 1], scn[NSC > 0 ? NSC : 1];
+    auto load_scales = [&](float (&dst)[NSC > 0 ? NSC : 1], int64_t m0, int64_t n0) {
+#pragma unroll
+        for (int i = 0; i < NSC; ++i) {
+            const int q = (int)threadIdx.x + i * NW * 64;
+            const float *src = q < TN ? args.s_w + min(n0 + q, N - 1)
+                                      : args.s_tok + min(m0 + min(q - TN, TM - 1), M - 1);
+            dst[i] = *src;
+        }
+    };
+
+    int t = blockIdx.x;
+    if (t >= tiles)
+        return;
+    int tn, tm;
+    tile_coords(t, tiles_n, tiles_m, group_m, tn, tm);
+    int g = 0;  // K tiles this workgroup has consumed: K tile kt of the current output tile is in stage (g + kt) & 1
+    load_scales(scv, (int64_t)tm * TM, (int64_t)tn * TN);
+    copy_tile(0, (int64_t)tm * TM, (int64_t)tn * TN, 0);
+    copy_tile(1, (int64_t)tm * TM, (int64_t)tn * TN, 1);
+    wait_vmcnt<D>();  // K tile 0 has landed
+    for (;;) {
+        const int64_t n0 = (int64_t)tn * TN, m0 = (int64_t)tm * TM;
+        const int tnext = t + (int)gridDim.x;
+        const bool has_next = tnext < tiles;  // workgroup-uniform
+        int tn2 = 0, tm2 = 0;
+        if (has_next)
+            tile_coords(tnext, tiles_n, tiles_m, group_m, tn2, tm2);
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                acc[i][j] = i32x16{};
+#pragma unroll
+        for (int j = 0; j < (USUM ? FM : 1); ++j)
+            xs[j] = 0;
+        __builtin_amdgcn_s_barrier();  // K tile 0 of this output tile is in, in every wave's view
+        __builtin_amdgcn_sched_barrier(0);
+        Frags f0, f1;
+        load_frags(f0, g & 1, 0);
+        for (int kt = 0; kt < KT; ++kt) {
+            const int cs = (g + kt) & 1, ns = cs ^ 1;
+            const bool last = kt == KT - 1;
+            step(f0, f1, true, cs, 1, false, 0, 0, 0, 0);
+            step(f1, f0, true, cs, 2, false, 0, 0, 0, 0);
+            step(f0, f1, true, cs, 3, false, 0, 0, 0, 0);
+            // Every wave is done reading stage cs.  Before the barrier: K tile
+            // kt + 1 has landed (it is the newest copy in flight, except in the
+            // last K tile, where the next output tile's first K tile may follow).
+            wait_lgkm0();
+            if (!last)
+                wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // refill stage cs: K tile kt + 2, or the next output tile's first
+            const bool own = kt + 2 < KT, nxt_tile = kt + 2 == KT && has_next;
+            step(f1, f0, !last, ns, 0, own || nxt_tile, cs, own ? m0 : (int64_t)tm2 * TM,
+                 own ? n0 : (int64_t)tn2 * TN, own ? kt + 2 : 0);
+        }
+        const int es = (g + KT - 1) & 1;  // the stage of the last K tile: idle now
+        g += KT;
+        // the next output tile's scales (after its first K tile's copies, before
+        // this tile's stores: the wait for those copies below counts them)
+        load_scales(scn, (int64_t)tm2 * TM, (int64_t)tn2 * TN);
+
+        if constexpr (USUM) {
+            // both halves of each token's K: sum q x = sum u x - 8 sum x
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                const int s8 = 8 * (xs[j] + __shfl_xor(xs[j], 32, 64));
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        acc[i][j][e] -= s8;
+            }
+        }
+
+        // Epilogue.  Block (i, j) gives the lane token m = wm*WM + 32j + lane%32
+        // and, for q = 0..3, channels nb .. nb+3, nb = wn*WN + 32i + 8q + 4*(lane/32).
+        // (The lane index is re-derived behind an empty asm so that no
+        // epilogue address is computed once before the tile loop and kept
+        // live through it.)
+        int elane = (int)threadIdx.x & 63;
+        asm volatile("" : "+v"(elane));
+        const int frow = elane & 31, fhalf = elane >> 5;
+        if constexpr (OUT == OUT_I32) {
+            const uint64_t ybase = reinterpret_cast<uint64_t>(args.out) + (uint64_t)m0 * (uint64_t)N * 4u;
+            const auto ry = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ybase), (short)0,
+                                                              (int)(min((int64_t)TM, M - m0) * N * 4), 0x00020000);
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                const int r = wm * WM + j * 32 + frow;
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int64_t nb = n0 + wn * WN + i * 32 + q * 8 + fhalf * 4;
+                        const uint32_t off = nb < N ? (uint32_t)(((int64_t)r * N + nb) * 4) : 0x80000000u;
+                        const i32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                         acc[i][j][4 * q + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NSC; ++i) {
+                const int q = (int)threadIdx.x + i * NW * 64;
+                if (q < TN)
+                    s_sw[q] = scv[i];
+                else if (q < TN + TM)
+                    s_st[q - TN] = scv[i];
+            }
+            __syncthreads();  // scales in LDS; every wave is done with stage es
+            const uint64_t ybase = reinterpret_cast<uint64_t>(args.out) + (uint64_t)m0 * (uint64_t)N * 2u;
+            const auto ry = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ybase), (short)0,
+                                                              (int)(min((int64_t)TM, M - m0) * N * 2), 0x00020000);
+            // Dequantize every block to packed 16-bit values first (half the
+            // registers of the int32 sums), channel block by channel block so
+            // each block's scales are read once for both token blocks.
+            float st[FM];
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                st[j] = s_st[wm * WM + j * 32 + frow];
+            uint2 pk[FN][FM][4];
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 sw = *reinterpret_cast<const f32x4 *>(&s_sw[wn * WN + i * 32 + q * 8 + fhalf * 4]);
+#pragma unroll
+                    for (int j = 0; j < FM; ++j) {
+                        float y[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            y[e] = (float)acc[i][j][4 * q + e] * st[j] * sw[e];
+                        pk[i][j][q].x = pack2<OUT>(y[0], y[1]);
+                        pk[i][j][q].y = pack2<OUT>(y[2], y[3]);
+                    }
+                }
+            const uint32_t rowbytes = (uint32_t)N * 2u;
+            const int nvalid = (int)min((int64_t)TN, N - n0);  // channels of this tile inside N
+            // Then 32 token rows at a time through this wave's share of the idle
+            // stage (rows of CB channel blocks, padded by 16 bytes so the 32 rows
+            // a write touches fall in distinct bank groups), leaving as 16-byte
+            // pieces, consecutive lanes along a token row.
+            uint8_t *ob = smem + es * STAGE + wave * WREG;
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int p = 0; p < NPASS; ++p) {
+                    const int i0 = p * CB;
+                    const int ncb = min(CB, FN - i0);  // compile-time after unrolling
+#pragma unroll
+                    for (int ii = 0; ii < CB; ++ii)
+                        if (ii < ncb)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                *reinterpret_cast<uint2 *>(ob + frow * ROWB + (ii * 32 + q * 8 + fhalf * 4) * 2) =
+                                    pk[i0 + ii][j][q];
+                    // ncb * 4 pieces of 16 bytes per row (a power of two up to 16):
+                    // lane l takes piece l % cpr of rows l / cpr + it * 64 / cpr
+                    const int cpr = ncb * 4;
+                    const int lr = elane / cpr, lc = elane % cpr;
+                    const int nc = wn * WN + i0 * 32 + lc * 8;  // channel within the tile
+                    const uint32_t base = nc < nvalid ? (uint32_t)(wm * WM + j * 32 + lr) * rowbytes +
+                                                            (uint32_t)(n0 + nc) * 2u
+                                                      : 0x80000000u;  // past the buffer: dropped
+                    const uint8_t *src = ob + lr * ROWB + lc * 16;
+#pragma unroll
+                    for (int it = 0; it < 32 * cpr / 64; ++it) {
+                        const uint4 v = *reinterpret_cast<const uint4 *>(src + it * (64 / cpr) * ROWB);
+                        __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, ry,
+                                                               base + (uint32_t)(it * (64 / cpr)) * rowbytes, 0,
+                                                               2 /* non-temporal */);
+                    }
+                }
+        }
+        if (!has_next)
+            break;
+        // every wave is done with stage es and with the scales; refill es with
+        // K tile 1 of the next output tile and wait for its K tile 0 (copied
+        // before this tile's stores)
+        __syncthreads();
+        t = tnext;
+        tn = tn2;
+        tm = tm2;
+#pragma unroll
+        for (int i = 0; i < NSC; ++i)
+            scv[i] = scn[i];
+        copy_tile(es, (int64_t)tm * TM, (int64_t)tn * TN, 1);  // es == (g + 1) & 1
+        // after K tile 0: the scale loads, the stores, K tile 1's copies
+        wait_vmcnt<NSC + STORES + D>();
+    }
+    wait_vmcnt<0>();
+}
+
 template <int TN, int TM, int WN, int WM, int BK, int BITS, int GS, int OUT, int STAGES>
 hipError_t launch_cfg(const ProductArgs &a, hipStream_t stream)
 {
@@ -832,6 +1247,21 @@ int compute_units()
     return cached[dev];
 }
 
+template <int TN, int TM, int WN, int WM, int BITS, int OUT>
+hipError_t launch_wide(const ProductArgs &a, hipStream_t stream)
+{
+
+    const int tiles_n = (int)((a.N + TN - 1) / TN);
+    const int tiles_m = (int)((a.M + TM - 1) / TM);
+    const int tiles = tiles_n * tiles_m;
+    int grid = compute_units();
+    if (grid > tiles)
+        grid = tiles;
+    hipLaunchKernelGGL((gemm_wide_kernel<TN, TM, WN, WM, BITS, OUT>), dim3(grid), dim3((TN / WN) * (TM / WM) * 64),
+                       0, stream, a, tiles_n, tiles_m, 8);
+    return hipGetLastError();
+}
+
 int64_t rounds(int64_t M, int64_t N, int TM, int TN)
 {
     const int64_t tiles = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
@@ -872,6 +1302,10 @@ hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
         return launch_cfg<160, 256, 160, 64, 64, BITS, 0, OUT, 4>(a, stream);
     if (a.M <= 1024)
         return launch_cfg<160, 128, 160, 32, 64, BITS, 0, OUT, 4>(a, stream);
+    // whole 128-byte K tiles, at least two of them, and a 256-row output
+    // tile addressable with 32-bit offsets: the persistent kernel
+    if (a.K % 128 == 0 && a.K >= 256 && 256 * a.N * 4 < (int64_t(1) << 31))
+        return launch_wide<320, 256, 160, 64, BITS, OUT>(a, stream);
     const int64_t r320 = rounds(a.M, a.N, 256, 320), r256 = rounds(a.M, a.N, 256, 256);
     if (100 * r320 <= 80 * r256)
         return launch_cfg<320, 256, 160, 64, 64, BITS, 0, OUT, 4>(a, stream);
