@@ -1201,6 +1201,309 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_wide_kernel(P
     wait_vmcnt<0>();
 }
 
+// Persistent per-group product for many tokens (int8 or packed int4
+// weights, groups of 64 / 128 along K): the copy path of gemm_wide_kernel
+// (128-byte K tiles, two-stage ring, one workgroup per compute unit walking
+// output tiles, copies streaming across tiles) with the operands of the
+// per-group gemm_kernel (tokens are operand A, so a lane's outputs belong to
+// one channel per 32-channel block and need one group scale each).  The
+// channel scales of a K tile's groups travel with it into the ring.
+//
+// What differs is where the group scale-accumulate runs: the int32 sums of
+// block i of a closed group are converted and scaled into the fp32 sums
+// (16 conversions and 16 FMAs per lane) just before block i's first MFMA of
+// the next group, so the vector ALU works on one block while the matrix core
+// works on the previous one, instead of all blocks in one burst after the
+// group's last MFMA.  The last group of an output tile is scaled before its
+// epilogue.  Outputs leave as 2-byte range-checked buffer stores, consecutive
+// lanes along a token row.  Needs K % 128 == 0, K >= 256, fp16 / bf16 output.
+template <int TN, int TM, int WN, int WM, int BITS, int GS, int OUT>
+__global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_kernel(ProductArgs args, int tiles_n,
+                                                                                     int tiles_m, int group_m)
+{
+    constexpr int BK = 128;
+    constexpr int NWN = TN / WN, NWM = TM / WM, NW = NWN * NWM;
+    constexpr int FN = WN / 32;  // 32-channel blocks per wave
+    static_assert(WM == 32, "one 32-token block per wave");
+    static_assert(OUT != OUT_I32, "the int32 hook takes gemm_kernel");
+    constexpr int XROW = BK, WROW = BITS == 8 ? BK : BK / 2;
+    constexpr int XBYTES = TM * XROW, WBYTES = TN * WROW;
+    constexpr int GPT = BK / GS;  // groups per K tile
+    constexpr int SPG = GS / 32;  // 32-deep steps per group
+    constexpr int SBYTES = (GPT * TN * 4 + 1023) / 1024 * 1024;
+    constexpr int STAGE = XBYTES + WBYTES + SBYTES;
+    constexpr int XB = XBYTES / 1024, WB = WBYTES / 1024, SB = GPT * TN / 64;
+    constexpr int DX = (XB + NW - 1) / NW, DW = (WB + NW - 1) / NW, DS = (SB + NW - 1) / NW;
+    constexpr int D = DX + DW + DS;  // copies per wave per K tile
+    static_assert(XBYTES % 1024 == 0 && WBYTES % 1024 == 0 && TN % 64 == 0, "whole copy blocks");
+    constexpr int STORES = FN * 16;  // 2-byte output stores per wave per output tile
+    constexpr int NSC = (TM + NW * 64 - 1) / (NW * 64);
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) float s_st[TM];
+
+    const int64_t M = args.M, N = args.N, K = args.K;
+    const int KT = (int)(K / BK);
+    const int G = (int)(K / GS);
+    const int tiles = tiles_n * tiles_m;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave % NWN, wm = wave / NWN;
+    const int frow = lane & 31, fhalf = lane >> 5;
+    const uint32_t wld = (uint32_t)(BITS == 8 ? K : K / 2);
+    const i32x4 rX = make_rsrc(args.xq, (uint32_t)(M * K));
+    const i32x4 rW = make_rsrc(args.wq, (uint32_t)(N * (int64_t)wld));
+    const i32x4 rS = make_rsrc(args.s_w, (uint32_t)(N * G * 4));
+
+    // Copies, as in gemm_wide_kernel; scale block sb (0 .. SB-1) holds the
+    // tile's channels 64 (sb % (TN/64)) .. +63 of its group sb / (TN/64):
+    // lane l copies s_w[n0 + 64 (sb % (TN/64)) + l, g0 + sb / (TN/64)] (past N:
+    // out of range, reads 0).
+    constexpr int CX = XROW / 16, CW = WROW / 16;
+    constexpr int RX = 1024 / XROW, RW = 1024 / WROW;
+    uint32_t xlane[2], wlane[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        const int rx = par * RX + lane / CX;
+        xlane[par] = (uint32_t)((lane / CX) * K) + (((lane % CX) ^ swz8<BK>(rx)) << 4);
+        const int rw = par * RW + lane / CW;
+        wlane[par] = (uint32_t)((lane / CW) * (int64_t)wld) +
+                     (((lane % CW) ^ (BITS == 8 ? swz8<BK>(rw) : swz4<BK>(rw))) << 4);
+    }
+    uint32_t slane = (uint32_t)lane * (uint32_t)G * 4u;
+    const uint32_t smem_lds = lds_address(smem);
+    const uint32_t xstep = (uint32_t)(RX * K), wstep = (uint32_t)(RW * (int64_t)wld);
+    auto copy_tile = [&](int stage, int64_t m0, int64_t n0, int kt) {
+        asm volatile("" : "+v"(xlane[0]), "+v"(xlane[1]), "+v"(wlane[0]), "+v"(wlane[1]), "+v"(slane));
+        const uint32_t lds = smem_lds + stage * STAGE;
+        const uint32_t xo = (uint32_t)(m0 * K) + (uint32_t)kt * XROW;
+#pragma unroll
+        for (int j = 0; j < DX; ++j) {
+            const int b = min(wave * DX + j, XB - 1);  // wavefront-uniform
+            dma16(rX, lds + b * 1024, xlane[b & 1] + xo + (uint32_t)b * xstep);
+        }
+        const uint32_t wo = (uint32_t)(n0 * (int64_t)wld) + (uint32_t)kt * WROW;
+#pragma unroll
+        for (int j = 0; j < DW; ++j) {
+            const int b = min(wave * DW + j, WB - 1);
+            dma16(rW, lds + XBYTES + b * 1024, wlane[b & 1] + wo + (uint32_t)b * wstep);
+        }
+#pragma unroll
+        for (int j = 0; j < DS; ++j) {
+            const int sb = min(wave * DS + j, SB - 1);
+            const int gi = sb / (TN / 64), cb = sb % (TN / 64);
+            const uint32_t so = (uint32_t)((n0 + cb * 64) * G + (int64_t)kt * GPT + gi) * 4u;
+            dma4(rS, lds + XBYTES + WBYTES + sb * 256, slane + so);
+        }
+    };
+
+    // Fragments: operand A = the wave's 32 token rows, operand B = its FN
+    // 32-channel blocks (packed int4 bytes until widened).
+    struct Frags {
+        i32x4 x;
+        i32x4 w[FN];
+        uint2 wp[BITS == 4 ? FN : 1];
+    };
+    const uint32_t xbase = (uint32_t)((wm * WM + frow) * XROW + ((fhalf ^ swz8<BK>(frow)) << 4));
+    const uint32_t wbase = BITS == 8 ? (uint32_t)(XBYTES + (wn * WN + frow) * WROW + ((fhalf ^ swz8<BK>(frow)) << 4))
+                                     : (uint32_t)(XBYTES + (wn * WN + frow) * WROW + (swz4<BK>(frow) << 4) + fhalf * 8);
+    auto load_frags = [&](Frags &f, int stage, int ks) {
+        const uint32_t a = (xbase + (uint32_t)(stage * STAGE)) ^ (uint32_t)(ks << 5);
+        const uint32_t b = (wbase + (uint32_t)(stage * STAGE)) ^ (uint32_t)(ks << (BITS == 8 ? 5 : 4));
+        f.x = *reinterpret_cast<const i32x4 *>(smem + a);
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            if constexpr (BITS == 8)
+                f.w[i] = *reinterpret_cast<const i32x4 *>(smem + b + i * 32 * WROW);
+            else
+                f.wp[i] = *reinterpret_cast<const uint2 *>(smem + b + i * 32 * WROW);
+        }
+    };
+    // channel scales of the wave's blocks for group gi of the K tile in `stage`
+    auto load_scales_lds = [&](float (&sw)[FN], int stage, int gi) {
+        const float *ss = reinterpret_cast<const float *>(smem + stage * STAGE + XBYTES + WBYTES) + gi * TN;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+            sw[i] = ss[wn * WN + i * 32 + frow];
+    };
+
+    i32x16 acc[FN];
+    float facc[FN][16];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+        acc[i] = i32x16{};
+    // One 32-deep step.  first: the step opens a group: block i of the group
+    // that closed before it is scaled into facc with the scales `sw` right
+    // before block i's first MFMA (which starts from zero) overwrites its
+    // sums.  (The first group of an output tile finds the previous tile's
+    // already-scaled sums, or zeros, with scales 0.)
+    auto step = [&](auto first, Frags &cur, Frags &nxt, bool reads, int lstage, int lks,
+                    const float (&sw)[FN], bool copies, int cstage, int64_t cm0, int64_t cn0, int ckt) {
+        if (copies)
+            copy_tile(cstage, cm0, cn0, ckt);
+        __builtin_amdgcn_sched_barrier(0);
+        if (reads)
+            load_frags(nxt, lstage, lks);
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            if constexpr (decltype(first)::value) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    facc[i][e] += (float)acc[i][e] * sw[i];
+            }
+            if constexpr (BITS == 4) {
+                uint32_t d0, d1, d2, d3;
+                unpack8(cur.wp[i].x, d0, d1);
+                unpack8(cur.wp[i].y, d2, d3);
+                cur.w[i] = i32x4{(int)d0, (int)d1, (int)d2, (int)d3};
+            }
+            if constexpr (decltype(first)::value) {
+                // Block i's MFMA must follow its scaling: otherwise the compiler
+                // may run the new group's MFMAs first and keep both groups' sums
+                // live (twice the registers).  The weight fragment passes through
+                // an empty asm that takes the scaled sums as inputs.
+                asm volatile(""
+                             : "+v"(cur.w[i])
+                             : "v"(facc[i][0]), "v"(facc[i][1]), "v"(facc[i][2]), "v"(facc[i][3]),
+                               "v"(facc[i][4]), "v"(facc[i][5]), "v"(facc[i][6]), "v"(facc[i][7]),
+                               "v"(facc[i][8]), "v"(facc[i][9]), "v"(facc[i][10]), "v"(facc[i][11]),
+                               "v"(facc[i][12]), "v"(facc[i][13]), "v"(facc[i][14]), "v"(facc[i][15]));
+                acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.x, cur.w[i], i32x16{}, 0, 0, 0);
+            } else {
+                acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.x, cur.w[i], acc[i], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto load_tok_scales = [&](float (&dst)[NSC], int64_t m0) {
+#pragma unroll
+        for (int i = 0; i < NSC; ++i) {
+            const int q = (int)threadIdx.x + i * NW * 64;
+            dst[i] = args.s_tok[min(m0 + min(q, TM - 1), M - 1)];
+        }
+    };
+    float scv[NSC], scn[NSC];
+
+    int t = blockIdx.x;
+    if (t >= tiles)
+        return;
+    int tn, tm;
+    tile_coords(t, tiles_n, tiles_m, group_m, tn, tm);
+    int g = 0;  // K tiles consumed: K tile kt of the current output tile is in stage (g + kt) & 1
+    load_tok_scales(scv, (int64_t)tm * TM);
+    copy_tile(0, (int64_t)tm * TM, (int64_t)tn * TN, 0);
+    copy_tile(1, (int64_t)tm * TM, (int64_t)tn * TN, 1);
+    wait_vmcnt<D>();  // K tile 0 has landed
+    for (;;) {
+        const int64_t n0 = (int64_t)tn * TN, m0 = (int64_t)tm * TM;
+        const int tnext = t + (int)gridDim.x;
+        const bool has_next = tnext < tiles;  // workgroup-uniform
+        int tn2 = 0, tm2 = 0;
+        if (has_next)
+            tile_coords(tnext, tiles_n, tiles_m, group_m, tn2, tm2);
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                facc[i][e] = 0.f;
+        __builtin_amdgcn_s_barrier();  // K tile 0 of this output tile is in, in every wave's view
+        __builtin_amdgcn_sched_barrier(0);
+        Frags f0, f1;
+        load_frags(f0, g & 1, 0);
+        // scales of the group waiting to be scaled (read from the ring before
+        // the barrier after which its stage may be refilled)
+        float swp[FN];
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+            swp[i] = 0.f;
+        for (int kt = 0; kt < KT; ++kt) {
+            const int cs = (g + kt) & 1, ns = cs ^ 1;
+            const bool last = kt == KT - 1;
+            step(Flag<true>{}, f0, f1, true, cs, 1, swp, false, 0, 0, 0, 0);
+            step(Flag<false>{}, f1, f0, true, cs, 2, swp, false, 0, 0, 0, 0);
+            if constexpr (GPT == 2) {
+                float swa[FN];  // the K tile's first group, closed after step 1
+                load_scales_lds(swa, cs, 0);
+                step(Flag<true>{}, f0, f1, true, cs, 3, swa, false, 0, 0, 0, 0);
+            } else {
+                step(Flag<false>{}, f0, f1, true, cs, 3, swp, false, 0, 0, 0, 0);
+            }
+            // the group closing at this K tile's end is scaled in the next K
+            // tile (or before the epilogue)
+            load_scales_lds(swp, cs, GPT - 1);
+            wait_lgkm0();
+            if (!last)
+                wait_vmcnt<0>();  // K tile kt + 1 has landed
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // refill stage cs with the next K tile not yet copied: K tile
+            // kt + 2 of this output tile, or K tile kt + 2 - KT of the next
+            const bool own = kt + 2 < KT;
+            const bool nxt_tile = !own && has_next;
+            step(Flag<false>{}, f1, f0, !last, ns, 0, swp, own || nxt_tile, cs,
+                 own ? m0 : (int64_t)tm2 * TM, own ? n0 : (int64_t)tn2 * TN, own ? kt + 2 : kt + 2 - KT);
+        }
+        g += KT;
+        load_tok_scales(scn, (int64_t)tm2 * TM);  // after the next tile's first copies
+        // the last group
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                facc[i][e] += (float)acc[i][e] * swp[i];
+
+        // Epilogue: y = s_tok[m] * facc.  Block i: channel n = wn*WN + 32i +
+        // lane%32, tokens wm*WM + 8q + 4*(lane/32) + e for element 4q + e.
+#pragma unroll
+        for (int i = 0; i < NSC; ++i) {
+            const int q = (int)threadIdx.x + i * NW * 64;
+            if (q < TM)
+                s_st[q] = scv[i];
+        }
+        __syncthreads();  // token scales in LDS (the previous tile's readers are past its barrier)
+        int elane = (int)threadIdx.x & 63;
+        asm volatile("" : "+v"(elane));
+        const int er = elane & 31, eh = elane >> 5;
+        const uint32_t rowbytes = (uint32_t)N * 2u;
+        const uint64_t ybase = reinterpret_cast<uint64_t>(args.out) + (uint64_t)m0 * (uint64_t)N * 2u;
+        const auto ry = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ybase), (short)0,
+                                                          (int)(min((int64_t)TM, M - m0) * N * 2), 0x00020000);
+        const int nvalid = (int)min((int64_t)TN, N - n0);
+        f32x4 stv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            stv[q] = *reinterpret_cast<const f32x4 *>(&s_st[wm * WM + q * 8 + eh * 4]);
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int nc = wn * WN + i * 32 + er;
+            const uint32_t base = nc < nvalid ? (uint32_t)(wm * WM + eh * 4) * rowbytes + (uint32_t)(n0 + nc) * 2u
+                                              : 0x80000000u;  // past the buffer: dropped
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float y = stv[q][e] * facc[i][4 * q + e];
+                    __builtin_amdgcn_raw_buffer_store_b16(out_bits<OUT>(y), ry,
+                                                          base + (uint32_t)(q * 8 + e) * rowbytes, 0, 2);
+                }
+        }
+        if (!has_next)
+            break;
+        __syncthreads();  // every wave is done reading the token scales
+        t = tnext;
+        tn = tn2;
+        tm = tm2;
+#pragma unroll
+        for (int i = 0; i < NSC; ++i)
+            scv[i] = scn[i];
+        // the next tile's K tile 0 is older than its K tile 1, the token scale
+        // loads and this tile's stores
+        wait_vmcnt<(D + NSC + STORES < 63 ? D + NSC + STORES : 63)>();
+    }
+    wait_vmcnt<0>();
+}
+
 template <int TN, int TM, int WN, int WM, int BK, int BITS, int GS, int OUT, int STAGES>
 hipError_t launch_cfg(const ProductArgs &a, hipStream_t stream)
 {
@@ -1262,6 +1565,20 @@ hipError_t launch_wide(const ProductArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+template <int TN, int TM, int WN, int WM, int BITS, int GS, int OUT>
+hipError_t launch_group_wide(const ProductArgs &a, hipStream_t stream)
+{
+    const int tiles_n = (int)((a.N + TN - 1) / TN);
+    const int tiles_m = (int)((a.M + TM - 1) / TM);
+    const int tiles = tiles_n * tiles_m;
+    int grid = compute_units();
+    if (grid > tiles)
+        grid = tiles;
+    hipLaunchKernelGGL((gemm_group_wide_kernel<TN, TM, WN, WM, BITS, GS, OUT>), dim3(grid),
+                       dim3((TN / WN) * (TM / WM) * 64), 0, stream, a, tiles_n, tiles_m, 8);
+    return hipGetLastError();
+}
+
 int64_t rounds(int64_t M, int64_t N, int TM, int TN)
 {
     const int64_t tiles = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
@@ -1316,6 +1633,16 @@ hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
 template <int BITS, int GS, int OUT>
 hipError_t launch_group(const ProductArgs &a, hipStream_t stream)
 {
+    // Groups of 128 above 3072 tokens: the persistent kernel (M = 4096, N =
+    // 2560, K = 10240: int8 176.7 -> 153.3 us, int4 209.1 -> 199.9 us on one
+    // box).  Groups of 64 it did not speed up (187.2 -> 187.6 us; int4 238 ->
+    // 249 us): there the scale-accumulate's two vector operations per output
+    // and group bound both kernels.  Below 3072 tokens its 320 x 128 tiles
+    // leave compute units idle.
+    if constexpr (OUT != OUT_I32 && GS == 128) {
+        if (a.M > 3072 && a.K % 128 == 0 && a.K >= 256 && 128 * a.N * 2 < (int64_t(1) << 31))
+            return launch_group_wide<320, 128, 160, 32, BITS, GS, OUT>(a, stream);
+    }
     if (a.M <= 768)
         return launch_cfg<64, 128, 64, 32, 64, BITS, GS, OUT, 6>(a, stream);
     if (a.M <= 1536)
