@@ -10,8 +10,8 @@ timed on its own with HIP events recorded on the launch stream.
 
 `value` is INT8 TOPS of the whole step (2*M*N*K / step time, steps back to
 back).  The JSON line also carries: the roofline of the product kernel
-(achieved TOPS from its average launch duration -- the same launches timed
-back to back between two HIP events on the launch stream -- against the
+(achieved TOPS from its average launch duration -- HIP events on the launch
+stream around each product launch of the timed steps -- against the
 5.0 POPS dense INT8 peak, and its HBM bytes per launch from the committed
 counter summary), the
 oracle's CPU throughput on a bounded sample of the same workload, the
@@ -61,6 +61,10 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
                         "reference for the HBM byte counters)")
+    p.add_argument("--profile", metavar="WORKLOAD[:GS]:M", default=None,
+                   help="only run one operator workload (e.g. w8a8_pc:4096, w8a8_pg:64:1024) for "
+                        "a profiler: 30 launches of the product kernel, then 30 of the whole "
+                        "layer, over rotating copies")
     return p.parse_args()
 
 
@@ -116,6 +120,57 @@ class Layer:
         else:
             f(s["x"], self.M, self.K, self.K, s["wq"], s["sw"], self.N, self.gs, self.ws,
               self.ws_bytes, s["y"])
+
+
+class LaunchEvents:
+    """HIP timing events made with hipEventDisableSystemFence, recorded on a
+    given stream through the HIP runtime torch already loaded.
+
+    A default timing event (torch.cuda.Event) ends with a system-scope
+    release and makes the next dispatch acquire at system scope, which opens
+    a gap of a few microseconds before the kernel after it; that gap falls
+    inside the bracket of the kernel being timed.  These events only order
+    and time work on the device, so a bracket around one launch comes within
+    about 1% of the kernel's own duration in a kernel trace."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        import ctypes
+        self._c = ctypes
+        hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch loaded (same soname)
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip = hip
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
+            if rc != 0:
+                self.close()
+                raise RuntimeError("hipEventCreateWithFlags failed (%d)" % rc)
+            self.ev.append(e)
+
+    def record(self, i, stream):
+        rc = self._hip.hipEventRecord(self.ev[i], self._c.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed (%d)" % rc)
+
+    def ms(self, i, j):
+        """Milliseconds from event i to event j (both complete)."""
+        f = self._c.c_float()
+        rc = self._hip.hipEventElapsedTime(self._c.byref(f), self.ev[i], self.ev[j])
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return f.value
+
+    def close(self):
+        for e in self.ev:
+            self._hip.hipEventDestroy(e)
+        self.ev = []
 
 
 def alg_bytes(bits, gs, N, K, M):
@@ -588,6 +643,9 @@ def main():
         return
     cider.load(build_if_missing=True)
     assert cider.cider_is_available(), "libcider.so reports no usable gfx950 device"
+    if args.profile:
+        profile_workload(torch, cider, si, args.profile)
+        return
 
     # ---------------------------------------------------------- headline ---
     M, N, K = 4096, 10240, 2560
@@ -619,25 +677,26 @@ def main():
     # is the time from the second event of step i to the first of step i+1
     # (or the closing event), so both kernel averages come from the very
     # launches the step time covers and cannot exceed it.
-    ev_q = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev_g = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev_end = torch.cuda.Event(enable_timing=True)
+    # Events 2i and 2i+1 precede step i's quantize and product launches;
+    # event 2K closes the region.
+    S = args.steps
+    ev = LaunchEvents(2 * S + 1)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev_q[i].record(stream)
+    for i in range(S):
+        ev.record(2 * i, stream)
         L.quantize(i)
-        ev_g[i].record(stream)
+        ev.record(2 * i + 1, stream)
         L.gemm(i)
-    ev_end.record(stream)
+    ev.record(2 * S, stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    ms_per_step = dt / args.steps * 1e3
-    value = ops / (dt / args.steps) / 1e12
-    nxt = ev_q[1:] + [ev_end]
-    gemm_ms = [ev_g[i].elapsed_time(nxt[i]) for i in range(args.steps)]
-    quant_ms = [ev_q[i].elapsed_time(ev_g[i]) for i in range(args.steps)]
-    device_ms = ev_q[0].elapsed_time(ev_end)
+    ms_per_step = dt / S * 1e3
+    value = ops / (dt / S) / 1e12
+    gemm_ms = [ev.ms(2 * i + 1, 2 * i + 2) for i in range(S)]
+    quant_ms = [ev.ms(2 * i, 2 * i + 1) for i in range(S)]
+    device_ms = ev.ms(0, 2 * S)
+    ev.close()
     gemm_s = sum(gemm_ms) / args.steps / 1e3
     quant_s = sum(quant_ms) / args.steps / 1e3
     assert gemm_s + quant_s <= dt / args.steps * 1.0001, (gemm_s, quant_s, dt / args.steps)
@@ -669,11 +728,13 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
                      "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
                      "traffic": traffic,
-                     "kernel": "gemm_kernel (int8 matrix-core product + dequant, per channel)",
+                     "kernel": "gemm_wide_kernel<320, 256, 160, 64, 8, 0> (int8 matrix-core product "
+                               "+ dequant, per channel)",
                      "kernel_us": round(gemm_s * 1e6, 2),
                      "quantize_kernel_us": round(quant_s * 1e6, 2),
-                     "timing": "HIP events on the launch stream around each launch of the "
-                               "timed steps (the same launches as ms_per_step)"},
+                     "timing": "HIP events without system-scope fences on the launch stream "
+                               "around each launch of the timed steps (the same launches as "
+                               "ms_per_step)"},
     }
     del L
     torch.cuda.empty_cache()
@@ -720,6 +781,28 @@ def main():
         result["cpu_baseline"] = None
 
     print(json.dumps(result), flush=True)
+
+
+def profile_workload(torch, cider, si, spec, launches=30):
+    """One operator workload for a profiler's counters: its product kernel,
+    then its whole layer (the linear call with the split workspace), each
+    `launches` times back to back over rotating copies."""
+    parts = spec.split(":")
+    name, M = parts[0], int(parts[-1])
+    wl = si.WORKLOADS[name]
+    gs = int(parts[1]) if len(parts) == 3 else wl["group_sizes"][0]
+    N, K, bits = wl["N"], wl["K"], wl["bits"]
+    B = copies_for(bits, gs, N, K, M)
+    L = Layer(torch, cider, bits, gs, N, K, M, si.activations(M, K), si.weights(N, K), B)
+    torch.cuda.synchronize()
+    log("profile %s gs=%d M=%d N=%d K=%d: %d product launches, %d layer launches"
+        % (name, gs, M, N, K, launches, launches))
+    for i in range(launches):
+        L.gemm(i)
+    torch.cuda.synchronize()
+    for i in range(launches):
+        L.linear(i)
+    torch.cuda.synchronize()
 
 
 def one_token(torch, cider, x_np, w_np, N, K, result):
