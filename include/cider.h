@@ -195,19 +195,17 @@ size_t cider_linear_workspace_bytes(int64_t M, int64_t K);
 
 /* Bytes of workspace that also let a linear call of this shape split K over
    several workgroups per output tile (2 to 8 splits on the matrix-core path,
-   where that is faster: per group up to 256 tokens, int4 per channel up to 64
-   tokens; int8 per channel never): the int8 activations and scales as above,
-   then the partial sums of the split product (4 bytes per output of each 64 x
-   32, 64 or 128 tile and split) and one counter per tile. Equal to
-   cider_linear_workspace_bytes(M, K) when the shape is not split, shapes the
-   matrix-vector kernel serves under the current path setting included. The
-   split count follows the current device's compute-unit count. A linear call
-   given at least this many bytes splits; given fewer (but at least
-   cider_linear_workspace_bytes(M, K)) it runs unsplit. Per channel the split
-   result is bit-identical to the unsplit one (the int32 partial sums add
-   exactly); per group the fp32 partial sums of the splits are added in split
-   order (deterministic; a different rounding order from the unsplit
-   group-by-group sum, within the same tolerance of the exact result). */
+   where that is faster: per group up to 256 tokens; per channel never): the
+   int8 activations and scales as above, then the partial sums of the split
+   product (4 bytes per output of each 64 x 32, 64 or 128 tile and split) and
+   one counter per tile. Equal to cider_linear_workspace_bytes(M, K) when the
+   shape is not split, shapes the matrix-vector kernel serves under the
+   current path setting included. The split count follows the current
+   device's compute-unit count. A linear call given at least this many bytes
+   splits; given fewer (but at least cider_linear_workspace_bytes(M, K)) it
+   runs unsplit. The fp32 partial sums of the splits are added in split order
+   (deterministic; a different rounding order from the unsplit group-by-group
+   sum, within the same tolerance of the exact result). */
 size_t cider_linear_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int bits,
                                        int group_size);
 

@@ -64,8 +64,8 @@ def _r256(v):
     return (v + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("M,N,K,bits,gs", [(64, 10240, 2560, 4, 0), (16, 2560, 10240, 4, 64),
-                                           (128, 64, 10240, 8, 128), (9, 640, 2560, 4, 0),
+@pytest.mark.parametrize("M,N,K,bits,gs", [(64, 2560, 10240, 8, 64), (16, 2560, 10240, 4, 64),
+                                           (128, 64, 10240, 8, 128), (9, 640, 2560, 4, 128),
                                            (100, 320, 1024, 8, 64), (256, 2560, 10240, 8, 64)])
 def test_workspace_bytes_split(M, N, K, bits, gs):
     """The split workspace: activations + scales, then partial sums of whole
@@ -75,16 +75,16 @@ def test_workspace_bytes_split(M, N, K, bits, gs):
     ex = cider.cider_linear_workspace_bytes_ex(M, N, K, bits, gs)
     TM = 32 if M <= 32 else 64 if M <= 64 else 128
     tiles = -(-N // 64) * -(-M // TM)
-    unit = gs if gs else (128 if bits == 8 else 256)
-    fits = [S for S in range(2, 9) if S <= K // unit and
+    fits = [S for S in range(2, 9) if S <= K // gs and
             ex == base + _r256(tiles * S * 64 * TM * 4) + _r256(tiles * 4)]
     assert len(fits) == 1, (ex, base)
 
 
 def test_workspace_bytes_no_split():
-    # int8 per channel never splits; int4 per channel up to 64 tokens, per
-    # group up to 256
+    # per channel never splits; per group up to 256 tokens
     for M, N, K, bits, gs in [(64, 10240, 2560, 8, 0), (65, 10240, 2560, 4, 0),
+                              (16, 10240, 2560, 4, 0), (64, 10240, 2560, 4, 0),
+                              (9, 640, 2560, 4, 0),
                               (257, 2560, 10240, 8, 64), (4096, 10240, 2560, 8, 0),
                               (1, 10240, 2560, 8, 0), (8, 512, 4096, 8, 0),
                               (64, 512, 128, 4, 0), (0, 512, 1024, 8, 0)]:

@@ -493,17 +493,44 @@ def test_many_token_tiles(M, N, K, bits, out):
 @pytest.mark.parametrize("bits,gs", [(8, 128), (4, 128), (8, 64)])
 @pytest.mark.parametrize("M,N,K", [(4100, 2624, 1024), (3100, 640, 2048), (3100, 640, 1344)])
 def test_many_token_tiles_per_group(M, N, K, bits, gs, out):
-    """Per-group products above 3072 tokens.  Groups of 128 with K a multiple
-    of 128 take the persistent kernel (4100 x 2624: 297 output tiles of
-    320 x 128, ragged in M and N, so some workgroups take two; 3100 x 640:
-    fewer tiles than compute units); K = 1344 and groups of 64 take the other
-    kernel.  Sampled rows against the oracle, every output against the exact
-    product."""
+    """Per-group products with many tokens.  4100 x 2624: too many tiles for
+    one round even at 256 channels, so groups of 128 take the 320 x 128
+    persistent kernel (297 output tiles, ragged in M and N, so some
+    workgroups take two) and groups of 64 the other kernel; 3100 x 640: one
+    round of 64 x 128 persistent tiles (250 of them, ragged in M); K = 1344
+    (not a multiple of 128) takes the other kernel.  Sampled rows against the
+    oracle, every output against the exact product."""
     if K % gs:
         pytest.skip("K not a multiple of the group size")
     import torch
     orc = get_oracle()
     _, _, xq, st, wq, sw = _inputs(M, N, K, bits, gs, seed=M + N + K + gs)
+    d = [gu.to_dev(a) for a in (xq, st, wq, sw)]
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, M // 2, M - 2, M - 1],
+                                     np.random.default_rng(M + gs).integers(0, M, 8)]))
+    y_dtype = 0 if out == "f16" else 1
+    y = gu.empty((M, N), torch.int16)
+    cider.cider_gemm_ex(d[0], d[1], d[2], d[3], M, N, K, bits, gs, y_dtype, y)
+    got = gu.bits_to_host(y)
+    ref = orc.dequant_ex(orc.gemm_acc(xq[rows], wq, bits, gs), st[rows], sw, y_dtype)
+    gu.assert_out_close(got[rows], ref, y_dtype, "%s M=%d N=%d K=%d bits=%d gs=%d" % (out, M, N, K, bits, gs))
+    if out == "f16":
+        gu.assert_every_output(y.view(torch.float16), xq, st, wq if bits == 8 else gu.unpack_int4(wq), sw, gs,
+                               "M=%d N=%d K=%d bits=%d gs=%d" % (M, N, K, bits, gs))
+
+
+@pytest.mark.parametrize("out", ["f16", "bf16"])
+@pytest.mark.parametrize("bits,gs", MODES[1:3] + MODES[4:6], ids=MODE_IDS[1:3] + MODE_IDS[4:6])
+@pytest.mark.parametrize("M,N,K", [(1030, 1984, 1024), (1100, 3776, 1024), (2100, 3008, 1024)])
+def test_mid_token_tiles_per_group(M, N, K, bits, gs, out):
+    """Per-group persistent tiles of 128, 192 and 256 channels (on a
+    256-unit device: 1030 x 1984 needs 279 tiles of 64 channels and 144 of
+    128; 1100 x 3776 270 of 128 and 180 of 192; 2100 x 3008 272 of 192 and
+    204 of 256), ragged in M and N.  Sampled rows against the oracle, every
+    output against the exact product."""
+    import torch
+    orc = get_oracle()
+    _, _, xq, st, wq, sw = _inputs(M, N, K, bits, gs, seed=M + N + K + gs + bits)
     d = [gu.to_dev(a) for a in (xq, st, wq, sw)]
     rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, M // 2, M - 2, M - 1],
                                      np.random.default_rng(M + gs).integers(0, M, 8)]))

@@ -29,8 +29,8 @@ SHAPES = [(9, 640, 2560), (16, 512, 1024), (32, 192, 512), (37, 2560, 2560), (64
 
 
 def _splits(M, bits, gs):
-    """Where the library splits (int8 per channel never: measured slower)."""
-    return (gs != 0 and M <= 256) or (bits == 4 and gs == 0 and M <= 64)
+    """Where the library splits (per channel never: measured slower)."""
+    return gs != 0 and M <= 256
 
 
 @pytest.fixture(scope="module", autouse=True)

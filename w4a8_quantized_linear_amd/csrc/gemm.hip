@@ -593,15 +593,18 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
     if constexpr (SPLIT) {
         // Split reduction.  Partial sums live tile by tile, split by split,
         // each lane's 16-byte quarters of its (i, j) block 64 lanes apart.
-        // They are stored and loaded as relaxed device-scope atomics, which
-        // this GPU performs at the device-coherent level, past the XCD-private
-        // L2 caches; each split waits for its stores to complete before the
-        // barrier after which thread 0 counts the split in, and the last of a
-        // tile's splits to count in loads the others' partials only after
-        // that.  (A release / acquire fence pair per workgroup would write
-        // back and invalidate the whole L2 of its XCD instead -- measured at
-        // 3-4x the time of the unsplit product.)  The partials are added in
-        // split order, so the sum does not depend on which split was last.
+        // Each split stores its partials, waits for them to complete, meets
+        // the workgroup barrier, and thread 0 counts the split in with an
+        // agent-scope acquire-release read-modify-write: the release part
+        // publishes every wave's stores (ordered before it by the barrier)
+        // to the whole device, and in the last split to count in the
+        // acquire part, followed by the barrier, orders every wave's loads
+        // of the other splits' partials after their stores (the AMDGPU
+        // memory model, gfx942 / gfx950 code sequences: release = write back
+        // the XCD's L2 and wait, acquire = invalidate the caches).  The
+        // partials themselves are relaxed agent-scope atomics.  The
+        // partials are added in split order, so the sum does not depend on
+        // which split was last.
         static_assert(OUT != OUT_I32, "split products dequantize");
         constexpr int TILE = TM * TN;
         typedef unsigned long long u64;
@@ -634,7 +637,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
         __syncthreads();
         uint32_t *flag = reinterpret_cast<uint32_t *>(smem);  // the ring is idle now
         if (threadIdx.x == 0)
-            *flag = __hip_atomic_fetch_add(sp.cnt + pid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *flag = __hip_atomic_fetch_add(sp.cnt + pid, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         if (*flag != (uint32_t)(sp.splits - 1))
             return;
@@ -1203,8 +1206,8 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_wide_kernel(P
 
 // Persistent per-group product for many tokens (int8 or packed int4
 // weights, groups of 64 / 128 along K): the copy path of gemm_wide_kernel
-// (128-byte K tiles, two-stage ring, one workgroup per compute unit walking
-// output tiles, copies streaming across tiles) with the operands of the
+// (128-byte K tiles, one workgroup per compute unit walking output tiles,
+// copies streaming across tiles) with the operands of the
 // per-group gemm_kernel (tokens are operand A, so a lane's outputs belong to
 // one channel per 32-channel block and need one group scale each).  The
 // channel scales of a K tile's groups travel with it into the ring.
@@ -1216,8 +1219,16 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_wide_kernel(P
 // works on the previous one, instead of all blocks in one burst after the
 // group's last MFMA.  The last group of an output tile is scaled before its
 // epilogue.  Outputs leave as 2-byte range-checked buffer stores, consecutive
-// lanes along a token row.  Needs K % 128 == 0, K >= 256, fp16 / bf16 output.
-template <int TN, int TM, int WN, int WM, int BITS, int GS, int OUT>
+// lanes along a token row.
+//
+// The ring has STG stages of one K tile each; K tile kt + STG is copied into
+// the stage of K tile kt once every wave is done reading it, so STG - 1 K
+// tiles are in flight while one is computed.  Small output tiles (little
+// matrix work per K tile) need the deeper rings to cover the copy latency.
+// Every K tile issues its copies even when no K tile is left to fetch (a
+// repeat of the current one, never read), so the in-order copy counts stay
+// fixed.  Needs K % 128 == 0, K >= 128 * STG, fp16 / bf16 output.
+template <int TN, int TM, int WN, int WM, int BITS, int GS, int OUT, int STG>
 __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_kernel(ProductArgs args, int tiles_n,
                                                                                      int tiles_m, int group_m)
 {
@@ -1239,7 +1250,8 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
     constexpr int STORES = FN * 16;  // 2-byte output stores per wave per output tile
     constexpr int NSC = (TM + NW * 64 - 1) / (NW * 64);
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+    static_assert(STG >= 2, "at least double buffering");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STG * STAGE];
     __shared__ __attribute__((aligned(16))) float s_st[TM];
 
     const int64_t M = args.M, N = args.N, K = args.K;
@@ -1390,11 +1402,12 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
         return;
     int tn, tm;
     tile_coords(t, tiles_n, tiles_m, group_m, tn, tm);
-    int g = 0;  // K tiles consumed: K tile kt of the current output tile is in stage (g + kt) & 1
+    int cs = 0;  // the stage of the K tile being computed (K tile 0 of the first output tile: 0)
     load_tok_scales(scv, (int64_t)tm * TM);
-    copy_tile(0, (int64_t)tm * TM, (int64_t)tn * TN, 0);
-    copy_tile(1, (int64_t)tm * TM, (int64_t)tn * TN, 1);
-    wait_vmcnt<D>();  // K tile 0 has landed
+#pragma unroll
+    for (int j = 0; j < STG; ++j)
+        copy_tile(j, (int64_t)tm * TM, (int64_t)tn * TN, j);
+    wait_vmcnt<D * (STG - 1)>();  // K tile 0 has landed
     for (;;) {
         const int64_t n0 = (int64_t)tn * TN, m0 = (int64_t)tm * TM;
         const int tnext = t + (int)gridDim.x;
@@ -1410,7 +1423,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
         __builtin_amdgcn_s_barrier();  // K tile 0 of this output tile is in, in every wave's view
         __builtin_amdgcn_sched_barrier(0);
         Frags f0, f1;
-        load_frags(f0, g & 1, 0);
+        load_frags(f0, cs, 0);
         // scales of the group waiting to be scaled (read from the ring before
         // the barrier after which its stage may be refilled)
         float swp[FN];
@@ -1418,7 +1431,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
         for (int i = 0; i < FN; ++i)
             swp[i] = 0.f;
         for (int kt = 0; kt < KT; ++kt) {
-            const int cs = (g + kt) & 1, ns = cs ^ 1;
+            const int ns = cs + 1 == STG ? 0 : cs + 1;
             const bool last = kt == KT - 1;
             step(Flag<true>{}, f0, f1, true, cs, 1, swp, false, 0, 0, 0, 0);
             step(Flag<false>{}, f1, f0, true, cs, 2, swp, false, 0, 0, 0, 0);
@@ -1434,17 +1447,19 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
             load_scales_lds(swp, cs, GPT - 1);
             wait_lgkm0();
             if (!last)
-                wait_vmcnt<0>();  // K tile kt + 1 has landed
+                wait_vmcnt<D * (STG - 2)>();  // K tile kt + 1 has landed
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
             // refill stage cs with the next K tile not yet copied: K tile
-            // kt + 2 of this output tile, or K tile kt + 2 - KT of the next
-            const bool own = kt + 2 < KT;
+            // kt + STG of this output tile, or K tile kt + STG - KT of the
+            // next; past the last output tile, a repeat of K tile kt
+            const bool own = kt + STG < KT;
             const bool nxt_tile = !own && has_next;
-            step(Flag<false>{}, f1, f0, !last, ns, 0, swp, own || nxt_tile, cs,
-                 own ? m0 : (int64_t)tm2 * TM, own ? n0 : (int64_t)tn2 * TN, own ? kt + 2 : kt + 2 - KT);
+            step(Flag<false>{}, f1, f0, !last, ns, 0, swp, true, cs,
+                 nxt_tile ? (int64_t)tm2 * TM : m0, nxt_tile ? (int64_t)tn2 * TN : n0,
+                 own ? kt + STG : nxt_tile ? kt + STG - KT : kt);
+            cs = ns;
         }
-        g += KT;
         load_tok_scales(scn, (int64_t)tm2 * TM);  // after the next tile's first copies
         // the last group
 #pragma unroll
@@ -1497,9 +1512,10 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
 #pragma unroll
         for (int i = 0; i < NSC; ++i)
             scv[i] = scn[i];
-        // the next tile's K tile 0 is older than its K tile 1, the token scale
-        // loads and this tile's stores
-        wait_vmcnt<(D + NSC + STORES < 63 ? D + NSC + STORES : 63)>();
+        // the next tile's K tile 0 is older than its K tiles 1 .. STG - 1, the
+        // token scale loads and this tile's stores
+        constexpr int AFTER0 = D * (STG - 1) + NSC + STORES;
+        wait_vmcnt<(AFTER0 < 63 ? AFTER0 : 63)>();
     }
     wait_vmcnt<0>();
 }
@@ -1565,16 +1581,18 @@ hipError_t launch_wide(const ProductArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int TN, int TM, int WN, int WM, int BITS, int GS, int OUT>
+template <int TN, int TM, int WN, int WM, int BITS, int GS, int OUT, int STG>
 hipError_t launch_group_wide(const ProductArgs &a, hipStream_t stream)
 {
+    if (a.K % 128 != 0 || a.K < 128 * STG)  // whole K tiles, the ring filled by one output tile
+        return hipErrorInvalidValue;
     const int tiles_n = (int)((a.N + TN - 1) / TN);
     const int tiles_m = (int)((a.M + TM - 1) / TM);
     const int tiles = tiles_n * tiles_m;
     int grid = compute_units();
     if (grid > tiles)
         grid = tiles;
-    hipLaunchKernelGGL((gemm_group_wide_kernel<TN, TM, WN, WM, BITS, GS, OUT>), dim3(grid),
+    hipLaunchKernelGGL((gemm_group_wide_kernel<TN, TM, WN, WM, BITS, GS, OUT, STG>), dim3(grid),
                        dim3((TN / WN) * (TM / WM) * 64), 0, stream, a, tiles_n, tiles_m, 8);
     return hipGetLastError();
 }
@@ -1630,18 +1648,45 @@ hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
 }
 
 // Per group (operands swapped; a wave owns 32 tokens of WN channels).
+//
+// Past the few-token range, the persistent kernel with 128-token tiles: the
+// narrowest channel tile (64, 128, 192 or 256 channels, with a ring deep
+// enough to cover the copy latency of its little matrix work per K tile)
+// whose tiles all run at once, one per compute unit.  Measured time per
+// output tile at N = 2560, K = 10240 (one tile per compute unit, int8 gs64 /
+// gs128): 60 / 52, 88 / 81, 128 / 110 and 148 / 126 us for 64 to 256
+// channels; a second round of tiles costs a whole tile time again, so the
+// narrowest tile that needs one round wins (M = 512 and 768: 80.6 / 71.0 us
+// before, 60.5 / 52.5 after; M = 1024: 96.0 / 99.7 -> 88.4 / 81.4 us; M =
+// 2048: 141.2 / 138.4 -> 128.1 / 109.8 us; M = 3072: 180.6 / 164.3 ->
+// 148.0 / 125.9 us).  Past one round of 256-channel tiles: groups of 128
+// take the 320-channel persistent kernel (M = 4096: int8 176.7 -> 153.3 us,
+// int4 209.1 -> 199.9 us on one box); groups of 64 the 320 x 128 tiles of
+// gemm_kernel, which the persistent kernel did not beat there (187.2 ->
+// 187.6 us; int4 238 -> 249 us): there the scale-accumulate's two vector
+// operations per output and group bound both kernels.
 template <int BITS, int GS, int OUT>
 hipError_t launch_group(const ProductArgs &a, hipStream_t stream)
 {
-    // Groups of 128 above 3072 tokens: the persistent kernel (M = 4096, N =
-    // 2560, K = 10240: int8 176.7 -> 153.3 us, int4 209.1 -> 199.9 us on one
-    // box).  Groups of 64 it did not speed up (187.2 -> 187.6 us; int4 238 ->
-    // 249 us): there the scale-accumulate's two vector operations per output
-    // and group bound both kernels.  Below 3072 tokens its 320 x 128 tiles
-    // leave compute units idle.
-    if constexpr (OUT != OUT_I32 && GS == 128) {
-        if (a.M > 3072 && a.K % 128 == 0 && a.K >= 256 && 128 * a.N * 2 < (int64_t(1) << 31))
-            return launch_group_wide<320, 128, 160, 32, BITS, GS, OUT>(a, stream);
+    if constexpr (OUT != OUT_I32) {
+        // whole 128-byte K tiles; 128-token output tiles addressable with
+        // 32-bit offsets
+        if (a.K % 128 == 0 && 128 * a.N * 2 < (int64_t(1) << 31)) {
+            const int64_t cu = compute_units(), tiles_m = (a.M + 127) / 128;
+            auto one_round = [&](int64_t tn) { return (a.N + tn - 1) / tn * tiles_m <= cu; };
+            if (a.K >= 512) {  // the deepest ring below holds 4 K tiles
+                if (one_round(64))
+                    return launch_group_wide<64, 128, 64, 32, BITS, GS, OUT, 4>(a, stream);
+                if (one_round(128))
+                    return launch_group_wide<128, 128, 64, 32, BITS, GS, OUT, 3>(a, stream);
+                if (one_round(192))
+                    return launch_group_wide<192, 128, 64, 32, BITS, GS, OUT, 3>(a, stream);
+                if (one_round(256))
+                    return launch_group_wide<256, 128, 128, 32, BITS, GS, OUT, 3>(a, stream);
+            }
+            if (GS == 128 && a.M > 3072 && a.K >= 256)
+                return launch_group_wide<320, 128, 160, 32, BITS, GS, OUT, 2>(a, stream);
+        }
     }
     if (a.M <= 768)
         return launch_cfg<64, 128, 64, 32, 64, BITS, GS, OUT, 6>(a, stream);
@@ -1658,31 +1703,21 @@ hipError_t launch_group_bits(const ProductArgs &a, hipStream_t stream)
     return a.bits == 8 ? launch_group<8, GS, OUT>(a, stream) : launch_group<4, GS, OUT>(a, stream);
 }
 
-// Split-K tiles for few tokens: 64 channels x 32 / 64 / 128 tokens; per
-// channel with the deep K tiles of the unsplit few-token product, per group
-// with 64-deep tiles (whole groups per split).
+// Split-K tiles for few tokens (per group only): 64 channels x 32 / 64 / 128
+// tokens with 64-deep K tiles (whole groups per split).
 constexpr int kSplitTN = 64;
+constexpr int kSplitBK = 64;
 constexpr int split_tm(int64_t M) { return M <= 32 ? 32 : M <= 64 ? 64 : 128; }
-constexpr int split_bk(int bits, int group_size) { return group_size ? 64 : bits == 8 ? 128 : 256; }
 
 template <int BITS, int GS, int OUT>
 hipError_t launch_split_bits(const ProductArgs &a, const SplitPlan &p, void *part, uint32_t *cnt,
                              hipStream_t stream)
 {
-    if constexpr (GS == 0) {
-        constexpr int BKS = BITS == 8 ? 128 : 256, STS = BITS == 8 ? 4 : 3;
-        if (a.M <= 32)
-            return launch_split_cfg<kSplitTN, 32, 32, 32, BKS, BITS, 0, OUT, STS>(a, p, part, cnt, stream);
-        if (a.M <= 64)
-            return launch_split_cfg<kSplitTN, 64, 32, 64, BKS, BITS, 0, OUT, STS>(a, p, part, cnt, stream);
-        return launch_split_cfg<kSplitTN, 128, 32, 64, BKS, BITS, 0, OUT, STS>(a, p, part, cnt, stream);
-    } else {
-        if (a.M <= 32)
-            return launch_split_cfg<kSplitTN, 32, 64, 32, 64, BITS, GS, OUT, 6>(a, p, part, cnt, stream);
-        if (a.M <= 64)
-            return launch_split_cfg<kSplitTN, 64, 64, 32, 64, BITS, GS, OUT, 6>(a, p, part, cnt, stream);
-        return launch_split_cfg<kSplitTN, 128, 64, 32, 64, BITS, GS, OUT, 6>(a, p, part, cnt, stream);
-    }
+    if (a.M <= 32)
+        return launch_split_cfg<kSplitTN, 32, 64, 32, kSplitBK, BITS, GS, OUT, 6>(a, p, part, cnt, stream);
+    if (a.M <= 64)
+        return launch_split_cfg<kSplitTN, 64, 64, 32, kSplitBK, BITS, GS, OUT, 6>(a, p, part, cnt, stream);
+    return launch_split_cfg<kSplitTN, 128, 64, 32, kSplitBK, BITS, GS, OUT, 6>(a, p, part, cnt, stream);
 }
 
 template <int OUT>
@@ -1692,8 +1727,7 @@ hipError_t launch_split_kind(const ProductArgs &a, const SplitPlan &p, void *par
     const bool b8 = a.bits == 8;
     switch (a.group_size) {
     case 0:
-        return b8 ? launch_split_bits<8, 0, OUT>(a, p, part, cnt, stream)
-                  : launch_split_bits<4, 0, OUT>(a, p, part, cnt, stream);
+        return hipErrorInvalidValue;  // per-channel products are never split
     case 64:
         return b8 ? launch_split_bits<8, 64, OUT>(a, p, part, cnt, stream)
                   : launch_split_bits<4, 64, OUT>(a, p, part, cnt, stream);
@@ -1710,22 +1744,21 @@ hipError_t launch_split_kind(const ProductArgs &a, const SplitPlan &p, void *par
 //   * per group (up to 256 tokens): the unsplit few-token kernel takes
 //     35-70 us; split into about one workgroup per compute unit, the
 //     matrix-core tiles take 26-42 us;
-//   * int4 per channel (up to 64 tokens): about two workgroups per compute
-//     unit, 12-14% faster;
-//   * int8 per channel: never faster -- the deep-K tiles already stream the
-//     weights at the rate the split reaches, and the partial sums' round trip
-//     through memory costs more than the extra workgroups gain.
+//   * per channel (int8 and int4): never faster -- the deep-K tiles already
+//     stream the weights at the rate the split reaches, and the partial sums'
+//     round trip plus the acquire-release handoff (an L2 write-back per
+//     workgroup) cost more than the extra workgroups gain (int4, 16 / 32 / 64
+//     tokens: 20.6 / 21.6 / 24.7 us split, 15.0 / 15.2 / 17.0 us unsplit).
 SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int bits, int group_size)
 {
     SplitPlan p{1, 0, 0};
-    const int bk = split_bk(bits, group_size);
-    const int64_t max_m = group_size ? 256 : bits == 4 ? 64 : 0;
-    if (M < 1 || M > max_m || N < 1 || K < bk || K % bk != 0)
+    (void)bits;
+    if (group_size == 0 || M < 1 || M > 256 || N < 1 || K < group_size || K % group_size != 0)
         return p;
     const int TM = split_tm(M);
     const int64_t tiles = ((N + kSplitTN - 1) / kSplitTN) * ((M + TM - 1) / TM);
-    const int64_t units = K / bk / (group_size ? group_size / bk : 1);
-    const int64_t target = (group_size ? 1 : 2) * (int64_t)compute_units();
+    const int64_t units = K / group_size;
+    const int64_t target = compute_units();
     int64_t S = (target + tiles / 2) / tiles;  // nearest
     S = S < 8 ? S : 8;
     S = S < units ? S : units;
