@@ -850,6 +850,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_wide_kernel(P
     constexpr int XB = XBYTES / 1024, WB = WBYTES / 1024, TB = XB + WB;
     constexpr int D = (XB + NW - 1) / NW + (WB + NW - 1) / NW;  // copies per wave per K tile
     static_assert(XBYTES % 1024 == 0 && WBYTES % 1024 == 0, "tiles of whole 1 KB blocks");
+    static_assert(WN % 32 == 0 && WM % 32 == 0 && TN % WN == 0 && TM % WM == 0, "whole 32 x 32 blocks per wave");
     constexpr bool USUM = BITS == 4;  // unsigned int4 codes, corrected by the token sums
     // epilogue: each wave stages CB channel blocks of 32 tokens at a time in
     // its share of the idle stage (rows of 64 * CB bytes padded by 16)
@@ -1235,7 +1236,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
     constexpr int BK = 128;
     constexpr int NWN = TN / WN, NWM = TM / WM, NW = NWN * NWM;
     constexpr int FN = WN / 32;  // 32-channel blocks per wave
-    static_assert(WM == 32, "one 32-token block per wave");
+    static_assert(WM == 32 && WN % 32 == 0 && TN % WN == 0 && TM % WM == 0, "one 32-token block per wave");
     static_assert(OUT != OUT_I32, "the int32 hook takes gemm_kernel");
     constexpr int XROW = BK, WROW = BITS == 8 ? BK : BK / 2;
     constexpr int XBYTES = TM * XROW, WBYTES = TN * WROW;
@@ -1605,17 +1606,24 @@ int64_t rounds(int64_t M, int64_t N, int TM, int TN)
 }
 
 // Tile shape by M (measured on MI355X over the N=10240 / N=2560 operator
-// shapes).  M <= 128: 64 channels x 32 / 64 / 128 tokens with deep K tiles;
-// M <= 256: 64-channel x 128-token tiles with a deep copy ring
-// (latency-bound: more copies in flight).  Up to 1024 tokens: 160-channel
-// tiles (int8 above 512 tokens: 8 waves of 160 x 64 over 256 tokens, 10%
-// faster than 128 tokens at M = 768..1024).  Larger M: a big tile, chosen by
-// how many whole rounds of workgroups over the compute units it needs times
-// its measured time per tile: 320 x 256 (8 waves of 160 x 64), or 256 x 256
-// (8 waves of 128 x 64, about 0.8x the time per tile on HBM-cold operands).
-// int4 follows the same rule since its widening costs five VALU operations per
-// 8 codes (it used to favour a 4-wave 128 x 128 layout that widens each
-// weight fragment once for 4 token blocks).
+// shapes).  M <= 128: 64 channels x 32 / 64 / 128 tokens with deep K tiles.
+// Past that, with whole 128-byte K tiles (at least two) and outputs
+// addressable with 32-bit offsets, the persistent kernel with the smallest
+// output tile whose tiles all run at once, one per compute unit: 160 x 128
+// (4 waves of 160 x 32), 160 x 256 (4 waves of 160 x 64), else 320 x 256
+// (8 waves of 160 x 64) over several rounds.  A second round costs a whole
+// tile time again (at N = 10240, K = 2560, int8 / int4: 160 x 128 tiles take
+// 23.6-26.0 / 21.1-22.6 us for M = 192..512 in one round and 45.1 / 40.2 us
+// at M = 768 in two; 160 x 256: 33.7 / 32.9 us at M = 768; the earlier
+// 64 x 128 and 160 x 128 / 160 x 256 tiles of gemm_kernel with 64-byte K
+// tiles: 26.6-34.2 / 26.1-37.7 us over M = 192..768, 36.7 / 41.9 us at
+// M = 1024, where 160 x 256 takes 35.7 / 34.6 us).
+// Otherwise (K not a multiple of 128): 64 x 128 tiles with a deep copy ring
+// up to 256 tokens (latency-bound: more copies in flight), 160-channel tiles
+// up to 1024 (int8 above 512 tokens: 8 waves of 160 x 64 over 256 tokens),
+// then 320 x 256 or 256 x 256 by how many whole rounds of workgroups over the
+// compute units each needs times its measured time per tile (256 x 256 takes
+// about 0.8x the time per tile on HBM-cold operands).
 template <int BITS, int OUT>
 hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
 {
@@ -1631,16 +1639,21 @@ hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
             return launch_cfg<64, 64, 32, 64, BKS, BITS, 0, OUT, STS>(a, stream);
         return launch_cfg<64, 128, 32, 64, BKS, BITS, 0, OUT, STS>(a, stream);
     }
+    if (a.K % 128 == 0 && a.K >= 256 && 256 * a.N * 4 < (int64_t(1) << 31)) {
+        const int64_t cu = compute_units();
+        auto one_round = [&](int64_t tn, int64_t tm) { return (a.N + tn - 1) / tn * ((a.M + tm - 1) / tm) <= cu; };
+        if (one_round(160, 128))
+            return launch_wide<160, 128, 160, 32, BITS, OUT>(a, stream);
+        if (one_round(160, 256))
+            return launch_wide<160, 256, 160, 64, BITS, OUT>(a, stream);
+        return launch_wide<320, 256, 160, 64, BITS, OUT>(a, stream);
+    }
     if (a.M <= 256)
         return launch_cfg<64, 128, 32, 64, 64, BITS, 0, OUT, 8>(a, stream);
     if (BITS == 8 && a.M > 512 && a.M <= 1024)
         return launch_cfg<160, 256, 160, 64, 64, BITS, 0, OUT, 4>(a, stream);
     if (a.M <= 1024)
         return launch_cfg<160, 128, 160, 32, 64, BITS, 0, OUT, 4>(a, stream);
-    // whole 128-byte K tiles, at least two of them, and a 256-row output
-    // tile addressable with 32-bit offsets: the persistent kernel
-    if (a.K % 128 == 0 && a.K >= 256 && 256 * a.N * 4 < (int64_t(1) << 31))
-        return launch_wide<320, 256, 160, 64, BITS, OUT>(a, stream);
     const int64_t r320 = rounds(a.M, a.N, 256, 320), r256 = rounds(a.M, a.N, 256, 256);
     if (100 * r320 <= 80 * r256)
         return launch_cfg<320, 256, 160, 64, 64, BITS, 0, OUT, 4>(a, stream);
