@@ -456,18 +456,20 @@ def test_product_f16_tolerance(M, N, K, bits, gs, path):
 @pytest.mark.parametrize("out", ["i32", "f16", "bf16"])
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("M,N,K", [(2100, 10304, 1024), (1100, 640, 256), (1030, 576, 1344),
-                                   (1100, 320, 128), (4100, 704, 2560), (1100, 5056, 1024)])
+                                   (1100, 320, 128), (4100, 704, 2560), (1100, 5056, 1024),
+                                   (1100, 10176, 512), (2040, 10176, 256)])
 def test_many_token_tiles(M, N, K, bits, out):
     """Per-channel persistent tiles.  With K a multiple of 128 and at least
-    256, one workgroup per compute unit walks output tiles: 2100 x 10304
-    needs more than one round even of 320 x 256 tiles (297, so some
-    workgroups take two; ragged in M and N); on a 256-unit device 1100 x 5056
-    fits one round of 160 x 256 tiles (160) but not of 160 x 128 (288); 1100
-    x 640 and 4100 x 704 fit one round of 160 x 128 tiles (36 and 165, ragged
-    N).  K = 1344 (not a multiple of 128) and K = 128 (one K tile) take the
-    other kernel.  int32 sums bit-exact and outputs within tolerance on
-    sampled rows against the oracle, every output against the exact
-    product."""
+    256, one workgroup per compute unit walks output tiles.  On a 256-unit
+    device: 2100 x 10304 takes two rounds of 256 x 256 tiles (369, so some
+    workgroups take two; ragged in M and N); 1100 x 10176 one round of
+    256 x 256 (200); 2040 x 10176 one round of 320 x 256 (256), where
+    256 x 256 would need two; 1100 x 5056 one round of 160 x 256 (160) but
+    not of 160 x 128 (288); 1100 x 640 and 4100 x 704 one round of 160 x 128
+    (36 and 165, ragged N).  K = 1344 (not a multiple of 128) and K = 128
+    (one K tile) take the other kernel.  int32 sums bit-exact and outputs
+    within tolerance on sampled rows against the oracle, every output
+    against the exact product."""
     import torch
     orc = get_oracle()
     _, _, xq, st, wq, sw = _inputs(M, N, K, bits, 0, seed=M + N + K)

@@ -1610,8 +1610,12 @@ int64_t rounds(int64_t M, int64_t N, int TM, int TN)
 // Past that, with whole 128-byte K tiles (at least two) and outputs
 // addressable with 32-bit offsets, the persistent kernel with the smallest
 // output tile whose tiles all run at once, one per compute unit: 160 x 128
-// (4 waves of 160 x 32), 160 x 256 (4 waves of 160 x 64), else 320 x 256
-// (8 waves of 160 x 64) over several rounds.  A second round costs a whole
+// (4 waves of 160 x 32), 160 x 256 (4 waves of 160 x 64), else 256 x 256
+// (8 waves of 128 x 64) or 320 x 256 (8 waves of 160 x 64) over several
+// rounds, by rounds times time per tile (M = 1280 / 1536 / 2560 / 3072, int8:
+// 256 x 256 45.0 -> 41.2, 46.3 -> 44.3, 85.0 -> 74.2, 89.6 -> 79.9 us; at
+// M = 2048, 3584, 4096 and 6144 it needs one more round than 320 x 256 and
+// loses, 53.5 -> 73.6 us at 2048).  A second round costs a whole
 // tile time again (at N = 10240, K = 2560, int8 / int4: 160 x 128 tiles take
 // 23.6-26.0 / 21.1-22.6 us for M = 192..512 in one round and 45.1 / 40.2 us
 // at M = 768 in two; 160 x 256: 33.7 / 32.9 us at M = 768; the earlier
@@ -1650,6 +1654,10 @@ hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
             return launch_wide<160, 128, 160, 32, BITS, OUT>(a, stream);
         if (one_round(160, 256))
             return launch_wide<160, 256, 160, 64, BITS, OUT>(a, stream);
+        // several rounds: 256 x 256 tiles take about 0.88x the time of
+        // 320 x 256 ones, so they win unless they need more rounds
+        if (88 * rounds(a.M, a.N, 256, 256) < 100 * rounds(a.M, a.N, 256, 320))
+            return launch_wide<256, 256, 128, 64, BITS, OUT>(a, stream);
         return launch_wide<320, 256, 160, 64, BITS, OUT>(a, stream);
     }
     if (a.M <= 256)
