@@ -221,7 +221,7 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_n, int tiles_m, i
 // that a lane's outputs all belong to one channel per 32-channel block and
 // need one group scale each; the int32 sum of each group is scaled into an
 // fp32 accumulator as soon as the group's last K tile is multiplied.
-// SPLIT: workgroup blockIdx.x computes split z = blockIdx.x / tiles of tile
+// SPLIT (per group only): workgroup blockIdx.x computes split z = blockIdx.x / tiles of tile
 // blockIdx.x % tiles (the splits of a tile share its XCD), over its share
 // of the K tiles, then takes part in the split reduction.
 template <int TN, int TM, int WN, int WM, int BK, int BITS, int GS, int OUT, int STAGES, bool SPLIT = false>
@@ -605,7 +605,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
         // partials themselves are relaxed agent-scope atomics.  The
         // partials are added in split order, so the sum does not depend on
         // which split was last.
-        static_assert(OUT != OUT_I32, "split products dequantize");
+        static_assert(SCALED, "split products are per group and dequantize");
         constexpr int TILE = TM * TN;
         typedef unsigned long long u64;
         uint32_t *mine = static_cast<uint32_t *>(sp.part) + (int64_t)pid * sp.splits * TILE +
@@ -614,11 +614,8 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
             return reinterpret_cast<u64 *>(mine + (int64_t)zz * TILE + ((i * FM + j) * 4 + q) * 256);
         };
         auto quarter = [&](int i, int j, int q) -> i32x4 {
-            if constexpr (SCALED)
-                return i32x4{__float_as_int(facc[i][j][4 * q]), __float_as_int(facc[i][j][4 * q + 1]),
-                             __float_as_int(facc[i][j][4 * q + 2]), __float_as_int(facc[i][j][4 * q + 3])};
-            else
-                return i32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            return i32x4{__float_as_int(facc[i][j][4 * q]), __float_as_int(facc[i][j][4 * q + 1]),
+                         __float_as_int(facc[i][j][4 * q + 2]), __float_as_int(facc[i][j][4 * q + 3])};
         };
 #pragma unroll
         for (int i = 0; i < FN; ++i)
@@ -669,13 +666,8 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
                     for (int q = 0; q < 4; ++q)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            if constexpr (SCALED) {
-                                const float f = __int_as_float(v[i][j][q][e]);
-                                facc[i][j][4 * q + e] = first_split ? f : facc[i][j][4 * q + e] + f;
-                            } else {
-                                const int t = v[i][j][q][e];
-                                acc[i][j][4 * q + e] = first_split ? t : acc[i][j][4 * q + e] + t;
-                            }
+                            const float f = __int_as_float(v[i][j][q][e]);
+                            facc[i][j][4 * q + e] = first_split ? f : facc[i][j][4 * q + e] + f;
                         }
         };
         const int S = sp.splits;
