@@ -426,8 +426,16 @@ def dtype_variants_bench(torch, cider, si, steps=50):
         def call(i):
             cider.cider_linear_ex(xs[x_dt][i % B], x_dt, M, K, K, sm if smooth else None, wq, sw,
                                   N, 8, 0, y_dt, ws, ws_bytes, ys[i % B])
-        for i in range(5):
+        # the same time-based warm-up as the headline: the first variant
+        # would otherwise run on clocks still ramping up
+        t0 = time.perf_counter()
+        i = 0
+        while i < 5 or time.perf_counter() - t0 < WARMUP_MIN_S:
             call(i)
+            i += 1
+            if i % 32 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(steps):
