@@ -526,13 +526,17 @@ def test_many_token_tiles_per_group(M, N, K, bits, gs, out):
 
 @pytest.mark.parametrize("out", ["f16", "bf16"])
 @pytest.mark.parametrize("bits,gs", MODES[1:3] + MODES[4:6], ids=MODE_IDS[1:3] + MODE_IDS[4:6])
-@pytest.mark.parametrize("M,N,K", [(1030, 1984, 1024), (1100, 3776, 1024), (2100, 3008, 1024)])
+@pytest.mark.parametrize("M,N,K", [(1030, 1984, 1024), (1300, 2496, 1024), (1100, 3776, 1024),
+                                   (2100, 3008, 1024)])
 def test_mid_token_tiles_per_group(M, N, K, bits, gs, out):
-    """Per-group persistent tiles of 128, 192 and 256 channels (on a
-    256-unit device: 1030 x 1984 needs 279 tiles of 64 channels and 144 of
-    128; 1100 x 3776 270 of 128 and 180 of 192; 2100 x 3008 272 of 192 and
-    204 of 256), ragged in M and N.  Sampled rows against the oracle, every
-    output against the exact product."""
+    """Per-group persistent tiles with more than one channel block per wave
+    row, ragged in M and N.  On a 256-unit device: 1030 x 1984 takes one
+    round of 128 x 96 tiles (176; 64 x 128 would need 279); 1300 x 2496 of
+    128 x 128 (220; 128 x 96 would need 280); 1100 x 3776 of 192 x 128 (180;
+    128 x 128 would need 270); 2100 x 3008 of 256 x 128 (204; 192 x 128
+    would need 272).  (The 64-channel tiles are reached by the product tests'
+    shapes.)  Sampled rows against the oracle, every output against the
+    exact product."""
     import torch
     orc = get_oracle()
     _, _, xq, st, wq, sw = _inputs(M, N, K, bits, gs, seed=M + N + K + gs + bits)

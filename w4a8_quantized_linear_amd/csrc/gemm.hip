@@ -1666,10 +1666,14 @@ hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
 
 // Per group (operands swapped; a wave owns 32 tokens of WN channels).
 //
-// Past the few-token range, the persistent kernel with 128-token tiles: the
-// narrowest channel tile (64, 128, 192 or 256 channels, with a ring deep
-// enough to cover the copy latency of its little matrix work per K tile)
-// whose tiles all run at once, one per compute unit.  Measured time per
+// Past the few-token range, the persistent kernel: of the tiles whose
+// output tiles all run at once, one per compute unit, the one with the
+// fewest rows per K tile (64 x 96, 64 x 128, 128 x 96, 128 x 128, 192 x 128,
+// 256 x 128 channels x tokens, each with a ring deep enough to cover the copy
+// latency of its little matrix work per K tile).  96-token tiles: M = 1024
+// int8 gs64 / gs128 88.3 / 81.2 -> 79.7 / 74.7 us (128 x 96 against
+// 128 x 128); M = 300..512 gs128 50.0-52.2 -> 47.2-47.6 us (64 x 96 against
+// 64 x 128), gs64 unchanged.  Measured time per
 // output tile at N = 2560, K = 10240 (one tile per compute unit, int8 gs64 /
 // gs128): 60 / 52, 88 / 81, 128 / 110 and 148 / 126 us for 64 to 256
 // channels; a second round of tiles costs a whole tile time again, so the
@@ -1691,9 +1695,15 @@ hipError_t launch_group(const ProductArgs &a, hipStream_t stream)
         if (a.K % 128 == 0 && 128 * a.N * 2 < (int64_t(1) << 31)) {
             const int64_t cu = compute_units(), tiles_m = (a.M + 127) / 128;
             auto one_round = [&](int64_t tn) { return (a.N + tn - 1) / tn * tiles_m <= cu; };
+            auto one_round96 = [&](int64_t tn) { return (a.N + tn - 1) / tn * ((a.M + 95) / 96) <= cu; };
             if (a.K >= 512) {  // the deepest ring below holds 4 K tiles
+                // candidates in order of rows per K tile (TN + TM)
+                if (one_round96(64))
+                    return launch_group_wide<64, 96, 64, 32, BITS, GS, OUT, 4>(a, stream);
                 if (one_round(64))
                     return launch_group_wide<64, 128, 64, 32, BITS, GS, OUT, 4>(a, stream);
+                if (one_round96(128))
+                    return launch_group_wide<128, 96, 64, 32, BITS, GS, OUT, 3>(a, stream);
                 if (one_round(128))
                     return launch_group_wide<128, 128, 64, 32, BITS, GS, OUT, 3>(a, stream);
                 if (one_round(192))
