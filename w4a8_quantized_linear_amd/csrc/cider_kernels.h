@@ -37,20 +37,16 @@ hipError_t launch_smooth_fold(const uint16_t *w, int dtype, int64_t N, int64_t K
 // accumulators (test hook).
 enum OutKind { OUT_F16 = 0, OUT_I32 = 1, OUT_BF16 = 2 };
 
-// Bit pattern of an fp32 result rounded to the output type, to nearest even
-// (fp16: the hardware conversion; bf16: the upper half of the fp32 pattern
-// after adding half an ulp, ties to even; NaN stays a quiet NaN).
+// Bit pattern of an fp32 result rounded to the output type, to nearest even,
+// by the hardware conversion of each type (gfx950 converts to bf16 in one
+// instruction; NaN stays a quiet NaN).
 template <int OUT>
 __device__ __forceinline__ uint16_t out_bits(float y)
 {
-    if constexpr (OUT == OUT_BF16) {
-        const uint32_t u = __builtin_bit_cast(uint32_t, y);
-        if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-            return (uint16_t)((u >> 16) | 0x40u);
-        return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-    } else {
+    if constexpr (OUT == OUT_BF16)
+        return __builtin_bit_cast(uint16_t, (__bf16)y);
+    else
         return __builtin_bit_cast(uint16_t, (_Float16)y);
-    }
 }
 
 struct ProductArgs {

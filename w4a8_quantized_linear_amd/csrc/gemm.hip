@@ -216,6 +216,22 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_n, int tiles_m, i
     tn = r / gsize;
 }
 
+// Two outputs packed into one dword (first in the low half) by the packed
+// hardware conversion of the output type (round to nearest even, as the
+// scalar one in out_bits).
+template <int OUT>
+__device__ __forceinline__ uint32_t pack2(float a, float b)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    if constexpr (OUT == OUT_F16) {
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
+    } else {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+    }
+}
+
 // GS = 0: one scale per channel.  GS = 64 / 128: per-group scaling.  The
 // operands then swap roles -- tokens are operand A, weights operand B -- so
 // that a lane's outputs all belong to one channel per 32-channel block and
@@ -759,8 +775,8 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
                     for (int e = 0; e < 4; ++e)
                         y[e] = (float)acc[i][j][4 * q + e] * st * sw[e];
                     uint2 packed;
-                    packed.x = (uint32_t)out_bits<OUT>(y[0]) | ((uint32_t)out_bits<OUT>(y[1]) << 16);
-                    packed.y = (uint32_t)out_bits<OUT>(y[2]) | ((uint32_t)out_bits<OUT>(y[3]) << 16);
+                    packed.x = pack2<OUT>(y[0], y[1]);
+                    packed.y = pack2<OUT>(y[2], y[3]);
                     *reinterpret_cast<uint2 *>(ob + frow * ROWB + c * 2) = packed;
                 }
             constexpr int CHUNKS = 32 * CPRO;
@@ -804,20 +820,6 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_kernel(
 //     number of memory instructions and the in-order vmcnt waits count
 //     exactly.
 // Needs K % 128 == 0 and K >= 256 (two K tiles).
-// Two outputs packed into one dword (first in the low half): fp16 through
-// the packed conversion (round to nearest even, as the scalar one), bf16 by
-// out_bits.
-template <int OUT>
-__device__ __forceinline__ uint32_t pack2(float a, float b)
-{
-    if constexpr (OUT == OUT_F16) {
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
-    } else {
-        return (uint32_t)out_bits<OUT>(a) | ((uint32_t)out_bits<OUT>(b) << 16);
-    }
-}
 
 // Channel blocks (of 32) per staging pass: the largest power of two up to
 // fn whose 32 rows (cb * 64 bytes + 16 of padding each) fit in wreg bytes.
