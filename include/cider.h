@@ -212,10 +212,14 @@ size_t cider_linear_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int bits
 /* The whole layer on fp16 activations, mirroring perchannel_linear(x, w, s)
    and w4a8_linear(x, packed, s) of Cider README "Low-Level API":
    quantize_act into `workspace`, then the product.  On the matrix-vector path
-   (M * K <= 65536 and M <= 8, or M <= 4 for int4 weights, under the automatic
-   path setting) the quantization is fused into the matrix-vector kernel and
-   the workspace is not touched (it may be null).  x: fp16 [M, K] row stride
-   ldx; y: fp16 [M, N]. */
+   the quantization is fused into the matrix-vector kernel and the workspace
+   is not touched (it may be null).  Under the automatic path setting that
+   path takes M * K <= 65536 with M <= 3 per channel or M <= 2 per group
+   where the few-token matrix-core kernel applies (K a multiple of 128 for
+   int8 weights, 256 for int4), else M <= 8 (M <= 4 for int4 weights); calls
+   within M <= 8 (int4: 4) and M * K <= 65536 given no workspace, or less
+   than cider_linear_workspace_bytes(M, K), also take it.  x: fp16 [M, K]
+   row stride ldx; y: fp16 [M, N]. */
 cider_status cider_w8a8_linear(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
                                const int8_t *wq, const float *s_w, int64_t N, int group_size,
                                void *workspace, size_t workspace_bytes, void *y_f16,

@@ -64,9 +64,10 @@ def _r256(v):
     return (v + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("M,N,K,bits,gs", [(64, 2560, 10240, 8, 64), (16, 2560, 10240, 4, 64),
-                                           (128, 64, 10240, 8, 128), (9, 640, 2560, 4, 128),
-                                           (100, 320, 1024, 8, 64), (256, 2560, 10240, 8, 64)])
+@pytest.mark.parametrize("M,N,K,bits,gs", [(64, 2560, 10240, 8, 64), (48, 2560, 10240, 4, 64),
+                                           (128, 64, 10240, 8, 128), (40, 640, 2560, 4, 128),
+                                           (100, 320, 1024, 8, 64), (256, 2560, 10240, 8, 64),
+                                           (16, 640, 320, 8, 64), (32, 256, 640, 4, 64)])
 def test_workspace_bytes_split(M, N, K, bits, gs):
     """The split workspace: activations + scales, then partial sums of whole
     64 x TM tiles (TM = 32 / 64 / 128 by token count) for 2..8 splits (no
@@ -81,8 +82,12 @@ def test_workspace_bytes_split(M, N, K, bits, gs):
 
 
 def test_workspace_bytes_no_split():
-    # per channel never splits; per group up to 256 tokens
-    for M, N, K, bits, gs in [(64, 10240, 2560, 8, 0), (65, 10240, 2560, 4, 0),
+    # per channel never splits; per group from 33 to 256 tokens, and up to 32
+    # only where K is not a multiple of the few-token kernel's unit (128
+    # values int8, 256 int4)
+    for M, N, K, bits, gs in [(16, 2560, 10240, 4, 64), (9, 640, 2560, 4, 128), (32, 2560, 10240, 8, 64),
+                              (1, 2560, 10240, 8, 128),
+                              (64, 10240, 2560, 8, 0), (65, 10240, 2560, 4, 0),
                               (16, 10240, 2560, 4, 0), (64, 10240, 2560, 4, 0),
                               (9, 640, 2560, 4, 0),
                               (257, 2560, 10240, 8, 64), (4096, 10240, 2560, 8, 0),

@@ -454,6 +454,35 @@ def test_product_f16_tolerance(M, N, K, bits, gs, path):
 
 
 @pytest.mark.parametrize("out", ["i32", "f16", "bf16"])
+@pytest.mark.parametrize("bits,gs", MODES, ids=MODE_IDS)
+@pytest.mark.parametrize("M,N,K", [(16, 8256, 512), (32, 10240, 2560), (24, 8192, 256),
+                                   (9, 192, 1024), (32, 2560, 10240), (31, 64, 768), (5, 128, 256)])
+def test_few_token_kernel(M, N, K, bits, gs, out):
+    """The few-token product (up to 32 tokens, ragged in M): 64-channel tiles
+    from N = 8192, 16-channel tiles below, one or two 16-token blocks, one to
+    twenty K units per K-split wavefront, int8 / int4 weights, per channel and
+    per group; int32 sums bit-exact (the per-group int32 hook takes another
+    kernel), fp16 / bf16 outputs within tolerance of the oracle."""
+    if gs and K % gs:
+        pytest.skip("K not a multiple of the group size")
+    import torch
+    cider.cider_set_path(cider.PATH_GEMM)
+    orc = get_oracle()
+    _, _, xq, st, wq, sw = _inputs(M, N, K, bits, gs, seed=M * 11 + N)
+    acc = orc.gemm_acc(xq, wq, bits, gs)
+    what = "M=%d N=%d K=%d bits=%d gs=%d %s" % (M, N, K, bits, gs, out)
+    if out == "i32":
+        got = gu.gemm_i32_gpu(gu.to_dev(xq), gu.to_dev(wq), M, N, K, bits, gs)
+        assert np.array_equal(gu.to_host(got), acc), what
+        return
+    dt = 0 if out == "f16" else 1
+    y = gu.empty((M, N), torch.int16)
+    cider.cider_gemm_ex(gu.to_dev(xq), gu.to_dev(st), gu.to_dev(wq), gu.to_dev(sw), M, N, K, bits,
+                        gs, dt, y)
+    gu.assert_out_close(gu.bits_to_host(y), orc.dequant_ex(acc, st, sw, dt), dt, what)
+
+
+@pytest.mark.parametrize("out", ["i32", "f16", "bf16"])
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("M,N,K", [(2100, 10304, 1024), (1100, 640, 256), (1030, 576, 1344),
                                    (1100, 320, 128), (4100, 704, 2560), (1100, 5056, 1024),
@@ -592,6 +621,37 @@ def test_linear_whole_path(M, N, K, ldx, bits, gs):
     y = gu.linear_gpu(gu.to_dev(x), M, K, ldx, gu.to_dev(wq), gu.to_dev(sw), N, bits, gs)
     ref, _, _ = orc.linear(x, wq, sw, bits, gs, K=K)
     gu.assert_f16_close(gu.to_host(y), ref, "linear M=%d" % M)
+
+
+@pytest.mark.parametrize("bits,gs", MODES, ids=MODE_IDS)
+@pytest.mark.parametrize("M,N,K", [(2, 10240, 2560), (3, 2560, 10240), (4, 10240, 2560),
+                                   (6, 2560, 10240), (8, 10240, 2560)])
+def test_linear_few_tokens_auto(M, N, K, bits, gs):
+    """The automatic path at 2..8 tokens: given the workspace, the few-token
+    matrix-core kernel from 4 tokens per channel / 3 per group (the
+    matrix-vector kernel below); given none, the matrix-vector kernel with the
+    tokens quantized inside it wherever M * K <= 65536 (int4: M <= 4), and a
+    workspace error past that.  Both against the oracle's whole layer."""
+    if gs and K % gs:
+        pytest.skip("K not a multiple of the group size")
+    import torch
+    cider.cider_set_path(cider.PATH_AUTO)
+    orc = get_oracle()
+    x = si.activations(M, K, seed=M + K)
+    w = si.weights(N, K, seed=N)
+    wq, sw = orc.quantize_weight(w, bits, gs)
+    ref, _, _ = orc.linear(x, wq, sw, bits, gs, K=K)
+    xd, wqd, swd = gu.to_dev(x), gu.to_dev(wq), gu.to_dev(sw)
+    y = gu.linear_gpu(xd, M, K, K, wqd, swd, N, bits, gs)
+    gu.assert_f16_close(gu.to_host(y), ref, "linear M=%d with workspace" % M)
+    f = cider.cider_w8a8_linear if bits == 8 else cider.cider_w4a8_linear
+    y0 = gu.empty((M, N), torch.float16)
+    st = f(xd, M, K, K, wqd, swd, N, gs, None, 0, y0, check=False)
+    if M * K <= 65536 and M <= (4 if bits == 4 else 8):
+        assert st == cider.CIDER_OK
+        gu.assert_f16_close(gu.to_host(y0), ref, "linear M=%d without workspace" % M)
+    else:
+        assert st == cider.CIDER_ERR_WORKSPACE
 
 
 def test_deterministic_repeats():

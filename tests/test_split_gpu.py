@@ -21,16 +21,21 @@ pytestmark = pytest.mark.gpu
 
 MODES = [(8, 0), (8, 64), (8, 128), (4, 0), (4, 64), (4, 128)]
 MODE_IDS = ["w8a8_pc", "w8a8_pg64", "w8a8_pg128", "w4a8_pc", "w4a8_pg64", "w4a8_pg128"]
-# token counts on both sides of the 32 / 64 / 128-token tiles, ragged in M;
-# K from one split unit per split up to long rows
-SHAPES = [(9, 640, 2560), (16, 512, 1024), (32, 192, 512), (37, 2560, 2560), (64, 1024, 4096),
-          (100, 320, 1024), (128, 2560, 2560), (128, 64, 10240), (200, 320, 1024),
-          (256, 640, 2048)]
+# token counts on both sides of the 64 / 128-token tiles, ragged in M; up to
+# 32 tokens the few-token kernel takes the call unsplit (K = 320 / 192: K not
+# a multiple of its 128-value unit, so those split); K from one split unit
+# per split up to long rows
+SHAPES = [(9, 640, 2560), (16, 512, 1024), (32, 192, 512), (20, 256, 320), (30, 128, 192),
+          (37, 2560, 2560), (64, 1024, 4096), (100, 320, 1024), (128, 2560, 2560),
+          (128, 64, 10240), (200, 320, 1024), (256, 640, 2048)]
 
 
-def _splits(M, bits, gs):
-    """Where the library splits (per channel never: measured slower)."""
-    return gs != 0 and M <= 256
+def _splits(M, K, bits, gs):
+    """Where the library splits: per group from 33 to 256 tokens, and up to 32
+    where the few-token kernel does not take the shape (K not a multiple of
+    128 int8 / 256 int4 values); per channel never (measured slower)."""
+    few = M <= 32 and K % (128 if bits == 8 else 256) == 0
+    return gs != 0 and M <= 256 and not few
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -72,7 +77,7 @@ def test_split_linear(M, N, K, bits, gs, y_dtype):
     orc = get_oracle()
     base = cider.cider_linear_workspace_bytes(M, K)
     ex = cider.cider_linear_workspace_bytes_ex(M, N, K, bits, gs)
-    assert (ex > base) == _splits(M, bits, gs)
+    assert (ex > base) == _splits(M, K, bits, gs)
     x = si.activations(M, K, seed=M + K)
     xb = x.view(np.uint16)
     w = si.weights(N, K, seed=N)
@@ -114,8 +119,9 @@ def test_split_consecutive_calls_share_workspace(bits, gs):
 
 
 def test_split_not_used_past_its_range_or_for_one_token():
-    """Shapes the split does not serve need no extra workspace."""
-    for M, bits, gs in ((257, 8, 64), (65, 4, 0), (16, 8, 0), (1, 8, 64)):
+    """Shapes the split does not serve (per channel, past 256 tokens, and the
+    few-token kernel's shapes up to 32) need no extra workspace."""
+    for M, bits, gs in ((257, 8, 64), (65, 4, 0), (16, 8, 0), (1, 8, 64), (32, 8, 64), (9, 4, 128)):
         assert cider.cider_linear_workspace_bytes_ex(M, 2560, 2560, bits, gs) == \
             cider.cider_linear_workspace_bytes(M, 2560)
 

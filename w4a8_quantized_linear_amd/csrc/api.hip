@@ -131,17 +131,29 @@ cider_status check_shape(int64_t M, int64_t N, int64_t K, int bits, int group_si
 enum Path { PATH_AUTO = 0, PATH_GEMV = 1, PATH_GEMM = 2 };
 
 // Which kernel serves M tokens of K features; CIDER_ERR_UNSUPPORTED_SHAPE
-// when the matrix-vector kernel is forced outside its range.  Automatic:
-// the matrix-vector kernel (one pass over the weights, each token's dot
-// products on the vector ALUs) up to 8 int8-weight tokens or 4 int4-weight
-// tokens (whose nibble handling costs more per token), where it measured
-// faster than the matrix-core products on the operator shapes (N=10240
-// K=2560 and N=2560 K=10240, every mode).
-cider_status pick_path(int64_t M, int64_t K, int bits, int *path)
+// when the matrix-vector kernel is forced outside its range.  Automatic: the
+// matrix-vector kernel (one pass over the weights, each token's dot products
+// on the vector ALUs) where it measured faster than the matrix-core products
+// on the operator shapes (N=10240 K=2560 and N=2560 K=10240, every mode,
+// whole layer): where the few-token matrix-core kernel takes the product, up
+// to 3 tokens per channel and 2 per group (per channel int8, M = 3 / 4:
+// 8.9 / 10.8 us against 10.2 / 10.1; per group int8 gs64, M = 2 / 3: 11.3 /
+// 15.6 against 15.0 / 15.1); elsewhere up to 8 int8-weight or 4 int4-weight
+// tokens.
+cider_status pick_path(int64_t M, int64_t N, int64_t K, int bits, int group_size, cider::OutKind kind,
+                       int *path)
 {
     const int forced = g_path.load(std::memory_order_relaxed);
     const bool gemv_ok = M <= 8 && M * K <= kGemvMaxBytes;
-    const bool gemv_auto = gemv_ok && M <= (bits == 4 ? 4 : 8);
+    cider::ProductArgs fa{};
+    fa.M = M;
+    fa.N = N;
+    fa.K = K;
+    fa.bits = bits;
+    fa.group_size = group_size;
+    fa.out_kind = kind;
+    const int64_t gemv_max = cider::few_supported(fa) ? (group_size ? 2 : 3) : (bits == 4 ? 4 : 8);
+    const bool gemv_auto = gemv_ok && M <= gemv_max;
     if (forced == PATH_GEMV) {
         if (!gemv_ok)
             return CIDER_ERR_UNSUPPORTED_SHAPE;
@@ -169,7 +181,7 @@ cider_status run_product(const int8_t *xq, const float *s_tok, const void *wq, c
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(out) || (scaled && !aligned16(s_w)))
         return CIDER_ERR_MISALIGNED;
     int path = PATH_GEMM;
-    st = pick_path(M, K, bits, &path);
+    st = pick_path(M, N, K, bits, group_size, kind, &path);
     if (st != CIDER_OK)
         return st;
     if (!device_usable())
@@ -217,9 +229,16 @@ cider_status run_linear(const void *x, int x_dtype, int64_t M, int64_t K, int64_
         (smooth && !aligned16(smooth)))
         return CIDER_ERR_MISALIGNED;
     int path = PATH_GEMM;
-    st = pick_path(M, K, bits, &path);
+    st = pick_path(M, N, K, bits, group_size, out_kind_of(y_dtype), &path);
     if (st != CIDER_OK)
         return st;
+    // Calls in the matrix-vector kernel's earlier automatic range (up to 8
+    // int8-weight or 4 int4-weight tokens) may come without a workspace:
+    // those keep that kernel, which needs none.
+    if (path == PATH_GEMM && !static_ws && (!ws || ws_bytes < cider_linear_workspace_bytes(M, K)) &&
+        g_path.load(std::memory_order_relaxed) == PATH_AUTO && M <= (bits == 4 ? 4 : 8) &&
+        M * K <= kGemvMaxBytes)
+        path = PATH_GEMV;
     // fp16 tokens without smoothing on the matrix-vector path: quantized inside
     // the matrix-vector kernel, whose buffer descriptor spans the tokens with
     // 32-bit byte offsets; a row stride that puts the last token 2 GiB or more
@@ -465,7 +484,7 @@ size_t cider_linear_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int bits
     const size_t base = cider_linear_workspace_bytes(M, K);
     int path = PATH_GEMM;
     if (check_shape(M, N, K, bits, group_size) != CIDER_OK || M <= 0 || N <= 0 ||
-        pick_path(M, K, bits, &path) != CIDER_OK || path != PATH_GEMM)
+        pick_path(M, N, K, bits, group_size, cider::OUT_F16, &path) != CIDER_OK || path != PATH_GEMM)
         return base;
     const cider::SplitPlan p = cider::plan_split(M, N, K, bits, group_size);
     return p.splits < 2 ? base : base + split_bytes(p);

@@ -49,6 +49,22 @@ __device__ __forceinline__ uint16_t out_bits(float y)
         return __builtin_bit_cast(uint16_t, (_Float16)y);
 }
 
+// Two outputs packed into one dword (first in the low half) by the packed
+// hardware conversion of the output type (round to nearest even, as the
+// scalar one in out_bits).
+template <int OUT>
+__device__ __forceinline__ uint32_t pack2(float a, float b)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    if constexpr (OUT == OUT_F16) {
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
+    } else {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+    }
+}
+
 struct ProductArgs {
     const int8_t *xq;      // [M, K]
     const float *s_tok;    // [M]         (OUT_F16)
@@ -68,8 +84,9 @@ struct SplitArgs {
     int splits;
 };
 
-// Matrix-core product (any M >= 1, every mode); per group with M <= 256
-// goes to the few-token kernel.
+// Matrix-core product (any M >= 1, every mode); up to 32 tokens it goes to
+// the few-token kernel where that supports the shape, else per group with
+// M <= 256 to the skinny kernel.
 hipError_t launch_gemm(const ProductArgs &a, hipStream_t stream);
 
 // Split-K product for few tokens (fp16 / bf16 output only).  Each output
@@ -87,6 +104,12 @@ SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int bits, int group_size);
 hipError_t launch_gemm_split(const ProductArgs &a, const SplitPlan &p, void *part, uint32_t *cnt,
                              hipStream_t stream);
 hipError_t launch_gemm_skinny(const ProductArgs &a, hipStream_t stream);
+
+// Few-token product (M <= 32, every mode but the per-group int32 hook; K a
+// multiple of 128 for int8 weights, 256 for int4): weights streamed as whole
+// lines and turned into matrix-core operands in per-wavefront LDS slots.
+bool few_supported(const ProductArgs &a);
+hipError_t launch_gemm_few(const ProductArgs &a, hipStream_t stream);
 
 // Matrix-vector product for M <= 8 and M * K <= 32768.
 hipError_t launch_gemv(const ProductArgs &a, hipStream_t stream);

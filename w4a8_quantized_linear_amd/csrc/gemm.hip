@@ -216,22 +216,6 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_n, int tiles_m, i
     tn = r / gsize;
 }
 
-// Two outputs packed into one dword (first in the low half) by the packed
-// hardware conversion of the output type (round to nearest even, as the
-// scalar one in out_bits).
-template <int OUT>
-__device__ __forceinline__ uint32_t pack2(float a, float b)
-{
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    if constexpr (OUT == OUT_F16) {
-        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
-    } else {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
-    }
-}
-
 // GS = 0: one scale per channel.  GS = 64 / 128: per-group scaling.  The
 // operands then swap roles -- tokens are operand A, weights operand B -- so
 // that a lane's outputs all belong to one channel per 32-channel block and
@@ -1785,8 +1769,18 @@ hipError_t launch_split_kind(const ProductArgs &a, const SplitPlan &p, void *par
 SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int bits, int group_size)
 {
     SplitPlan p{1, 0, 0};
-    (void)bits;
     if (group_size == 0 || M < 1 || M > 256 || N < 1 || K < group_size || K % group_size != 0)
+        return p;
+    // Up to 32 tokens the few-token kernel is faster unsplit (int8 gs64,
+    // N = 2560, K = 10240, M = 16: 12.9 us against about 20 us split).
+    ProductArgs fa{};
+    fa.M = M;
+    fa.N = N;
+    fa.K = K;
+    fa.bits = bits;
+    fa.group_size = group_size;
+    fa.out_kind = OUT_F16;
+    if (few_supported(fa))
         return p;
     const int TM = split_tm(M);
     const int64_t tiles = ((N + kSplitTN - 1) / kSplitTN) * ((M + TM - 1) / TM);
@@ -1827,6 +1821,8 @@ hipError_t launch_kind(const ProductArgs &a, hipStream_t stream)
 
 hipError_t launch_gemm(const ProductArgs &a, hipStream_t stream)
 {
+    if (few_supported(a))
+        return launch_gemm_few(a, stream);
     if (a.M <= 256 && a.group_size != 0)
         return launch_gemm_skinny(a, stream);
     switch (a.out_kind) {
