@@ -1589,8 +1589,9 @@ int64_t rounds(int64_t M, int64_t N, int TM, int TN)
 // addressable with 32-bit offsets, the persistent kernel with the smallest
 // output tile whose tiles all run at once, one per compute unit: 160 x 128
 // (4 waves of 160 x 32), 160 x 256 (4 waves of 160 x 64), else 256 x 256
-// (8 waves of 128 x 64) or 320 x 256 (8 waves of 160 x 64) over several
-// rounds, by rounds times time per tile (M = 1280 / 1536 / 2560 / 3072, int8:
+// (8 waves of 128 x 64), 320 x 256 (8 waves of 160 x 64) or, with int8
+// weights, 192 x 256 (8 waves of 96 x 64) over several rounds, by rounds
+// times time per tile (M = 1280 / 1536 / 2560 / 3072, int8:
 // 256 x 256 45.0 -> 41.2, 46.3 -> 44.3, 85.0 -> 74.2, 89.6 -> 79.9 us; at
 // M = 2048, 3584, 4096 and 6144 it needs one more round than 320 x 256 and
 // loses, 53.5 -> 73.6 us at 2048).  A second round costs a whole
@@ -1632,9 +1633,21 @@ hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
             return launch_wide<160, 128, 160, 32, BITS, OUT>(a, stream);
         if (one_round(160, 256))
             return launch_wide<160, 256, 160, 64, BITS, OUT>(a, stream);
-        // several rounds: 256 x 256 tiles take about 0.88x the time of
-        // 320 x 256 ones, so they win unless they need more rounds
-        if (88 * rounds(a.M, a.N, 256, 256) < 100 * rounds(a.M, a.N, 256, 320))
+        // several rounds: rounds times the time per tile, relative to a
+        // 320 x 256 tile: 256 x 256 about 0.88, and (int8) 192 x 256 (8 waves
+        // of 96 x 64) about 0.81 -- more time per unit of work, but whole
+        // rounds where the larger tiles leave the last round half empty (the
+        // 4096 x 6144 x 4096 product of the decoder stack's QKV projection:
+        // 192 x 256 100.3 us against 109.1 for 256 x 256 and 127.0 for
+        // 320 x 256; at 4096 x 10240 x 2560 it needs 4 rounds and takes
+        // 130.0 against 102.1 us)
+        const int64_t t320 = 100 * rounds(a.M, a.N, 256, 320), t256 = 88 * rounds(a.M, a.N, 256, 256);
+        if constexpr (BITS == 8) {
+            const int64_t t192 = 81 * rounds(a.M, a.N, 256, 192);
+            if (t192 < t256 && t192 < t320)
+                return launch_wide<192, 256, 96, 64, BITS, OUT>(a, stream);
+        }
+        if (t256 < t320)
             return launch_wide<256, 256, 128, 64, BITS, OUT>(a, stream);
         return launch_wide<320, 256, 160, 64, BITS, OUT>(a, stream);
     }
