@@ -669,6 +669,49 @@ def pin_dequant_vs_fake_quant(orc):
         assert np.array_equal(xq2, xq) and np.array_equal(st2, st)
 
 
+def _nearest_16(bits16, exact, dtype):
+    """True when the 16-bit pattern (fp16 dtype 0, bf16 dtype 1) is a value
+    nearest to the exact rational: no neighbouring pattern is closer."""
+    from fractions import Fraction
+    def val(b):
+        b = int(b) & 0xFFFF
+        if dtype == 0:
+            return Fraction(float(np.array([b], np.uint16).view(np.float16)[0]))
+        return Fraction(float(np.array([b << 16], np.uint32).view(np.float32)[0]))
+    got = val(bits16)
+    mag = int(bits16) & 0x7FFF
+    sign = int(bits16) & 0x8000
+    near = [sign | (mag + 1)]
+    near.append(sign | (mag - 1) if mag else (sign ^ 0x8000) | 1)
+    return all(abs(got - exact) <= abs(val(b) - exact) for b in near)
+
+
+def pin_dequant_nearest_rational(orc):
+    """The dequant, from the oracle's own codes and scales: every fp16 and
+    bf16 output is a value nearest to the exact rational
+    s_tok[m] * sum_g s_w[n, g] * acc[m, n, g] (Python fractions; fp32 scales
+    are exact rationals), per channel, per group 64 / 128 and int4.  A dropped
+    scale, a wrong group index or a transposed scale fails it."""
+    from fractions import Fraction
+    from synth_inputs import activations, weights
+    M, N, K = 5, 7, 256
+    x = activations(M, K, seed=47)
+    w = weights(N, K, seed=47)
+    xq, st = orc.quantize_act(x)
+    for bits, gs in ((8, 0), (8, 64), (8, 128), (4, 0), (4, 64)):
+        wq, sw = orc.quantize_weight(w, bits, gs)
+        acc = orc.gemm_acc(xq, wq, bits, gs)
+        a3 = acc if acc.ndim == 3 else acc[:, :, None]
+        swf = np.asarray(sw, np.float32).reshape(N, -1)
+        outs = [orc.dequant_ex(acc, st, sw, d) for d in (0, 1)]
+        for m in range(M):
+            for n in range(N):
+                exact = Fraction(float(st[m])) * sum(Fraction(float(swf[n, g])) * int(a3[m, n, g])
+                                                     for g in range(a3.shape[2]))
+                for d in (0, 1):
+                    assert _nearest_16(outs[d][m, n], exact, d), (bits, gs, m, n, d)
+
+
 def pin_symmetry(orc):
     """quantize(-X) = -quantize(X) and Y(-X) = -Y(X), bit for bit."""
     from synth_inputs import activations, weights

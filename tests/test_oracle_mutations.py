@@ -32,6 +32,9 @@ MUTATIONS = {
     "group_scale_transposed": ("t += (double)s_w_row[g] * (double)acc_row[g];",
                                "t += (double)s_w_row[0] * (double)acc_row[g];"),
     "token_scale_dropped": ("return (double)s_tok * t;", "return t;"),
+    "group_sum_shifted": ("t += (double)s_w_row[g] * (double)acc_row[g];",
+                          "t += (double)s_w_row[g] * (double)acc_row[g ? g - 1 : 0];"),
+    "token_scale_squared": ("return (double)s_tok * t;", "return (double)s_tok * (double)s_tok * t * 64.0;"),
     "half_decode_exponent": ("ldexp((double)(1024 + man), e - 25)", "ldexp((double)(1024 + man), e - 24)"),
     "half_encode_ties_away": ("double m = nearbyint(ldexp(a, -q));", "double m = round(ldexp(a, -q));"),
     "half_encode_quantum": ("? -24 : e - 11;", "? -24 : e - 10;"),
