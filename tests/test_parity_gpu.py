@@ -411,9 +411,13 @@ def test_decode_linear(N, K, bits, gs, y_dtype):
 
 # ----------------------------------------------------------------- product ---
 
+# (100 / 200 / 256 tokens at K = 1024 / 2048: per group, the few-token
+# kernel's 32-token tiles repeated over M, or with int8 weights past 192
+# tokens the persistent per-group tiles)
 PRODUCT_SHAPES = [(64, 512, 1024), (300, 320, 1024), (700, 576, 512), (513, 1024, 2560),
                   (1, 512, 1024), (17, 64, 128), (1100, 704, 1024), (2100, 320, 1024),
-                  (40, 320, 576), (200, 192, 1344)]
+                  (40, 320, 576), (200, 192, 1344), (100, 320, 1024), (200, 320, 1024),
+                  (256, 640, 2048)]
 
 
 def _inputs(M, N, K, bits, gs, seed):

@@ -105,9 +105,13 @@ hipError_t launch_gemm_split(const ProductArgs &a, const SplitPlan &p, void *par
                              hipStream_t stream);
 hipError_t launch_gemm_skinny(const ProductArgs &a, hipStream_t stream);
 
-// Few-token product (M <= 32, every mode but the per-group int32 hook; K a
-// multiple of 128 for int8 weights, 256 for int4): weights streamed as whole
-// lines and turned into matrix-core operands in per-wavefront LDS slots.
+// Few-token product (every mode but the per-group int32 hook; K a multiple of
+// 128 for int8 weights, 256 for int4): weights streamed as whole lines and
+// turned into matrix-core operands in per-wavefront LDS slots, 16 or 32
+// tokens per tile.  few_shape_ok: the kernel can take the shape at any M;
+// few_supported: it is the product of choice (M <= 32).  launch_gemm_few
+// takes any shape few_shape_ok accepts.
+bool few_shape_ok(const ProductArgs &a);
 bool few_supported(const ProductArgs &a);
 hipError_t launch_gemm_few(const ProductArgs &a, hipStream_t stream);
 

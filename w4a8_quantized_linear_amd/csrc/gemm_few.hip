@@ -1,4 +1,5 @@
-// Matrix-core product for a few tokens (9..32 per tile), every mode: the
+// Matrix-core product for a few tokens (up to 32 per tile; per group without
+// a split workspace, tiles repeated over up to 256 tokens), every mode: the
 // int32 sums of int8 x int8 (or widened int4) products, dequantized in the
 // epilogue (Cider README, ossradar.top repo page, "Quantization" table:
 // INT32 accumulation, C_fp16 = C_int32 * s_act * s_weight; "W8A8
@@ -435,19 +436,21 @@ hipError_t launch_gs(const ProductArgs &a, hipStream_t stream)
 
 }  // namespace
 
-bool few_supported(const ProductArgs &a)
+bool few_shape_ok(const ProductArgs &a)
 {
     const int64_t uk = a.bits == 8 ? 128 : 256;
     const int64_t wld = a.bits == 8 ? a.K : a.K / 2;
     const int64_t G = a.group_size ? a.K / a.group_size : 1;
-    return a.M >= 1 && a.M <= 32 && a.N >= 1 && a.K >= uk && a.K % uk == 0 &&
+    return a.M >= 1 && a.N >= 1 && a.K >= uk && a.K % uk == 0 &&
            !(a.group_size != 0 && a.out_kind == OUT_I32) && a.N * wld < (1LL << 31) &&
-           a.M * a.K < (1LL << 31) && a.N * G * 4 < (1LL << 31);
+           (a.M + 32) * a.K < (1LL << 31) && a.N * G * 4 < (1LL << 31);
 }
+
+bool few_supported(const ProductArgs &a) { return a.M <= 32 && few_shape_ok(a); }
 
 hipError_t launch_gemm_few(const ProductArgs &a, hipStream_t stream)
 {
-    if (!few_supported(a))
+    if (!few_shape_ok(a))
         return hipErrorNotSupported;
     if (a.bits == 8) {
         if (a.group_size == 0)
