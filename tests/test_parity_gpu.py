@@ -530,13 +530,15 @@ def test_many_token_tiles(M, N, K, bits, out):
 
 
 @pytest.mark.parametrize("out", ["f16", "bf16"])
-@pytest.mark.parametrize("bits,gs", [(8, 128), (4, 128), (8, 64)])
+@pytest.mark.parametrize("bits,gs", [(8, 128), (4, 128), (8, 64), (4, 64)])
 @pytest.mark.parametrize("M,N,K", [(4100, 2624, 1024), (3100, 640, 2048), (3100, 640, 1344)])
 def test_many_token_tiles_per_group(M, N, K, bits, gs, out):
     """Per-group products with many tokens.  4100 x 2624: too many tiles for
-    one round even at 256 channels, so groups of 128 take the 320 x 128
+    one round even at 256 channels, so int8 groups of 128 take the 320 x 128
     persistent kernel (297 output tiles, ragged in M and N, so some
-    workgroups take two) and groups of 64 the other kernel; 3100 x 640: one
+    workgroups take two), int8 groups of 64 the other kernel, and int4
+    weights the 192 x 256 persistent tiles with two token blocks per wave
+    (238 tiles, ragged in M and N); 3100 x 640: one
     round of 64 x 128 persistent tiles (250 of them, ragged in M); K = 1344
     (not a multiple of 128) takes the other kernel.  Sampled rows against the
     oracle, every output against the exact product."""

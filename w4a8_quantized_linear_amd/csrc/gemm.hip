@@ -1184,7 +1184,8 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_wide_kernel(P
 }
 
 // Persistent per-group product for many tokens (int8 or packed int4
-// weights, groups of 64 / 128 along K): the copy path of gemm_wide_kernel
+// weights, groups of 64 / 128 along K; a wave owns one or two 32-token blocks
+// of WN channels): the copy path of gemm_wide_kernel
 // (128-byte K tiles, one workgroup per compute unit walking output tiles,
 // copies streaming across tiles) with the operands of the
 // per-group gemm_kernel (tokens are operand A, so a lane's outputs belong to
@@ -1214,7 +1215,8 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
     constexpr int BK = 128;
     constexpr int NWN = TN / WN, NWM = TM / WM, NW = NWN * NWM;
     constexpr int FN = WN / 32;  // 32-channel blocks per wave
-    static_assert(WM == 32 && WN % 32 == 0 && TN % WN == 0 && TM % WM == 0, "one 32-token block per wave");
+    constexpr int FM = WM / 32;  // 32-token blocks per wave
+    static_assert(WM % 32 == 0 && WN % 32 == 0 && TN % WN == 0 && TM % WM == 0, "whole 32 x 32 blocks per wave");
     static_assert(OUT != OUT_I32, "the int32 hook takes gemm_kernel");
     constexpr int XROW = BK, WROW = BITS == 8 ? BK : BK / 2;
     constexpr int XBYTES = TM * XROW, WBYTES = TN * WROW;
@@ -1226,7 +1228,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
     constexpr int DX = (XB + NW - 1) / NW, DW = (WB + NW - 1) / NW, DS = (SB + NW - 1) / NW;
     constexpr int D = DX + DW + DS;  // copies per wave per K tile
     static_assert(XBYTES % 1024 == 0 && WBYTES % 1024 == 0 && TN % 64 == 0, "whole copy blocks");
-    constexpr int STORES = FN * 16;  // 2-byte output stores per wave per output tile
+    constexpr int STORES = FN * FM * 16;  // 2-byte output stores per wave per output tile
     constexpr int NSC = (TM + NW * 64 - 1) / (NW * 64);
 
     static_assert(STG >= 2, "at least double buffering");
@@ -1288,10 +1290,10 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
         }
     };
 
-    // Fragments: operand A = the wave's 32 token rows, operand B = its FN
-    // 32-channel blocks (packed int4 bytes until widened).
+    // Fragments: operand A = the wave's FM blocks of 32 token rows, operand
+    // B = its FN 32-channel blocks (packed int4 bytes until widened).
     struct Frags {
-        i32x4 x;
+        i32x4 x[FM];
         i32x4 w[FN];
         uint2 wp[BITS == 4 ? FN : 1];
     };
@@ -1301,7 +1303,9 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
     auto load_frags = [&](Frags &f, int stage, int ks) {
         const uint32_t a = (xbase + (uint32_t)(stage * STAGE)) ^ (uint32_t)(ks << 5);
         const uint32_t b = (wbase + (uint32_t)(stage * STAGE)) ^ (uint32_t)(ks << (BITS == 8 ? 5 : 4));
-        f.x = *reinterpret_cast<const i32x4 *>(smem + a);
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+            f.x[j] = *reinterpret_cast<const i32x4 *>(smem + a + j * 32 * XROW);
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
             if constexpr (BITS == 8)
@@ -1318,11 +1322,13 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
             sw[i] = ss[wn * WN + i * 32 + frow];
     };
 
-    i32x16 acc[FN];
-    float facc[FN][16];
+    i32x16 acc[FN][FM];
+    float facc[FN][FM][16];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
-        acc[i] = i32x16{};
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+            acc[i][j] = i32x16{};
     // One 32-deep step.  first: the step opens a group: block i of the group
     // that closed before it is scaled into facc with the scales `sw` right
     // before block i's first MFMA (which starts from zero) overwrites its
@@ -1337,31 +1343,37 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
             load_frags(nxt, lstage, lks);
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
-            if constexpr (decltype(first)::value) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    facc[i][e] += (float)acc[i][e] * sw[i];
-            }
-            if constexpr (BITS == 4) {
-                uint32_t d0, d1, d2, d3;
-                unpack8(cur.wp[i].x, d0, d1);
-                unpack8(cur.wp[i].y, d2, d3);
-                cur.w[i] = i32x4{(int)d0, (int)d1, (int)d2, (int)d3};
-            }
-            if constexpr (decltype(first)::value) {
-                // Block i's MFMA must follow its scaling: otherwise the compiler
-                // may run the new group's MFMAs first and keep both groups' sums
-                // live (twice the registers).  The weight fragment passes through
-                // an empty asm that takes the scaled sums as inputs.
-                asm volatile(""
-                             : "+v"(cur.w[i])
-                             : "v"(facc[i][0]), "v"(facc[i][1]), "v"(facc[i][2]), "v"(facc[i][3]),
-                               "v"(facc[i][4]), "v"(facc[i][5]), "v"(facc[i][6]), "v"(facc[i][7]),
-                               "v"(facc[i][8]), "v"(facc[i][9]), "v"(facc[i][10]), "v"(facc[i][11]),
-                               "v"(facc[i][12]), "v"(facc[i][13]), "v"(facc[i][14]), "v"(facc[i][15]));
-                acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.x, cur.w[i], i32x16{}, 0, 0, 0);
-            } else {
-                acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.x, cur.w[i], acc[i], 0, 0, 0);
+            for (int j = 0; j < FM; ++j) {
+                if constexpr (decltype(first)::value) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        facc[i][j][e] += (float)acc[i][j][e] * sw[i];
+                }
+                if constexpr (BITS == 4) {
+                    if (j == 0) {
+                        uint32_t d0, d1, d2, d3;
+                        unpack8(cur.wp[i].x, d0, d1);
+                        unpack8(cur.wp[i].y, d2, d3);
+                        cur.w[i] = i32x4{(int)d0, (int)d1, (int)d2, (int)d3};
+                    }
+                }
+                if constexpr (decltype(first)::value) {
+                    // Block (i, j)'s MFMA must follow its scaling: otherwise the
+                    // compiler may run the new group's MFMAs first and keep both
+                    // groups' sums live (twice the registers).  The weight
+                    // fragment passes through an empty asm that takes the scaled
+                    // sums as inputs.
+                    const float(&f)[16] = facc[i][j];
+                    asm volatile(""
+                                 : "+v"(cur.w[i])
+                                 : "v"(f[0]), "v"(f[1]), "v"(f[2]), "v"(f[3]), "v"(f[4]), "v"(f[5]), "v"(f[6]),
+                                   "v"(f[7]), "v"(f[8]), "v"(f[9]), "v"(f[10]), "v"(f[11]), "v"(f[12]),
+                                   "v"(f[13]), "v"(f[14]), "v"(f[15]));
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.x[j], cur.w[i], i32x16{}, 0, 0, 0);
+                } else {
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.x[j], cur.w[i], acc[i][j], 0, 0, 0);
+                }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1397,8 +1409,10 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                facc[i][e] = 0.f;
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    facc[i][j][e] = 0.f;
         __builtin_amdgcn_s_barrier();  // K tile 0 of this output tile is in, in every wave's view
         __builtin_amdgcn_sched_barrier(0);
         Frags f0, f1;
@@ -1444,11 +1458,14 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                facc[i][e] += (float)acc[i][e] * swp[i];
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    facc[i][j][e] += (float)acc[i][j][e] * swp[i];
 
-        // Epilogue: y = s_tok[m] * facc.  Block i: channel n = wn*WN + 32i +
-        // lane%32, tokens wm*WM + 8q + 4*(lane/32) + e for element 4q + e.
+        // Epilogue: y = s_tok[m] * facc.  Block (i, j): channel n = wn*WN +
+        // 32i + lane%32, tokens wm*WM + 32j + 8q + 4*(lane/32) + e for element
+        // 4q + e.
 #pragma unroll
         for (int i = 0; i < NSC; ++i) {
             const int q = (int)threadIdx.x + i * NW * 64;
@@ -1464,23 +1481,27 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_group_wide_ke
         const auto ry = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ybase), (short)0,
                                                           (int)(min((int64_t)TM, M - m0) * N * 2), 0x00020000);
         const int nvalid = (int)min((int64_t)TN, N - n0);
-        f32x4 stv[4];
+        f32x4 stv[FM][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            stv[q] = *reinterpret_cast<const f32x4 *>(&s_st[wm * WM + q * 8 + eh * 4]);
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                stv[j][q] = *reinterpret_cast<const f32x4 *>(&s_st[wm * WM + j * 32 + q * 8 + eh * 4]);
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
             const int nc = wn * WN + i * 32 + er;
             const uint32_t base = nc < nvalid ? (uint32_t)(wm * WM + eh * 4) * rowbytes + (uint32_t)(n0 + nc) * 2u
                                               : 0x80000000u;  // past the buffer: dropped
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int j = 0; j < FM; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float y = stv[q][e] * facc[i][4 * q + e];
-                    __builtin_amdgcn_raw_buffer_store_b16(out_bits<OUT>(y), ry,
-                                                          base + (uint32_t)(q * 8 + e) * rowbytes, 0, 2);
-                }
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float y = stv[j][q][e] * facc[i][j][4 * q + e];
+                        __builtin_amdgcn_raw_buffer_store_b16(
+                            out_bits<OUT>(y), ry, base + (uint32_t)(j * 32 + q * 8 + e) * rowbytes, 0, 2);
+                    }
         }
         if (!has_next)
             break;
@@ -1709,6 +1730,17 @@ hipError_t launch_group(const ProductArgs &a, hipStream_t stream)
                     return launch_group_wide<192, 128, 64, 32, BITS, GS, OUT, 3>(a, stream);
                 if (one_round(256))
                     return launch_group_wide<256, 128, 128, 32, BITS, GS, OUT, 3>(a, stream);
+            }
+            // int4 weights past that: 192 x 256 tiles of 8 waves of 96 x 64, so
+            // every widened weight fragment feeds two token blocks (half the
+            // widening per MFMA): gs64 / gs128 M = 4096 246.3 / 204.8 ->
+            // 210.4 / 177.8 us, M = 8192 481.8 / 397.5 -> 412.7 / 349.0 us
+            // (int8: within +-3 %, kept).  Below one round of them they lose
+            // to the small one-round tiles (M = 2048 gs64 142.4 against
+            // 207.5 us).
+            if constexpr (BITS == 4) {
+                if (a.M > 3072 && a.K >= 256 && 256 * a.N * 2 < (int64_t(1) << 31))
+                    return launch_group_wide<192, 256, 96, 64, BITS, GS, OUT, 2>(a, stream);
             }
             if (GS == 128 && a.M > 3072 && a.K >= 256)
                 return launch_group_wide<320, 128, 160, 32, BITS, GS, OUT, 2>(a, stream);
