@@ -490,7 +490,8 @@ def test_few_token_kernel(M, N, K, bits, gs, out):
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("M,N,K", [(2100, 10304, 1024), (1100, 640, 256), (1030, 576, 1344),
                                    (1100, 320, 128), (4100, 704, 2560), (1100, 5056, 1024),
-                                   (1100, 10176, 512), (2040, 10176, 256), (4000, 6080, 256)])
+                                   (1100, 10176, 512), (2040, 10176, 256), (4000, 6080, 256),
+                                   (160, 2112, 1024), (224, 2176, 1024)])
 def test_many_token_tiles(M, N, K, bits, out):
     """Per-channel persistent tiles.  With K a multiple of 128 and at least
     256, one workgroup per compute unit walks output tiles.  On a 256-unit
@@ -501,7 +502,9 @@ def test_many_token_tiles(M, N, K, bits, out):
     not of 160 x 128 (288); 1100 x 640 and 4100 x 704 one round of 160 x 128
     (36 and 165, ragged N); 4000 x 6080 two whole rounds of 192 x 256 with
     int8 weights (512, ragged in M and N), where 256 x 256 and 320 x 256
-    would leave the second round partly empty.  K = 1344 (not a multiple of 128) and K = 128
+    would leave the second round partly empty; 160 x 2112 the 64 x 64
+    few-token tiles repeated over M (99 workgroups, ragged M) and 224 x 2176
+    the 96 x 128 persistent tiles (46, ragged in M and N).  K = 1344 (not a multiple of 128) and K = 128
     (one K tile) take the other kernel.  int32 sums bit-exact and outputs
     within tolerance on sampled rows against the oracle, every output
     against the exact product."""
@@ -511,6 +514,7 @@ def test_many_token_tiles(M, N, K, bits, out):
     d = [gu.to_dev(a) for a in (xq, st, wq, sw)]
     rows = np.unique(np.concatenate([[0, 1, 255, 256, 511, M // 2, M - 2, M - 1],
                                      np.random.default_rng(M).integers(0, M, 8)]))
+    rows = rows[rows < M]
     ref_acc = orc.gemm_acc(xq[rows], wq, bits, 0)
     if out == "i32":
         acc = gu.to_host(gu.gemm_i32_gpu(d[0], d[2], M, N, K, bits, 0))
