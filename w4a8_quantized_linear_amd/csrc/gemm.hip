@@ -1890,16 +1890,19 @@ hipError_t launch_kind(const ProductArgs &a, hipStream_t stream)
 // 40.1 / 60.2, M = 192: 61.4 / 52.3 / 60.5, M = 256: 89.2 / 65.6 / 60.4;
 // gs128 M = 128: 52.0 / 36.2 / 46.8, M = 256: 76.3 / 59.3 / 47.1; int4 gs64
 // M = 128: 58.8 / 34.4 / 81.3, M = 256: - / 54.9 / 81.4; int4 gs128 M = 256:
-// 74.9 / 46.3 / 70.0.  So int8 193..256 tokens take the persistent tiles
-// (whole 128-byte K tiles, deep enough for their ring); the skinny kernel
-// keeps the shapes neither takes and the per-group int32 hook.
+// 74.9 / 46.3 / 70.0; int4 gs64 / gs128 M = 320: - / 73.1 / 81.1 and
+// - / 61.5 / 69.7, M = 384: - / 83.8 / 81.2 and - / 70.6 / 69.5.  So int4
+// takes the few-token tiles up to 320 tokens, int8 up to 192, and int8
+// 193..256 tokens the persistent tiles (whole 128-byte K tiles, deep enough
+// for their ring); the skinny kernel keeps the shapes none of them takes and
+// the per-group int32 hook.
 hipError_t launch_gemm(const ProductArgs &a, hipStream_t stream)
 {
     if (few_supported(a))
         return launch_gemm_few(a, stream);
+    if (a.group_size != 0 && a.M <= (a.bits == 4 ? 320 : 192) && few_shape_ok(a))
+        return launch_gemm_few(a, stream);
     if (a.M <= 256 && a.group_size != 0) {
-        if (few_shape_ok(a) && (a.bits == 4 || a.M <= 192))
-            return launch_gemm_few(a, stream);
         if (a.bits == 8 && a.out_kind != OUT_I32 && a.K % 128 == 0 && a.K >= 512 &&
             128 * a.N * 2 < (int64_t(1) << 31))
             return a.out_kind == OUT_F16 ? launch_kind<OUT_F16>(a, stream) : launch_kind<OUT_BF16>(a, stream);
