@@ -1606,8 +1606,8 @@ int64_t rounds(int64_t M, int64_t N, int TM, int TN)
 
 // Tile shape by M (measured on MI355X over the N=10240 / N=2560 operator
 // shapes).  M <= 128: 64 channels x 32 / 64 / 128 tokens with deep K tiles;
-// up to 192 the 64 x 64 tiles repeated over M; up to 256 persistent 96 x 128
-// tiles.
+// up to 192 the 64 x 64 tiles repeated over M, up to 384 128 x 128 deep-K
+// tiles, up to 512 (int8) 128 x 192 deep-K tiles.
 // Past that, with whole 128-byte K tiles (at least two) and outputs
 // addressable with 32-bit offsets, the persistent kernel with the smallest
 // output tile whose tiles all run at once, one per compute unit: 160 x 128
@@ -1649,23 +1649,30 @@ hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
             return launch_cfg<64, 64, 32, 32, BKS, BITS, 0, OUT, STS>(a, stream);
         return launch_cfg<64, 128, 32, 32, BKS, BITS, 0, OUT, STS>(a, stream);
     }
-    // 129..192 tokens: the 64 x 64 few-token tiles repeated over M (at
-    // N = 10240, K = 2560 three of them per 64 channels, about two resident
-    // workgroups per compute unit) beat the one-round persistent tiles, which
-    // leave half the compute units idle here (M = 160 / 192: int8 15.1 /
-    // 16.0 us against 23.3 / 23.7 for 160 x 128; int4 14.7 / 14.4 against
-    // 22.0 / 22.4); at 128 tokens they lose (16.5 against 14.0 us).
-    if (a.M <= 192 && a.K % BKS == 0)
-        return launch_cfg<64, 64, 32, 32, BKS, BITS, 0, OUT, STS>(a, stream);
+    // 129..512 tokens, deep K tiles of the same kernel where they make about
+    // one round of workgroups, which the one-round persistent tiles (160 x
+    // 128, 4 waves) do not beat here: they leave compute units idle or run
+    // too few waves per unit.  At N = 10240, K = 2560 (product, us; persistent
+    // 160 x 128 in brackets): 64 x 64 tiles repeated over M, M = 160 / 192:
+    // int8 15.1 / 16.0 (23.3 / 23.7), int4 14.7 / 14.4 (22.0 / 22.4), and
+    // 16.5 against 14.0 for the 64 x 128 tiles at 128 tokens; 128 x 128 tiles
+    // of 8 waves of 64 x 32, M = 256 / 320 / 384: int8 17.2 / 16.4 / 17.3
+    // (21.7 for 96 x 128 at 256; 23.6 / 25.7 at 320 / 384), int4 M = 256 /
+    // 288 / 384: 19.6 / 19.5 / 19.8 (20.5 / 22.2 / 23.2); int8 128 x 192 tiles
+    // of 12 waves, M = 448 / 512: 21.4 / 21.9 (23.8 / 25.8; 128 x 128: 29.7 /
+    // 31.3, two rounds).
+    if (a.K % BKS == 0) {
+        if (a.M <= 192)
+            return launch_cfg<64, 64, 32, 32, BKS, BITS, 0, OUT, STS>(a, stream);
+        if (a.M <= 384)
+            return launch_cfg<128, 128, 64, 32, BKS, BITS, 0, OUT, STS>(a, stream);
+        if constexpr (BITS == 8) {
+            if (a.M <= 512)
+                return launch_cfg<128, 192, 64, 32, BKS, BITS, 0, OUT, 3>(a, stream);
+        }
+    }
     if (a.K % 128 == 0 && a.K >= 256 && 256 * a.N * 4 < (int64_t(1) << 31)) {
         const int64_t cu = compute_units();
-        // 193..256 tokens: persistent 96 x 128 tiles (4 waves of 96 x 32;
-        // 214 of them at N = 10240) fill the compute units that 160 x 128
-        // leaves idle (M = 224 / 256: int8 20.7 / 21.7 us against 24.9 /
-        // 25.9, int4 20.0 / 20.5 against 23.1 / 23.5); past 256 tokens they
-        // need two rounds (37.0 us at 288)
-        if (a.M <= 256)
-            return launch_wide<96, 128, 96, 32, BITS, OUT>(a, stream);
         auto one_round = [&](int64_t tn, int64_t tm) { return (a.N + tn - 1) / tn * ((a.M + tm - 1) / tm) <= cu; };
         if (one_round(160, 128))
             return launch_wide<160, 128, 160, 32, BITS, OUT>(a, stream);
