@@ -1607,7 +1607,7 @@ int64_t rounds(int64_t M, int64_t N, int TM, int TN)
 // Tile shape by M (measured on MI355X over the N=10240 / N=2560 operator
 // shapes).  M <= 128: 64 channels x 32 / 64 / 128 tokens with deep K tiles;
 // up to 192 the 64 x 64 tiles repeated over M, up to 384 128 x 128 deep-K
-// tiles, up to 512 (int8) 128 x 192 deep-K tiles.
+// tiles, int8 up to 576 128 x 192 and up to 768 128 x 256 deep-K tiles.
 // Past that, with whole 128-byte K tiles (at least two) and outputs
 // addressable with 32-bit offsets, the persistent kernel with the smallest
 // output tile whose tiles all run at once, one per compute unit: 160 x 128
@@ -1659,16 +1659,21 @@ hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
     // of 8 waves of 64 x 32, M = 256 / 320 / 384: int8 17.2 / 16.4 / 17.3
     // (21.7 for 96 x 128 at 256; 23.6 / 25.7 at 320 / 384), int4 M = 256 /
     // 288 / 384: 19.6 / 19.5 / 19.8 (20.5 / 22.2 / 23.2); int8 128 x 192 tiles
-    // of 12 waves, M = 448 / 512: 21.4 / 21.9 (23.8 / 25.8; 128 x 128: 29.7 /
-    // 31.3, two rounds).
+    // of 12 waves, M = 448 / 512 / 576: 21.4 / 21.9 / 23.1 (23.8 / 25.8 /
+    // 31.7; 128 x 128: 29.7 / 31.3 at 448 / 512, two rounds); int8 128 x 256
+    // tiles of 8 waves of 64 x 64, M = 640 / 768: 24.5 / 26.0 (persistent
+    // 160 x 256: 31.2 / 32.8; at 896 / 1024 they need two rounds, 42.3 /
+    // 45.6 against 33.5 / 35.9).
     if (a.K % BKS == 0) {
         if (a.M <= 192)
             return launch_cfg<64, 64, 32, 32, BKS, BITS, 0, OUT, STS>(a, stream);
         if (a.M <= 384)
             return launch_cfg<128, 128, 64, 32, BKS, BITS, 0, OUT, STS>(a, stream);
         if constexpr (BITS == 8) {
-            if (a.M <= 512)
+            if (a.M <= 576)
                 return launch_cfg<128, 192, 64, 32, BKS, BITS, 0, OUT, 3>(a, stream);
+            if (a.M <= 768)
+                return launch_cfg<128, 256, 64, 64, BKS, BITS, 0, OUT, 3>(a, stream);
         }
     }
     if (a.K % 128 == 0 && a.K >= 256 && 256 * a.N * 4 < (int64_t(1) << 31)) {
