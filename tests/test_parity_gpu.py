@@ -492,7 +492,7 @@ def test_few_token_kernel(M, N, K, bits, gs, out):
                                    (1100, 320, 128), (4100, 704, 2560), (1100, 5056, 1024),
                                    (1100, 10176, 512), (2040, 10176, 256), (4000, 6080, 256),
                                    (160, 2112, 1024), (224, 2176, 1024), (450, 2240, 1024),
-                                   (700, 2240, 1024)])
+                                   (700, 2240, 1024), (900, 2304, 1024)])
 def test_many_token_tiles(M, N, K, bits, out):
     """Per-channel persistent tiles.  With K a multiple of 128 and at least
     256, one workgroup per compute unit walks output tiles.  On a 256-unit
@@ -506,8 +506,9 @@ def test_many_token_tiles(M, N, K, bits, out):
     would leave the second round partly empty; deep-K tiles of the other
     kernel from 129 to 512 tokens: 160 x 2112 64 x 64 tiles (99 workgroups,
     ragged M), 224 x 2176 128 x 128 tiles (34, ragged in M and N) and, int8
-    only, 450 x 2240 128 x 192 tiles (54, ragged in M and N) and 700 x 2240
-    128 x 256 tiles (54, ragged in M and N).  K = 1344 (not a multiple of 128) and K = 128
+    only, 450 x 2240 128 x 192 tiles (54, ragged in M and N), 700 x 2240
+    128 x 256 tiles (54, ragged M) and 900 x 2304 160 x 256 tiles (60, ragged
+    in M and N).  K = 1344 (not a multiple of 128) and K = 128
     (one K tile) take the other kernel.  int32 sums bit-exact and outputs
     within tolerance on sampled rows against the oracle, every output
     against the exact product."""

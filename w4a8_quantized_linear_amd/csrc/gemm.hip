@@ -1607,7 +1607,8 @@ int64_t rounds(int64_t M, int64_t N, int TM, int TN)
 // Tile shape by M (measured on MI355X over the N=10240 / N=2560 operator
 // shapes).  M <= 128: 64 channels x 32 / 64 / 128 tokens with deep K tiles;
 // up to 192 the 64 x 64 tiles repeated over M, up to 384 128 x 128 deep-K
-// tiles, int8 up to 576 128 x 192 and up to 768 128 x 256 deep-K tiles.
+// tiles, int8 up to 576 128 x 192, up to 768 128 x 256 and up to 1024
+// 160 x 256 deep-K tiles (each where it makes about one round).
 // Past that, with whole 128-byte K tiles (at least two) and outputs
 // addressable with 32-bit offsets, the persistent kernel with the smallest
 // output tile whose tiles all run at once, one per compute unit: 160 x 128
@@ -1664,16 +1665,26 @@ hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
     // tiles of 8 waves of 64 x 64, M = 640 / 768: 24.5 / 26.0 (persistent
     // 160 x 256: 31.2 / 32.8; at 896 / 1024 they need two rounds, 42.3 /
     // 45.6 against 33.5 / 35.9).
+    // (Each only where its workgroups fit that round: the 64 x 64 tiles two
+    // per compute unit, the others one; wider layers keep the persistent
+    // tiles below.)  int8 160 x 256 tiles of 8 waves of 160 x 32, M = 896 /
+    // 1024: 30.5 / 31.9 (persistent 160 x 256 of 4 waves: 32.5 / 35.1).
     if (a.K % BKS == 0) {
-        if (a.M <= 192)
+        const int64_t cu = compute_units();
+        auto fits = [&](int64_t tn, int64_t tm, int64_t per_cu) {
+            return (a.N + tn - 1) / tn * ((a.M + tm - 1) / tm) <= per_cu * cu;
+        };
+        if (a.M <= 192 && fits(64, 64, 2))
             return launch_cfg<64, 64, 32, 32, BKS, BITS, 0, OUT, STS>(a, stream);
-        if (a.M <= 384)
+        if (a.M <= 384 && fits(128, 128, 1))
             return launch_cfg<128, 128, 64, 32, BKS, BITS, 0, OUT, STS>(a, stream);
         if constexpr (BITS == 8) {
-            if (a.M <= 576)
+            if (a.M <= 576 && fits(128, 192, 1))
                 return launch_cfg<128, 192, 64, 32, BKS, BITS, 0, OUT, 3>(a, stream);
-            if (a.M <= 768)
+            if (a.M <= 768 && fits(128, 256, 1))
                 return launch_cfg<128, 256, 64, 64, BKS, BITS, 0, OUT, 3>(a, stream);
+            if (a.M <= 1024 && fits(160, 256, 1))
+                return launch_cfg<160, 256, 160, 32, BKS, BITS, 0, OUT, 3>(a, stream);
         }
     }
     if (a.K % 128 == 0 && a.K >= 256 && 256 * a.N * 4 < (int64_t(1) << 31)) {
