@@ -507,8 +507,8 @@ def test_many_token_tiles(M, N, K, bits, out):
     kernel from 129 to 512 tokens: 160 x 2112 64 x 64 tiles (99 workgroups,
     ragged M), 224 x 2176 128 x 128 tiles (34, ragged in M and N) and, int8
     only, 450 x 2240 128 x 192 tiles (54, ragged in M and N), 700 x 2240
-    128 x 256 tiles (54, ragged M) and 900 x 2304 160 x 256 tiles (60, ragged
-    in M and N).  K = 1344 (not a multiple of 128) and K = 128
+    128 x 256 tiles (54, ragged M; int4 with 128-value K tiles) and
+    900 x 2304 160 x 256 tiles (60, ragged in M and N).  K = 1344 (not a multiple of 128) and K = 128
     (one K tile) take the other kernel.  int32 sums bit-exact and outputs
     within tolerance on sampled rows against the oracle, every output
     against the exact product."""

@@ -1669,11 +1669,19 @@ hipError_t launch_bits(const ProductArgs &a, hipStream_t stream)
     // per compute unit, the others one; wider layers keep the persistent
     // tiles below.)  int8 160 x 256 tiles of 8 waves of 160 x 32, M = 896 /
     // 1024: 30.5 / 31.9 (persistent 160 x 256 of 4 waves: 32.5 / 35.1).
+    const int64_t ncu = compute_units();
+    auto fits = [&](int64_t tn, int64_t tm, int64_t per_cu) {
+        return (a.N + tn - 1) / tn * ((a.M + tm - 1) / tm) <= per_cu * ncu;
+    };
+    // int4, 513..768 tokens: 128 x 256 tiles of 8 waves of 64 x 64 with
+    // 128-value K tiles (64-byte packed rows), M = 640 / 768: 26.7 / 28.2 us
+    // against 34.6 / 34.9 for the persistent 160 x 256 tiles (at 448 / 512:
+    // 26.3 / 26.4 against 22.7 / 23.5 for 160 x 128).
+    if constexpr (BITS == 4) {
+        if (a.M > 512 && a.M <= 768 && a.K % 128 == 0 && fits(128, 256, 1))
+            return launch_cfg<128, 256, 64, 64, 128, BITS, 0, OUT, 3>(a, stream);
+    }
     if (a.K % BKS == 0) {
-        const int64_t cu = compute_units();
-        auto fits = [&](int64_t tn, int64_t tm, int64_t per_cu) {
-            return (a.N + tn - 1) / tn * ((a.M + tm - 1) / tm) <= per_cu * cu;
-        };
         if (a.M <= 192 && fits(64, 64, 2))
             return launch_cfg<64, 64, 32, 32, BKS, BITS, 0, OUT, STS>(a, stream);
         if (a.M <= 384 && fits(128, 128, 1))
