@@ -161,8 +161,11 @@ cider_status cider_quantize_act(const void *x_f16, int64_t M, int64_t K, int64_t
    Pipeline", step matmul_fused_dequant; "TensorOps matmul2d"; "W8A8
    Quantization Granularity").  group_size 0: per-channel s_w [N];
    64 / 128: per-group s_w [N, K/gs].  y: fp16 [M, N].
-   Few tokens (M * K <= 65536 and M <= 8, or M <= 4 for int4 weights) run the
-   matrix-vector kernel, more the matrix-core kernel. */
+   Under the automatic path setting the matrix-vector kernel takes
+   M * K <= 65536 with M <= 3 per channel or M <= 2 per group where the
+   few-token matrix-core kernel applies (K a multiple of 128 int8 / 256 int4
+   values), else M <= 8 (M <= 4 for int4 weights); everything else runs the
+   matrix-core kernels. */
 cider_status cider_w8a8_gemm(const int8_t *xq, const float *s_tok, const int8_t *wq,
                              const float *s_w, int64_t M, int64_t N, int64_t K,
                              int group_size, void *y_f16, void *stream);
